@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X flash-CCE ORPO head: one step = forward (logits + online softmax +
+merge) -> ORPO loss (segmented means + epilogue + cotangent) -> backward (recompute + coefficients
++ dh and dW GEMMs) over one synthetic batch whose inputs are already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+Prints one JSON line. The default workload is the e4b-shaped head (d=2560, V=262144, softcap 30,
+M=8192 tokens as 16 chosen/rejected pairs). Runs on one GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
+PEAK_F32 = 157.3e12      # MI355X fp32 (vector and MFMA)
+HBM_PEAK = 8.0e12        # bytes/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload key in lm_head_cross_amd.synth.CONFIGS")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, rows: int):
+    """The float64 oracle as it stands, on a bounded sample of the same batch, on the host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import orpo_oracle as orc
+    from lm_head_cross_amd import synth
+
+    cfg = inp.cfg
+    if cfg.q4:
+        W = orc.dequant_q4(inp.wq, synth.bf16_bits(inp.scales), synth.bf16_bits(inp.biases), 64)
+    else:
+        W = inp.w.float().numpy()
+    h = inp.h[:rows].float().numpy()
+    labels = inp.labels[:rows].copy()
+    # The sample is treated as one chosen/rejected pair split in half (the loss epilogue is a
+    # negligible part of the oracle's time; the three [rows, V] x d products dominate).
+    half = rows // 2
+    off = np.array([0, half, rows], dtype=np.int32)
+    labels[labels == synth.IGNORE_INDEX] = 0
+    t0 = time.perf_counter()
+    out = orc.head_step(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
+    dt = time.perf_counter() - t0
+    assert math.isfinite(out["loss"])
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"first {rows} tokens of the same batch (full V={cfg.V}, d={cfg.d}), float64 "
+                  f"forward + loss + backward{' + dW' if not cfg.q4 else ''}; {dt:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this head is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from lm_head_cross_amd import head as H
+    from lm_head_cross_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    print(f"[bench] generating {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg, seed=args.seed, label_device="cuda")
+    h = inp.h.to(dev)
+    if cfg.q4:
+        w = torch.from_numpy(inp.wq.view(np.int32)).to(dev)
+        sc, bi = inp.scales.to(dev), inp.biases.to(dev)
+    else:
+        w, sc, bi = inp.w.to(dev), None, None
+    labels = torch.from_numpy(inp.labels).to(dev)
+    off = torch.from_numpy(inp.seg_offsets).to(dev)
+    torch.cuda.synchronize()
+    inputs_bytes = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
+                      want_dW=not cfg.q4)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+    loss0 = float(step.out[0].item())
+    assert math.isfinite(loss0), "non-finite loss"
+
+    H.trace_enable(max(64, 200 * args.steps))
+    H.trace_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tr = H.trace_collect()
+    H.trace_enable(0)
+    peak = torch.cuda.max_memory_allocated()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    n_valid = inp.n_valid
+    tok_s = n_valid / (ms / 1e3)
+    peak_flops = PEAK_F32 if cfg.dtype == "f32" else PEAK_BF16
+    work = (6 if cfg.q4 else 8) * cfg.M * cfg.V * cfg.d
+    mfma_frac = work / (ms / 1e3) / peak_flops
+
+    # Dominant kernel: the kind with the most traced time; achieved = its algorithmic FLOPs per
+    # launch over its average launch time (HIP events on the library's launch stream).
+    kinds = {k: v for k, v in tr.items() if v[0] > 0}
+    dom = max(kinds, key=lambda k: kinds[k][1])
+    n_l, tot_ms, fl = kinds[dom]
+    avg_ms = tot_ms / n_l
+    achieved = (fl / n_l) / (avg_ms / 1e3)
+    per_kernel = {k: {"launches_per_step": v[0] / args.steps, "avg_ms": v[1] / max(v[0], 1),
+                      "ms_per_step": v[1] / args.steps,
+                      "tflops": (v[2] / (v[1] / 1e3) / 1e12) if v[1] > 0 and v[2] > 0 else None}
+                  for k, v in kinds.items()}
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows = args.cpu_rows or (256 if cfg.M * cfg.V * cfg.d > 1e12 else min(cfg.M, 1024))
+        print(f"[bench] oracle cpu baseline on {rows} rows", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, rows)
+
+    line = {
+        "metric": "ORPO head fwd+bwd tokens/s (d=2560,V=262144); % bf16 MFMA peak; peak GB",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "M": cfg.M, "valid_tokens": n_valid, "d": cfg.d, "V": cfg.V,
+            "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam,
+            "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
+            "parallelism": "single GPU",
+        },
+        "mfma_frac_of_peak": round(mfma_frac, 4),
+        "algorithmic_tflops": round(work / (ms / 1e3) / 1e12, 1),
+        "peak_hbm_gb": round(peak / 1e9, 3),
+        "inputs_gb": round(inputs_bytes / 1e9, 3),
+        "workspace_gb": round(step.workspace_bytes() / 1e9, 3),
+        "loss": loss0,
+        "kernels": per_kernel,
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved / 1e12, 1),
+            "peak": round(peak_flops / 1e12, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak_flops, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * orpo_head.h — C ABI of the MI355X (gfx950) flash-CCE ORPO head.
+ *
+ * The head turns response hidden states h[M,d] into per-token log-probs through an LM head W[V,d]
+ * without ever materialising the [M,V] logits, reduces them to per-branch means, takes the ORPO
+ * loss, and back-propagates it to dh[M,d] and dW[V,d] by recomputing the logits tile by tile.
+ * Sources (the pages): "Training — design (ORPO, flash-CCE head, prefix sharing, segmented
+ * backward)" §1 "The objective" and §5.1 "The head"; its older revision "ORPO training — design",
+ * "Memory & speed optimization", ranked lever 1 and its "Implementation spec — fused linear-CE
+ * log-prob head"; "Steel flash-CCE — handoff", "The architecture" and Glossary D "The epilogue".
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) must point to device memory of the GPU that is current on the calling
+ *    thread; pointers marked (host) to host memory. All device buffers are owned by the caller: the
+ *    library allocates nothing in these calls and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on `stream`. Outputs are valid once the stream has reached
+ *    the call's end; inputs and the workspace must stay alive until then.
+ *  - Host-detectable argument errors (null pointers, sizes, formats, a workspace that is too small)
+ *    return an error status before anything is enqueued; the library never aborts. Data errors
+ *    that only the device can see (a label outside [0,V) that is not the ignore index, a branch
+ *    without a valid token, non-monotone segment offsets) set bits in a status word held in the
+ *    workspace, readable with orpo_read_status().
+ *  - Calls that share one workspace must not overlap (same stream, or ordered by the caller).
+ *  - Results are deterministic: no atomics take part in any floating-point reduction.
+ */
+#ifndef ORPO_HEAD_H
+#define ORPO_HEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORPO_OK = 0,
+  ORPO_EINVAL = -1,        /* null pointer, negative or inconsistent size, bad option          */
+  ORPO_EUNSUPPORTED = -2,  /* a valid request this build does not implement (see each call)     */
+  ORPO_ENOWS = -3,         /* workspace pointer null or smaller than the *_workspace_bytes size */
+  ORPO_EHIP = -4           /* a HIP runtime call failed (see orpo_last_hip_error)               */
+} orpo_status;
+
+/* Storage formats. ORPO_Q4G64: 4-bit affine codes, w = scale * q + bias per group of 64 along d,
+ * packed 8 codes per uint32 word, LSB first (code j of a row is bits [4(j%8), 4(j%8)+4) of word
+ * j/8), with bf16 scale[V, d/64] and bias[V, d/64] ("ORPO training — design", the flash-CCE Metal
+ * kernel note on in-kernel affine dequantisation; "Steel flash-CCE — handoff", Gotchas item 4). */
+typedef enum { ORPO_F32 = 0, ORPO_BF16 = 1, ORPO_Q4G64 = 2 } orpo_fmt;
+
+/* Bits of the device status word. */
+enum {
+  ORPO_DATA_BAD_LABEL = 1u << 0,    /* a label outside [0,V) that is not ignore_index (treated as ignored) */
+  ORPO_DATA_EMPTY_BRANCH = 1u << 1, /* a branch with no valid token (its mean, the loss and g are NaN)      */
+  ORPO_DATA_BAD_OFFSETS = 1u << 2   /* segment offsets not monotone within [0,M] (loss and g are NaN)       */
+};
+
+/* Option bits of orpo_head_desc.flags. */
+enum {
+  ORPO_DW_ACCUMULATE = 1u << 0      /* orpo_head_bwd adds into dW instead of overwriting it */
+};
+
+typedef struct {
+  int64_t M;            /* tokens (rows of h), >= 0                                             */
+  int64_t d;            /* hidden size, > 0, multiple of 64                                     */
+  int64_t V;            /* vocabulary size, > 0                                                 */
+  int32_t h_fmt;        /* ORPO_F32 or ORPO_BF16; row-major [M,d]                               */
+  int32_t w_fmt;        /* ORPO_F32 (needs h_fmt F32), ORPO_BF16 or ORPO_Q4G64 (need h_fmt BF16) */
+  float softcap;        /* > 0: z = softcap * tanh(raw / softcap); <= 0: z = raw                */
+  int32_t ignore_index; /* label value of ignored / padding tokens (conventionally -100)        */
+  uint32_t flags;       /* ORPO_DW_ACCUMULATE                                                   */
+} orpo_head_desc;
+
+/* The head weights: `w` is W[V,d] row-major in w_fmt (for ORPO_Q4G64 the packed uint32 words
+ * [V, d/8]); `scales` and `biases` are bf16 [V, d/64] for ORPO_Q4G64 and must be NULL otherwise. */
+typedef struct {
+  const void* w;
+  const void* scales;
+  const void* biases;
+} orpo_weight;
+
+/* Workspace sizes in bytes (0 on invalid arguments). The forward workspace grows as 256 + 8 * NBLK
+ * * M (per-token partials over NBLK vocabulary splits, like lse it is O(M)); the backward
+ * workspace is a fixed-size coefficient tile, independent of M beyond one token chunk. */
+size_t orpo_head_fwd_workspace_bytes(const orpo_head_desc* desc);
+size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc);
+size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs);
+
+/*
+ * orpo_head_fwd — per-token log-prob and log-sum-exp without the [M,V] logits.
+ *   z_tv = softcap(h_t . W_v); lse_t = log sum_v exp(z_tv); logp_t = z_t[y_t] - lse_t.
+ * ("Training — design" §5.1 "The head"; older revision, the spec's forward: online softmax over
+ * vocabulary tiles with target capture, storing O(M) state only; "Steel flash-CCE — handoff",
+ * "The architecture", forward: per-split partials merged across splits.)
+ *   h      (device) [M,d] in desc->h_fmt
+ *   W      (device) see orpo_weight
+ *   labels (device) int32 [M]; ignore_index marks tokens that get no log-prob
+ *   logp   (device) float [M] out: logp_t, 0 for ignored tokens
+ *   lse    (device) float [M] out: lse_t for every row (kept for orpo_head_bwd)
+ *   ws     (device) >= orpo_head_fwd_workspace_bytes(desc) bytes, 256-byte aligned
+ * Returns ORPO_EUNSUPPORTED for d not a multiple of 64 or format combinations not listed above.
+ */
+orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                          const int32_t* labels, float* logp, float* lse, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/*
+ * orpo_loss — segmented per-branch mean, scalar ORPO epilogue (float64) and per-token cotangent.
+ *   ell_b = mean of logp over the valid tokens of branch b = [off[b], off[b+1]); branch 2p is the
+ *   chosen, 2p+1 the rejected response of pair p. With log1mexp(x) = log(max(1 - e^x, 1e-12)):
+ *   log_odds_p = (lw - lr) - (log1mexp(lw) - log1mexp(lr)); or = mean_p softplus(-log_odds_p);
+ *   nll = mean_p(-lw); loss = nll + lambda * or. g_t = dloss/dlogp_t = (dloss/dell_b) / n_b.
+ * ("Training — design" §1 "The objective"; older revision, "File-by-file changes", orpoLoss and
+ * orpoMetrics; §4's note on the 1/(1-P) factor of the odds-ratio gradient.)
+ *   M, n_pairs     tokens (>= 0) and pairs (>= 1)
+ *   seg_offsets    (device) int32 [2*n_pairs + 1], monotone within [0, M]
+ *   logp, labels   (device) [M] as produced for / consumed by orpo_head_fwd
+ *   V, ignore_index the vocabulary size and ignore label: only labels in [0,V) that differ from
+ *                  ignore_index count (a bad label is ignored here too, as in orpo_head_fwd)
+ *   out            (device) double [5 + 2*n_pairs] out: loss, nll, or, accuracy (mean 1[lw > lr]),
+ *                  margin (mean log_odds), then lw[n_pairs], then lr[n_pairs]
+ *   g              (device) float [M] out: the cotangent fed to orpo_head_bwd (0 off-branch / ignored)
+ *   ws             (device) >= orpo_loss_workspace_bytes(M, n_pairs) bytes
+ */
+orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, const float* logp,
+                      const int32_t* labels, int64_t V, int32_t ignore_index, double lambda,
+                      double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * orpo_head_bwd — dh = coeff . W and dW = coeff^T . h, recomputing the logits tile by tile.
+ *   coeff_tv = g_t * (1[v = y_t] - exp(z_tv - lse_t)) * sech^2(raw_tv / softcap)   (sech^2 = 1
+ *   without a softcap). ("ORPO training — design", the spec's backward: recompute each vocabulary
+ *   tile from the saved lse and form g (onehot - softmax) sech^2; "Steel flash-CCE — handoff",
+ *   Glossary D "softmax-onehot coeff". dW is the same chain rule for the weight operand.)
+ *   h, W, labels   as for orpo_head_fwd
+ *   lse            (device) float [M] from orpo_head_fwd on the same h, W, labels
+ *   g              (device) float [M] dloss/dlogp (e.g. from orpo_loss); ignored tokens must hold 0
+ *   dh             (device) float [M,d] out (overwritten)
+ *   dW             (device) float [V,d] out (overwritten, or accumulated with ORPO_DW_ACCUMULATE);
+ *                  NULL computes dh only. Must be NULL for ORPO_Q4G64 (a quantised head is frozen).
+ *   ws             (device) >= orpo_head_bwd_workspace_bytes(desc) bytes
+ */
+orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                          const int32_t* labels, const float* lse, const float* g, float* dh,
+                          float* dW, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward tiling: the token chunk C (a multiple of 256, default 8192) and the byte budget of the
+ * coefficient tile [C, BVb] (default 256 MiB; BVb is the largest multiple of 256 that fits, at
+ * least 256). 0 restores a default. Process-wide; call it only while no call of this library is in
+ * flight, and size workspaces after it. Returns ORPO_EINVAL for a chunk that is not a multiple of
+ * 256 or a negative value. */
+orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes);
+
+/* Kernel tracing (a profiling aid). While enabled, every kernel this library launches is bracketed
+ * by a pair of HIP events recorded on the launch's stream (up to max_launches launches), tagged with
+ * its kind and its algorithmic floating-point work (2*d flops per (token, vocabulary) product of
+ * the forward and coefficient GEMMs, 4*d for the fused dh/dW launch; 0 for merge and loss).
+ * orpo_trace_collect waits for the recorded events of one kind and returns their totals;
+ * orpo_trace_reset starts a new record.
+ * Process-wide and not thread-safe; enabling allocates events (host API only, no device memory). */
+typedef enum {
+  ORPO_K_FWD = 0,    /* forward logits + online softmax             */
+  ORPO_K_MERGE = 1,  /* cross-split merge -> lse, logp              */
+  ORPO_K_LOSS = 2,   /* segmented means + ORPO epilogue + g         */
+  ORPO_K_COEFF = 3,  /* backward logit recompute + coefficients     */
+  ORPO_K_DHDW = 4,   /* backward dh and dW GEMMs                    */
+  ORPO_K_COUNT = 5
+} orpo_kernel_kind;
+orpo_status orpo_trace_enable(int32_t max_launches);   /* 0 disables and releases the events */
+orpo_status orpo_trace_collect(int32_t kind, int64_t* launches, double* total_ms, double* flops);
+orpo_status orpo_trace_reset(void);                    /* forget the records, keep the events  */
+
+/* Waits for `stream` and copies the status word of `ws` (a workspace used by any call above) to
+ * *status_out (host). Returns ORPO_EHIP if the wait or copy fails. */
+orpo_status orpo_read_status(const void* ws, uint32_t* status_out, hipStream_t stream);
+
+/* Text for a status code (static storage). */
+const char* orpo_status_string(orpo_status s);
+
+/* The last HIP error code seen by this library on the calling thread (hipSuccess if none). */
+int32_t orpo_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORPO_HEAD_H */

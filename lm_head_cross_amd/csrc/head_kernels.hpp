@@ -1,0 +1,526 @@
+// head_kernels.hpp — the flash-CCE ORPO head kernels for gfx950.
+//
+//   fwd_kernel    : raw = W . h^T tile by tile (MFMA), softcap, online softmax per token over the
+//                   workgroup's vocabulary split, label-logit capture -> per-split (max, sum) partials.
+//   merge_kernel  : partials of all splits -> lse, logp = z[y] - lse.
+//   loss_kernel   : segmented per-branch means (f64), scalar ORPO epilogue (f64), cotangent g.
+//   coeff_kernel  : recompute a logit tile, coeff = g (onehot - softmax) sech^2 -> coefficient tile.
+//   dhdw_kernel   : dh (+)= coeff . W_blk and dW_blk (+)= coeff^T . h_chunk from one coefficient tile.
+//
+// Sources: "Training — design" §1 "The objective" and §5.1 "The head"; its older revision "ORPO
+// training — design", "Memory & speed optimization", lever 1 and the "Implementation spec — fused
+// linear-CE log-prob head" (online softmax over vocabulary tiles, O(M) saved state, recompute in
+// the backward); "Steel flash-CCE — handoff", "The architecture" (per-split partials and their
+// merge) and Glossary D "The epilogue" (softcap, online softmax, target capture, softmax-onehot
+// coefficient). The (max, sum) running state and every gradient accumulation stay in fp32, as the
+// older revision's vocab-blocked head found necessary.
+#pragma once
+#include <type_traits>
+
+#include "gemm_core.hpp"
+
+namespace orpo {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr uint32_t kStatusBadLabel = 1u, kStatusEmptyBranch = 2u, kStatusBadOffsets = 4u;
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float log2_(float x) { return __builtin_amdgcn_logf(x); }
+
+// Softcap in the log2 domain. With E = 2^(raw * 2 log2e / cap) = e^(2 raw / cap) and
+// r = 1 / (E + 1): tanh(raw / cap) = 1 - 2r, so z = cap - 2 cap r and (z - cap) log2e = -2 cap log2e r,
+// and sech^2(raw / cap) = 1 - tanh^2 = 4 r (1 - r).
+struct Softcap {
+  float cap, c1, kz;
+  __device__ Softcap(float c) : cap(c), c1(2.f * kLog2e / c), kz(-2.f * c * kLog2e) {}
+  __device__ __forceinline__ float r_of(float raw) const { return rcp_(exp2_(raw * c1) + 1.f); }
+};
+
+// ------------------------------------------------------------------------------------------
+// Forward
+// ------------------------------------------------------------------------------------------
+struct FwdArgs {
+  const void* h;          // [M, d]
+  const void* w;          // [V, d] dense, or Q4Weight below
+  Q4Weight q4;
+  const int32_t* labels;  // [M]
+  float* logp;            // [M]: receives z[y] here, finished by merge_kernel
+  float2* part;           // [nblk, M] (max in log2 units, sum of 2^(u - max))
+  uint32_t* status;
+  int64_t M, d, V;
+  float cap;
+  int32_t ignore_index;
+  int32_t n_tb, nblk, tiles_per_split, n_vtiles;
+};
+
+template <class E, bool Q4, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
+  const int tb = blockIdx.x % a.n_tb, split = blockIdx.x / a.n_tb;
+  const int tile0 = split * a.tiles_per_split;
+  const int n_tiles = min(a.tiles_per_split, a.n_vtiles - tile0);
+  if (blockIdx.x == 0 && tid == 0) *a.status = 0u;
+  const int64_t t0 = (int64_t)tb * kTile;
+  const int64_t row_bytes = a.d * E::kSize;
+
+  int64_t tok[2];
+  int y[2];
+  float m[2], s[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    tok[nb] = t0 + acc_n(wn, nb, l);
+    // -1 marks "no capture": rows past M and ignored tokens (ignore_index may be any value).
+    const int lab = tok[nb] < a.M ? a.labels[tok[nb]] : -1;
+    y[nb] = lab == a.ignore_index ? -1 : lab;
+    m[nb] = SOFTCAP ? a.cap * kLog2e : kNegInf;   // with a softcap every z <= cap: fixed reference
+    s[nb] = 0.f;
+  }
+  const Softcap sc(SOFTCAP ? a.cap : 1.f);
+
+  typedef typename std::conditional<Q4, Q4KTile, DenseTile<kTile, 8>>::type LoaderA;
+  LoaderA la;
+  DenseTile<kTile, 8> lb;
+  const int nk = (int)(a.d / E::kBK);
+  auto issue = [&](int tile, int ks) {
+    const int64_t v0 = (int64_t)(tile0 + tile) * kTile;
+    if constexpr (Q4) {
+      la.load(a.q4, v0, (int64_t)ks * E::kBK, tid);
+    } else {
+      la.load((const char*)a.w, row_bytes, v0, (int64_t)ks * kKBytes, a.V, row_bytes, tid);
+    }
+    lb.load((const char*)a.h, row_bytes, t0, (int64_t)ks * kKBytes, a.M, row_bytes, tid);
+  };
+  auto epi = [&](int tile, f32x16(&acc)[4][2]) {
+    const int64_t vt0 = (int64_t)(tile0 + tile) * kTile;
+    const int64_t vw0 = vt0 + wm * 128;              // first vocabulary row of this wave
+    const bool tail = vt0 + kTile > a.V;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      // u = z * log2e (or (z - cap) * log2e under a softcap), masked to -inf past V. Values are
+      // recomputed from the accumulators in each pass instead of being staged in registers.
+      auto masked = [&](int mb, int r) {
+        return tail && vw0 + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3) >= a.V;
+      };
+      float ref = m[nb];
+      if (!SOFTCAP) {
+        float tmax = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!masked(mb, r)) tmax = fmaxf(tmax, acc[mb][nb][r]);
+        const float mn = fmaxf(m[nb], tmax * kLog2e);
+        if (mn != kNegInf) {
+          s[nb] *= exp2_(m[nb] - mn);   // m = -inf gives 0
+          m[nb] = mn;
+        }
+        ref = m[nb];
+      }
+      float acc_s = 0.f;
+      if (ref != kNegInf) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float raw = acc[mb][nb][r];
+            const float x = SOFTCAP ? sc.kz * sc.r_of(raw) : raw * kLog2e - ref;
+            acc_s += masked(mb, r) ? 0.f : exp2_(x);
+          }
+      }
+      s[nb] += acc_s;
+      // Target capture: the one lane holding (v = y, t) writes z[y] to logp[t].
+      const int64_t off = (int64_t)y[nb] - vw0;
+      const bool mine = off >= 0 && off < 128 && (((int)off >> 2) & 1) == (l >> 5);
+      if (__builtin_expect(__ballot(mine) != 0, 0)) {
+        if (mine) {
+          const int o = (int)off, mb = o >> 5, ro = o & 31;
+          const int r = ((ro >> 3) << 2) | (ro & 3);
+          float zsel = 0.f;
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+              if (mm == mb && rr == r) zsel = acc[mm][nb][rr];
+          const float z = SOFTCAP ? sc.cap - 2.f * sc.cap * sc.r_of(zsel) : zsel;
+          a.logp[tok[nb]] = z;
+        }
+      }
+    }
+  };
+  f32x16 acc[4][2];
+  zero_acc(acc);
+  gemm_run<E, true, true>(smem, la, lb, kKPitch, kKPitch, n_tiles, nk, issue, epi, acc);
+
+  // Combine the lane pair (l, l ^ 32), then the two m-waves, and write this split's partials.
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float mo = __shfl_xor(m[nb], 32), so = __shfl_xor(s[nb], 32);
+    if (!SOFTCAP) {
+      const float mn = fmaxf(m[nb], mo);
+      if (mn != kNegInf) {
+        s[nb] = s[nb] * exp2_(m[nb] - mn) + so * exp2_(mo - mn);
+        m[nb] = mn;
+      }
+    } else {
+      s[nb] += so;
+    }
+  }
+  float2* red = (float2*)smem;   // [256 tokens]
+  if (wm == 1 && l < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) red[acc_n(wn, nb, l)] = make_float2(m[nb], s[nb]);
+  }
+  __syncthreads();
+  if (wm == 0 && l < 32) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float2 o = red[acc_n(wn, nb, l)];
+      float mm = m[nb], ss = s[nb];
+      if (!SOFTCAP) {
+        const float mn = fmaxf(mm, o.x);
+        if (mn != kNegInf) {
+          ss = ss * exp2_(mm - mn) + o.y * exp2_(o.x - mn);
+          mm = mn;
+        }
+      } else {
+        ss += o.y;
+      }
+      if (tok[nb] < a.M) a.part[(int64_t)split * a.M + tok[nb]] = make_float2(mm, ss);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Merge the per-split partials: G = max_k m_k, S = sum_k s_k 2^(m_k - G), lse = (G + log2 S) ln 2.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(const float2* part, int nblk, int64_t M,
+                                                    const int32_t* labels, int64_t V,
+                                                    int32_t ignore_index, float* logp, float* lse,
+                                                    uint32_t* status) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= M) return;
+  float G = kNegInf;
+  for (int k = 0; k < nblk; ++k) G = fmaxf(G, part[(int64_t)k * M + t].x);
+  float S = 0.f;
+  for (int k = 0; k < nblk; ++k) {
+    const float2 p = part[(int64_t)k * M + t];
+    if (p.y > 0.f) S += p.y * exp2_(p.x - G);
+  }
+  const float L = (G + log2_(S)) * kLn2;
+  lse[t] = L;
+  const int y = labels[t];
+  if (y == ignore_index) {
+    logp[t] = 0.f;
+  } else if (y < 0 || (int64_t)y >= V) {
+    logp[t] = 0.f;
+    atomicOr(status, kStatusBadLabel);
+  } else {
+    logp[t] = logp[t] - L;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Loss: one workgroup. Per-branch sums in f64 with fixed-order wave reductions, the scalar ORPO
+// epilogue in f64 per pair, fixed-order sums over pairs, then g for every token.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ double log1mexp_d(double x, bool* clamped) {
+  const double v = -expm1(x);
+  if (!(v >= 1e-12)) {
+    *clamped = true;
+    return log(1e-12);
+  }
+  *clamped = false;
+  return x > -0.6931471805599453 ? log(v) : log1p(-exp(x));
+}
+
+struct LossArgs {
+  int64_t M, V;
+  int32_t P;
+  const int32_t* off;     // [2P+1]
+  const float* logp;
+  const int32_t* labels;
+  int32_t ignore_index;
+  double lam;
+  double* out;            // [5 + 2P]
+  float* g;               // [M]
+  double* ell;            // ws [2P]
+  double* dl;             // ws [2P]  dL/d ell
+  int64_t* cnt;           // ws [2P]
+  double* pair;           // ws [4P]: log_odds, L_OR, then accuracy bit
+  uint32_t* status;
+};
+
+__global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
+  __shared__ int bad;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int nb = 2 * a.P;
+  if (tid == 0) {
+    int b = a.off[0] < 0 || (int64_t)a.off[nb] > a.M;
+    for (int i = 0; i < nb; ++i) b |= a.off[i + 1] < a.off[i];
+    bad = b;
+    *a.status = b ? kStatusBadOffsets : 0u;
+  }
+  __syncthreads();
+  const double nan = __builtin_nan("");
+  if (bad) {
+    for (int i = tid; i < 5 + nb; i += 1024) a.out[i] = nan;
+    for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
+    return;
+  }
+  // Branch sums: wave w takes branches w, w + 16, ...
+  for (int b = w; b < nb; b += 16) {
+    double sum = 0.0;
+    long long n = 0;
+    for (int64_t t = a.off[b] + l; t < a.off[b + 1]; t += 64) {
+      const int y = a.labels[t];
+      if (y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
+        sum += (double)a.logp[t];
+        ++n;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      sum += __shfl_xor(sum, o);
+      n += __shfl_xor(n, o);
+    }
+    if (l == 0) {
+      a.cnt[b] = n;
+      a.ell[b] = n > 0 ? sum / (double)n : nan;
+      if (n == 0) atomicOr(a.status, kStatusEmptyBranch);
+    }
+  }
+  __syncthreads();
+  // Per pair: log-odds, L_OR, and dL/d ell for both branches.
+  for (int p = tid; p < a.P; p += 1024) {
+    const double lw = a.ell[2 * p], lr = a.ell[2 * p + 1];
+    bool cw, cr;
+    const double ow = log1mexp_d(lw, &cw), orr = log1mexp_d(lr, &cr);
+    const double z = (lw - lr) - (ow - orr);
+    const double lor = fmax(-z, 0.0) + log1p(exp(-fabs(z)));                 // softplus(-z)
+    const double oms = z >= 0 ? exp(-z) / (1.0 + exp(-z)) : 1.0 / (1.0 + exp(z));   // 1 - sigmoid(z)
+    const double fw = cw ? 1.0 : -1.0 / expm1(lw);
+    const double fr = cr ? 1.0 : -1.0 / expm1(lr);
+    a.dl[2 * p] = (-1.0 - a.lam * oms * fw) / (double)a.P;
+    a.dl[2 * p + 1] = (a.lam * oms * fr) / (double)a.P;
+    a.pair[p] = z;
+    a.pair[a.P + p] = lor;
+    a.pair[2 * a.P + p] = lw > lr ? 1.0 : 0.0;
+    a.out[5 + p] = lw;
+    a.out[5 + a.P + p] = lr;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double nll = 0.0, orv = 0.0, acc = 0.0, mar = 0.0;
+    for (int p = 0; p < a.P; ++p) {
+      nll -= a.ell[2 * p];
+      orv += a.pair[a.P + p];
+      acc += a.pair[2 * a.P + p];
+      mar += a.pair[p];
+    }
+    const double P = (double)a.P;
+    a.out[0] = nll / P + a.lam * (orv / P);
+    a.out[1] = nll / P;
+    a.out[2] = orv / P;
+    a.out[3] = acc / P;
+    a.out[4] = mar / P;
+  }
+  // g_t = (dL/d ell_b) / n_b for a valid token of branch b (binary search over the offsets).
+  for (int64_t t = tid; t < a.M; t += 1024) {
+    float gv = 0.f;
+    const int y = t < a.M ? a.labels[t] : a.ignore_index;
+    if (t >= a.off[0] && t < a.off[nb] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
+      int lo = 0, hi = nb;   // find b with off[b] <= t < off[b+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)a.off[mid] <= t) lo = mid; else hi = mid;
+      }
+      gv = (float)(a.dl[lo] / (double)a.cnt[lo]);
+    }
+    a.g[t] = gv;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward phase 1: recompute a 256 x 256 logit tile (m = vocabulary, n = token) and write its
+// coefficients to the tile [C][BVb] (token-major) in the workspace.
+// ------------------------------------------------------------------------------------------
+struct BwdArgs {
+  const void* h;
+  const void* w;
+  Q4Weight q4;
+  const int32_t* labels;
+  const float* lse;
+  const float* g;
+  float* dh;              // [M, d]
+  float* dW;              // [V, d] or null
+  void* coeff;            // [C, BVb] of E::T
+  int64_t M, d, V;
+  int64_t c0, C_cur;      // token chunk [c0, c0 + C_cur)
+  int64_t v0, BV_cur;     // vocabulary block [v0, v0 + BV_cur)
+  int64_t BVb;            // row pitch of the coefficient tile (elements)
+  float cap;
+  int32_t ignore_index;
+  int32_t n_vt, n_tt;     // coefficient tiles along vocabulary and tokens
+  int32_t n_dh, n_dw, n_jt;
+  int32_t dh_first, dw_first;
+};
+
+template <class E, bool Q4, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
+  const int vt = blockIdx.x % a.n_vt, tt = blockIdx.x / a.n_vt;
+  const int64_t vbase = a.v0 + (int64_t)vt * kTile;   // global vocabulary row of tile row 0
+  const int64_t tbase = a.c0 + (int64_t)tt * kTile;   // global token of tile column 0
+  const int64_t t_end = min(a.M, a.c0 + a.C_cur);
+  const int64_t row_bytes = a.d * E::kSize;
+
+  typedef typename std::conditional<Q4, Q4KTile, DenseTile<kTile, 8>>::type LoaderA;
+  LoaderA la;
+  DenseTile<kTile, 8> lb;
+  const int nk = (int)(a.d / E::kBK);
+  auto issue = [&](int, int ks) {
+    if constexpr (Q4) {
+      la.load(a.q4, vbase, (int64_t)ks * E::kBK, tid);
+    } else {
+      la.load((const char*)a.w, row_bytes, vbase, (int64_t)ks * kKBytes, a.V, row_bytes, tid);
+    }
+    lb.load((const char*)a.h, row_bytes, tbase, (int64_t)ks * kKBytes, t_end, row_bytes, tid);
+  };
+  f32x16 acc[4][2];
+  zero_acc(acc);
+  auto nop = [](int, f32x16(&)[4][2]) {};
+  gemm_run<E, true, true, false>(smem, la, lb, kKPitch, kKPitch, 1, nk, issue, nop, acc);
+
+  const Softcap sc(SOFTCAP ? a.cap : 1.f);
+  typedef typename E::T T;
+  T* out = (T*)a.coeff;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = acc_n(wn, nb, l);
+    const int64_t t = tbase + n;
+    const bool tv = t < t_end;
+    const int y = tv ? a.labels[t] : a.ignore_index;
+    const bool yv = tv && y != a.ignore_index && y >= 0 && (int64_t)y < a.V;   // else: ignored
+    const float gt = yv ? a.g[t] : 0.f;
+    const float L2 = yv ? a.lse[t] * kLog2e : 0.f;
+    const int64_t yo = (int64_t)y - vbase;            // label row within this tile
+    T* row = out + (t - a.c0) * a.BVb + (vbase - a.v0);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float vals[4];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri) {
+          const int r = rg * 4 + ri;
+          const int mm = acc_m(wm, mb, r, l);
+          const float raw = acc[mb][nb][r];
+          float zl2, slope;
+          if (SOFTCAP) {
+            const float rr = sc.r_of(raw);
+            zl2 = (sc.cap - 2.f * sc.cap * rr) * kLog2e;
+            slope = 4.f * rr * (1.f - rr);
+          } else {
+            zl2 = raw * kLog2e;
+            slope = 1.f;
+          }
+          const float p = exp2_(zl2 - L2);
+          float c = gt * ((yo == mm ? 1.f : 0.f) - p) * slope;
+          if (vbase + mm >= a.V || gt == 0.f) c = 0.f;
+          vals[ri] = c;
+        }
+        // 4 consecutive vocabulary entries of token t.
+        const int m0 = acc_m(wm, mb, rg * 4, l);
+        if constexpr (sizeof(T) == 2) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(vals[0], vals[1]);
+          pk[1] = pack_bf16x2(vals[2], vals[3]);
+          *(u32x2*)(row + m0) = pk;
+        } else {
+          *(f32x4*)(row + m0) = f32x4{vals[0], vals[1], vals[2], vals[3]};
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward phase 2: one launch holds n_dh tiles of dh[c0 + i][j] (+)= sum_v coeff[i][v] W[v0 + v][j]
+// and n_dw tiles of dW[v0 + v][j] (+)= sum_i coeff[i][v] h[c0 + i][j].
+// ------------------------------------------------------------------------------------------
+template <class E>
+__device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, int64_t n_rows,
+                                          int64_t col0, int64_t n_cols, bool first,
+                                          const f32x16 (&acc)[4][2]) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t col = col0 + acc_n(wn, nb, l);
+    if (col >= n_cols) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + acc_m(wm, mb, r, l);
+        if (row < n_rows) {
+          float* p = out + row * ld + col;
+          *p = first ? acc[mb][nb][r] : *p + acc[mb][nb][r];
+        }
+      }
+  }
+}
+
+template <class E, bool Q4>
+__global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const int tid = threadIdx.x;
+  const int64_t row_bytes = a.d * E::kSize;
+  const int64_t cpitch = a.BVb * E::kSize;            // coefficient tile row pitch (bytes)
+  const int64_t t_end = min(a.M, a.c0 + a.C_cur);
+  f32x16 acc[4][2];
+  zero_acc(acc);
+  auto nop = [](int, f32x16(&)[4][2]) {};
+  if ((int)blockIdx.x < a.n_dh) {
+    // m = token (C rows), n = hidden, k = vocabulary of the block.
+    const int it = blockIdx.x / a.n_jt, jt = blockIdx.x % a.n_jt;
+    const int64_t i0 = (int64_t)it * kTile, j0 = (int64_t)jt * kTile;
+    const int64_t kv = ((a.BV_cur + kTile - 1) / kTile) * kTile;   // coefficient columns written
+    const int nk = (int)((kv + E::kBK - 1) / E::kBK);
+    DenseTile<kTile, 8> la;   // coeff [i][v], K-major
+    typedef typename std::conditional<Q4, Q4NTile, DenseTile<E::kBK, kTile * E::kSize / 16>>::type LoaderB;
+    LoaderB lb;               // W [v][j], N-major
+    auto issue = [&](int, int ks) {
+      const int64_t k0 = (int64_t)ks * E::kBK;
+      la.load((const char*)a.coeff, cpitch, i0, k0 * E::kSize, a.C_cur, kv * E::kSize, tid);
+      if constexpr (Q4) {
+        lb.load(a.q4, a.v0 + k0, j0, tid);
+      } else {
+        lb.load((const char*)a.w, row_bytes, a.v0 + k0, j0 * E::kSize,
+                min(a.V, a.v0 + a.BV_cur), row_bytes, tid);
+      }
+    };
+    gemm_run<E, true, false, false>(smem, la, lb, kKPitch, E::kMnPitch, 1, nk, issue, nop, acc);
+    store_out<E>(a.dh, a.d, a.c0 + i0, t_end, j0, a.d, a.dh_first != 0, acc);
+  } else {
+    // m = vocabulary (block rows), n = hidden, k = token of the chunk.
+    const int bid = blockIdx.x - a.n_dh;
+    const int vt = bid / a.n_jt, jt = bid % a.n_jt;
+    const int64_t vl0 = (int64_t)vt * kTile, j0 = (int64_t)jt * kTile;
+    const int nk = (int)((a.C_cur + E::kBK - 1) / E::kBK);
+    DenseTile<E::kBK, kTile * E::kSize / 16> la;   // coeff [i][v], M-major
+    DenseTile<E::kBK, kTile * E::kSize / 16> lb;   // h [i][j], N-major
+    auto issue = [&](int, int ks) {
+      const int64_t k0 = (int64_t)ks * E::kBK;
+      la.load((const char*)a.coeff, cpitch, k0, vl0 * E::kSize, a.C_cur, cpitch, tid);
+      lb.load((const char*)a.h, row_bytes, a.c0 + k0, j0 * E::kSize, t_end, row_bytes, tid);
+    };
+    gemm_run<E, false, false, false>(smem, la, lb, E::kMnPitch, E::kMnPitch, 1, nk, issue, nop, acc);
+    store_out<E>(a.dW, a.d, a.v0 + vl0, min(a.V, a.v0 + a.BV_cur), j0, a.d, a.dw_first != 0, acc);
+  }
+}
+
+}  // namespace orpo

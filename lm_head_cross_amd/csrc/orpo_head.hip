@@ -1,0 +1,391 @@
+// orpo_head.hip — host side of the C ABI declared in include/orpo_head.h: argument validation,
+// launch planning (vocabulary splits for the forward, token chunk x vocabulary block for the
+// backward) and kernel launches on the caller's stream. No allocation, no host synchronisation
+// (except orpo_read_status, which is documented to wait).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/orpo_head.h"
+#include "head_kernels.hpp"
+
+namespace {
+
+using namespace orpo;
+
+thread_local int32_t g_last_hip = 0;
+
+constexpr size_t kHeader = 256;                     // status word + padding at the start of a workspace
+constexpr int kTargetWorkgroups = 512;              // forward grid target (2 rounds on 256 CUs)
+constexpr int64_t kChunkDefault = 8192;             // backward token chunk C (multiple of 256)
+constexpr size_t kCoeffDefault = size_t(256) << 20; // bytes of the backward coefficient tile
+int64_t g_chunk = kChunkDefault;
+size_t g_coeff_budget = kCoeffDefault;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+#define ORPO_HIP(x)                                  \
+  do {                                               \
+    hipError_t e_ = (x);                             \
+    if (e_ != hipSuccess) {                          \
+      g_last_hip = (int32_t)e_;                      \
+      return ORPO_EHIP;                              \
+    }                                                \
+  } while (0)
+
+inline orpo_status launched() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip = (int32_t)e;
+    return ORPO_EHIP;
+  }
+  return ORPO_OK;
+}
+
+// ---- tracing: event pairs around launches ------------------------------------------------
+struct TraceRec {
+  hipEvent_t start, end;
+  int kind;
+  double flops;
+};
+std::vector<TraceRec> g_trace;   // pre-created event pairs
+size_t g_trace_used = 0;
+bool g_trace_on = false;
+
+// Brackets one launch: `begin` before it, `end` after it (both on the launch's stream).
+struct TraceScope {
+  TraceRec* rec = nullptr;
+  hipStream_t st;
+  TraceScope(int kind, double flops, hipStream_t s) : st(s) {
+    if (g_trace_on && g_trace_used < g_trace.size()) {
+      rec = &g_trace[g_trace_used++];
+      rec->kind = kind;
+      rec->flops = flops;
+      if (hipEventRecord(rec->start, st) != hipSuccess) rec = nullptr;
+    }
+  }
+  ~TraceScope() {
+    if (rec) (void)hipEventRecord(rec->end, st);
+  }
+};
+
+// Format combinations this build implements.
+enum Kind { kF32, kBf16, kQ4, kBad };
+
+orpo_status check_desc(const orpo_head_desc* d, Kind* kind) {
+  if (!d) return ORPO_EINVAL;
+  if (d->M < 0 || d->d <= 0 || d->V <= 0) return ORPO_EINVAL;
+  if (d->V > INT32_MAX || d->M > INT32_MAX || d->d > (int64_t(1) << 20)) return ORPO_EUNSUPPORTED;
+  if ((d->flags & ~uint32_t(ORPO_DW_ACCUMULATE)) != 0) return ORPO_EINVAL;
+  if (!(d->softcap <= 0.f || d->softcap > 0.f)) return ORPO_EINVAL;   // NaN
+  Kind k = kBad;
+  if (d->h_fmt == ORPO_F32 && d->w_fmt == ORPO_F32) k = kF32;
+  else if (d->h_fmt == ORPO_BF16 && d->w_fmt == ORPO_BF16) k = kBf16;
+  else if (d->h_fmt == ORPO_BF16 && d->w_fmt == ORPO_Q4G64) k = kQ4;
+  else if ((d->h_fmt == ORPO_F32 || d->h_fmt == ORPO_BF16) &&
+           (d->w_fmt == ORPO_F32 || d->w_fmt == ORPO_BF16 || d->w_fmt == ORPO_Q4G64))
+    return ORPO_EUNSUPPORTED;
+  else
+    return ORPO_EINVAL;
+  if (d->d % 64 != 0) return ORPO_EUNSUPPORTED;
+  *kind = k;
+  return ORPO_OK;
+}
+
+orpo_status check_weight(Kind k, const orpo_weight& W) {
+  if (!W.w) return ORPO_EINVAL;
+  if (k == kQ4) return (W.scales && W.biases) ? ORPO_OK : ORPO_EINVAL;
+  return (W.scales || W.biases) ? ORPO_EINVAL : ORPO_OK;
+}
+
+struct FwdPlan {
+  int n_tb, nblk, tps, n_vtiles;
+  size_t ws;
+};
+
+FwdPlan plan_fwd(const orpo_head_desc* d) {
+  FwdPlan p;
+  p.n_tb = (int)cdiv(std::max<int64_t>(d->M, 1), kTile);
+  p.n_vtiles = (int)cdiv(d->V, kTile);
+  int nblk = (int)std::min<int64_t>(p.n_vtiles, std::max<int64_t>(1, cdiv(kTargetWorkgroups, p.n_tb)));
+  p.tps = (int)cdiv(p.n_vtiles, nblk);
+  p.nblk = (int)cdiv(p.n_vtiles, p.tps);
+  p.ws = kHeader + round_up(size_t(p.nblk) * size_t(std::max<int64_t>(d->M, 0)) * sizeof(float2), 256);
+  return p;
+}
+
+struct BwdPlan {
+  int64_t C, BVb;
+  size_t ws;
+};
+
+BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
+  BwdPlan p;
+  const int64_t esize = k == kF32 ? 4 : 2;
+  p.C = std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), kTile) * kTile, g_chunk);
+  const int64_t by_budget = std::max<int64_t>(kTile, int64_t(g_coeff_budget) / (p.C * esize) / kTile * kTile);
+  p.BVb = std::min<int64_t>(cdiv(d->V, kTile) * kTile, by_budget);
+  p.ws = kHeader + size_t(p.C) * size_t(p.BVb) * size_t(esize);
+  return p;
+}
+
+template <class E, bool Q4, bool SC>
+orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
+  TraceScope ts(ORPO_K_FWD, 2.0 * double(a.M) * double(a.V) * double(a.d), st);
+  hipLaunchKernelGGL((fwd_kernel<E, Q4, SC>), dim3(grid), dim3(kThreads), 0, st, a);
+  return launched();
+}
+
+template <class E, bool Q4, bool SC>
+orpo_status launch_coeff(const BwdArgs& a, int grid, hipStream_t st) {
+  TraceScope ts(ORPO_K_COEFF, 2.0 * double(a.C_cur) * double(a.BV_cur) * double(a.d), st);
+  hipLaunchKernelGGL((coeff_kernel<E, Q4, SC>), dim3(grid), dim3(kThreads), 0, st, a);
+  return launched();
+}
+
+template <class E, bool Q4>
+orpo_status launch_dhdw(const BwdArgs& a, int grid, hipStream_t st) {
+  TraceScope ts(ORPO_K_DHDW, (a.n_dw ? 4.0 : 2.0) * double(a.C_cur) * double(a.BV_cur) * double(a.d), st);
+  hipLaunchKernelGGL((dhdw_kernel<E, Q4>), dim3(grid), dim3(kThreads), 0, st, a);
+  return launched();
+}
+
+Q4Weight q4_of(const orpo_head_desc* d, const orpo_weight& W) {
+  Q4Weight q;
+  q.wq = (const uint32_t*)W.w;
+  q.scales = (const uint16_t*)W.scales;
+  q.biases = (const uint16_t*)W.biases;
+  q.V = d->V;
+  q.d = d->d;
+  return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t orpo_head_fwd_workspace_bytes(const orpo_head_desc* desc) {
+  Kind k;
+  if (check_desc(desc, &k) != ORPO_OK) return 0;
+  return plan_fwd(desc).ws;
+}
+
+size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc) {
+  Kind k;
+  if (check_desc(desc, &k) != ORPO_OK) return 0;
+  return plan_bwd(desc, k).ws;
+}
+
+size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs) {
+  if (M < 0 || n_pairs < 1) return 0;
+  return kHeader + round_up(size_t(n_pairs) * (2 * 3 + 3) * 8, 256);
+}
+
+orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                          const int32_t* labels, float* logp, float* lse, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+  const FwdPlan p = plan_fwd(desc);
+  if (!ws || ws_bytes < p.ws || (uintptr_t)ws % 256) return ORPO_ENOWS;
+  if (desc->M == 0) return ORPO_OK;
+  if (!h || !labels || !logp || !lse) return ORPO_EINVAL;
+
+  FwdArgs a;
+  a.h = h;
+  a.w = W.w;
+  a.q4 = q4_of(desc, W);
+  a.labels = labels;
+  a.logp = logp;
+  a.part = (float2*)((char*)ws + kHeader);
+  a.status = (uint32_t*)ws;
+  a.M = desc->M;
+  a.d = desc->d;
+  a.V = desc->V;
+  a.cap = desc->softcap;
+  a.ignore_index = desc->ignore_index;
+  a.n_tb = p.n_tb;
+  a.nblk = p.nblk;
+  a.tiles_per_split = p.tps;
+  a.n_vtiles = p.n_vtiles;
+  const int grid = p.n_tb * p.nblk;
+  const bool sc = desc->softcap > 0.f;
+  if (k == kF32) st = sc ? launch_fwd<EF32, false, true>(a, grid, stream) : launch_fwd<EF32, false, false>(a, grid, stream);
+  else if (k == kBf16) st = sc ? launch_fwd<EBf16, false, true>(a, grid, stream) : launch_fwd<EBf16, false, false>(a, grid, stream);
+  else st = sc ? launch_fwd<EBf16, true, true>(a, grid, stream) : launch_fwd<EBf16, true, false>(a, grid, stream);
+  if (st != ORPO_OK) return st;
+  TraceScope ts(ORPO_K_MERGE, 0.0, stream);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)cdiv(desc->M, 256)), dim3(256), 0, stream,
+                     (const float2*)a.part, p.nblk, desc->M, labels, desc->V, desc->ignore_index,
+                     logp, lse, a.status);
+  return launched();
+}
+
+orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, const float* logp,
+                      const int32_t* labels, int64_t V, int32_t ignore_index, double lambda,
+                      double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (M < 0 || M > INT32_MAX || n_pairs < 1 || V <= 0 || V > INT32_MAX) return ORPO_EINVAL;
+  if (!seg_offsets || !out || (M > 0 && (!logp || !labels || !g))) return ORPO_EINVAL;
+  if (!(lambda == lambda)) return ORPO_EINVAL;
+  const size_t need = orpo_loss_workspace_bytes(M, n_pairs);
+  if (!ws || ws_bytes < need || (uintptr_t)ws % 256) return ORPO_ENOWS;
+  LossArgs a;
+  a.M = M;
+  a.V = V;
+  a.P = n_pairs;
+  a.off = seg_offsets;
+  a.logp = logp;
+  a.labels = labels;
+  a.ignore_index = ignore_index;
+  a.lam = lambda;
+  a.out = out;
+  a.g = g;
+  double* base = (double*)((char*)ws + kHeader);
+  a.ell = base;
+  a.dl = base + 2 * size_t(n_pairs);
+  a.cnt = (int64_t*)(base + 4 * size_t(n_pairs));
+  a.pair = base + 6 * size_t(n_pairs);
+  a.status = (uint32_t*)ws;
+  TraceScope ts(ORPO_K_LOSS, 0.0, stream);
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return launched();
+}
+
+orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                          const int32_t* labels, const float* lse, const float* g, float* dh,
+                          float* dW, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+  if (k == kQ4 && dW) return ORPO_EUNSUPPORTED;
+  const BwdPlan p = plan_bwd(desc, k);
+  if (!ws || ws_bytes < p.ws || (uintptr_t)ws % 256) return ORPO_ENOWS;
+  if (desc->M == 0) return ORPO_OK;
+  if (!h || !labels || !lse || !g || !dh) return ORPO_EINVAL;
+
+  BwdArgs a;
+  a.h = h;
+  a.w = W.w;
+  a.q4 = q4_of(desc, W);
+  a.labels = labels;
+  a.lse = lse;
+  a.g = g;
+  a.dh = dh;
+  a.dW = dW;
+  a.coeff = (char*)ws + kHeader;
+  a.M = desc->M;
+  a.d = desc->d;
+  a.V = desc->V;
+  a.BVb = p.BVb;
+  a.cap = desc->softcap;
+  a.ignore_index = desc->ignore_index;
+  a.n_jt = (int)cdiv(desc->d, kTile);
+  const bool sc = desc->softcap > 0.f;
+  const bool acc_dw = (desc->flags & ORPO_DW_ACCUMULATE) != 0;
+  for (int64_t c0 = 0; c0 < desc->M; c0 += p.C) {
+    for (int64_t v0 = 0; v0 < desc->V; v0 += p.BVb) {
+      a.c0 = c0;
+      a.C_cur = std::min(p.C, desc->M - c0);
+      a.v0 = v0;
+      a.BV_cur = std::min(p.BVb, desc->V - v0);
+      a.n_vt = (int)cdiv(a.BV_cur, kTile);
+      a.n_tt = (int)cdiv(a.C_cur, kTile);
+      a.n_dh = a.n_tt * a.n_jt;
+      a.n_dw = dW ? a.n_vt * a.n_jt : 0;
+      a.dh_first = v0 == 0;
+      a.dw_first = c0 == 0 && !acc_dw;
+      const int gc = a.n_vt * a.n_tt, gd = a.n_dh + a.n_dw;
+      if (k == kF32) {
+        st = sc ? launch_coeff<EF32, false, true>(a, gc, stream) : launch_coeff<EF32, false, false>(a, gc, stream);
+        if (st == ORPO_OK) st = launch_dhdw<EF32, false>(a, gd, stream);
+      } else if (k == kBf16) {
+        st = sc ? launch_coeff<EBf16, false, true>(a, gc, stream) : launch_coeff<EBf16, false, false>(a, gc, stream);
+        if (st == ORPO_OK) st = launch_dhdw<EBf16, false>(a, gd, stream);
+      } else {
+        st = sc ? launch_coeff<EBf16, true, true>(a, gc, stream) : launch_coeff<EBf16, true, false>(a, gc, stream);
+        if (st == ORPO_OK) st = launch_dhdw<EBf16, true>(a, gd, stream);
+      }
+      if (st != ORPO_OK) return st;
+    }
+  }
+  return ORPO_OK;
+}
+
+orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes) {
+  if (chunk_tokens < 0 || chunk_tokens % kTile != 0) return ORPO_EINVAL;
+  g_chunk = chunk_tokens ? chunk_tokens : kChunkDefault;
+  g_coeff_budget = coeff_bytes ? coeff_bytes : kCoeffDefault;
+  return ORPO_OK;
+}
+
+orpo_status orpo_trace_enable(int32_t max_launches) {
+  if (max_launches < 0) return ORPO_EINVAL;
+  for (auto& r : g_trace) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.end);
+  }
+  g_trace.clear();
+  g_trace_used = 0;
+  g_trace_on = false;
+  for (int32_t i = 0; i < max_launches; ++i) {
+    TraceRec r{};
+    ORPO_HIP(hipEventCreate(&r.start));
+    ORPO_HIP(hipEventCreate(&r.end));
+    g_trace.push_back(r);
+  }
+  g_trace_on = max_launches > 0;
+  return ORPO_OK;
+}
+
+orpo_status orpo_trace_collect(int32_t kind, int64_t* launches, double* total_ms, double* flops) {
+  if (kind < 0 || kind >= ORPO_K_COUNT || !launches || !total_ms || !flops) return ORPO_EINVAL;
+  *launches = 0;
+  *total_ms = 0.0;
+  *flops = 0.0;
+  for (size_t i = 0; i < g_trace_used; ++i) {
+    const TraceRec& r = g_trace[i];
+    if (r.kind != kind) continue;
+    ORPO_HIP(hipEventSynchronize(r.end));
+    float ms = 0.f;
+    ORPO_HIP(hipEventElapsedTime(&ms, r.start, r.end));
+    *launches += 1;
+    *total_ms += ms;
+    *flops += r.flops;
+  }
+  return ORPO_OK;
+}
+
+orpo_status orpo_trace_reset(void) {
+  g_trace_used = 0;
+  return ORPO_OK;
+}
+
+orpo_status orpo_read_status(const void* ws, uint32_t* status_out, hipStream_t stream) {
+  if (!ws || !status_out) return ORPO_EINVAL;
+  uint32_t v = 0;
+  ORPO_HIP(hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream));
+  ORPO_HIP(hipStreamSynchronize(stream));
+  *status_out = v;
+  return ORPO_OK;
+}
+
+const char* orpo_status_string(orpo_status s) {
+  switch (s) {
+    case ORPO_OK: return "ok";
+    case ORPO_EINVAL: return "invalid argument";
+    case ORPO_EUNSUPPORTED: return "unsupported shape or format";
+    case ORPO_ENOWS: return "workspace missing, misaligned or too small";
+    case ORPO_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t orpo_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+"""Python binding of the C ABI in include/orpo_head.h (argument marshalling only).
+
+Every step of the head runs in the HIP library `liborpo_head.so`; this module checks tensor
+placement and dtypes, allocates outputs and workspaces through PyTorch (device memory and the
+current stream are PyTorch's), and calls the library with ctypes. There is no fallback: if the
+library is missing or the tensors are not on a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+ORPO_F32, ORPO_BF16, ORPO_Q4G64 = 0, 1, 2
+ORPO_DW_ACCUMULATE = 1
+STATUS_BITS = {1: "bad label", 2: "empty branch", 4: "bad segment offsets"}
+IGNORE_INDEX = -100
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liborpo_head.so")
+
+
+class OrpoError(RuntimeError):
+    pass
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("d", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("h_fmt", ctypes.c_int32), ("w_fmt", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("ignore_index", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "orpo_head_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Desc)]),
+    "orpo_head_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Desc)]),
+    "orpo_loss_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "orpo_head_fwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "orpo_loss": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
+                                 ctypes.c_int32, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P]),
+    "orpo_head_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]),
+    "orpo_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
+    "orpo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "orpo_last_hip_error": (ctypes.c_int32, []),
+    "orpo_set_bwd_tiling": (ctypes.c_int, [ctypes.c_int64, ctypes.c_size_t]),
+    "orpo_trace_enable": (ctypes.c_int, [ctypes.c_int32]),
+    "orpo_trace_collect": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
+    "orpo_trace_reset": (ctypes.c_int, []),
+}
+KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw"}
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built in-tree by lm_head_cross_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OrpoError(f"{LIB_PATH} is not built; run `python -m lm_head_cross_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        msg = lib().orpo_status_string(st).decode()
+        raise OrpoError(f"{what}: {msg} (status {st}, hip error {lib().orpo_last_hip_error()})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise OrpoError("tensors must be contiguous and on a GPU")
+
+
+def make_desc(M, d, V, h_dtype, w_fmt, softcap, ignore_index=IGNORE_INDEX, flags=0) -> Desc:
+    h_fmt = ORPO_F32 if h_dtype == torch.float32 else ORPO_BF16
+    return Desc(M, d, V, h_fmt, w_fmt, float(softcap), ignore_index, flags)
+
+
+def _w_fmt(w, scales):
+    if scales is not None:
+        return ORPO_Q4G64
+    return ORPO_F32 if w.dtype == torch.float32 else ORPO_BF16
+
+
+def _vocab(w, scales):
+    return w.shape[0]
+
+
+def _workspace(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def set_bwd_tiling(chunk_tokens: int = 0, coeff_bytes: int = 0):
+    """Token chunk and coefficient-tile budget of the backward (0 restores the defaults)."""
+    _check(lib().orpo_set_bwd_tiling(chunk_tokens, coeff_bytes), "orpo_set_bwd_tiling")
+
+
+def read_status(ws: torch.Tensor) -> int:
+    v = ctypes.c_uint32(0)
+    _check(lib().orpo_read_status(_ptr(ws), ctypes.byref(v), _stream(ws.device)), "orpo_read_status")
+    return int(v.value)
+
+
+def head_fwd(h, w, labels, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None, biases=None,
+             return_ws=False):
+    """logp[M], lse[M] (float32). `w` is W[V,d] (f32/bf16) or the packed q4 words [V,d/8] (int32)."""
+    _need_gpu(h, w, labels, scales, biases)
+    M, d = h.shape
+    V = _vocab(w, scales)
+    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
+    L = lib()
+    ws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(desc)), h.device)
+    logp = torch.empty(M, dtype=torch.float32, device=h.device)
+    lse = torch.empty(M, dtype=torch.float32, device=h.device)
+    wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
+                None if biases is None else biases.data_ptr())
+    _check(L.orpo_head_fwd(ctypes.byref(desc), _ptr(h), wt, _ptr(labels), _ptr(logp), _ptr(lse),
+                           _ptr(ws), ws.numel(), _stream(h.device)), "orpo_head_fwd")
+    return (logp, lse, ws) if return_ws else (logp, lse)
+
+
+def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, return_ws=False):
+    """out (float64 [5 + 2P]: loss, nll, or, accuracy, margin, lw[P], lr[P]) and g[M] (float32)."""
+    _need_gpu(logp, labels, seg_offsets)
+    M = logp.shape[0]
+    P = (seg_offsets.shape[0] - 1) // 2
+    L = lib()
+    ws = _workspace(L.orpo_loss_workspace_bytes(M, P), logp.device)
+    out = torch.empty(5 + 2 * P, dtype=torch.float64, device=logp.device)
+    g = torch.empty(M, dtype=torch.float32, device=logp.device)
+    _check(L.orpo_loss(M, P, _ptr(seg_offsets), _ptr(logp), _ptr(labels), V, ignore_index, float(lam),
+                       _ptr(out), _ptr(g), _ptr(ws), ws.numel(), _stream(logp.device)), "orpo_loss")
+    return (out, g, ws) if return_ws else (out, g)
+
+
+def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNORE_INDEX,
+             scales=None, biases=None, dW=None, accumulate=False):
+    """dh[M,d] and dW[V,d] (float32; dW None when want_dW is False)."""
+    _need_gpu(h, w, labels, lse, g, scales, biases, dW)
+    M, d = h.shape
+    V = _vocab(w, scales)
+    flags = ORPO_DW_ACCUMULATE if accumulate else 0
+    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, flags)
+    L = lib()
+    ws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc)), h.device)
+    dh = torch.empty(M, d, dtype=torch.float32, device=h.device)
+    if want_dW and dW is None:
+        dW = torch.empty(V, d, dtype=torch.float32, device=h.device)
+    if not want_dW:
+        dW = None
+    wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
+                None if biases is None else biases.data_ptr())
+    _check(L.orpo_head_bwd(ctypes.byref(desc), _ptr(h), wt, _ptr(labels), _ptr(lse), _ptr(g),
+                           _ptr(dh), _ptr(dW), _ptr(ws), ws.numel(), _stream(h.device)), "orpo_head_bwd")
+    return dh, dW
+
+
+# ------------------------------------------------------------------------------------------------
+# Tracing (HIP event pairs recorded by the library around each of its launches)
+# ------------------------------------------------------------------------------------------------
+def trace_enable(max_launches: int):
+    _check(lib().orpo_trace_enable(int(max_launches)), "orpo_trace_enable")
+
+
+def trace_reset():
+    _check(lib().orpo_trace_reset(), "orpo_trace_reset")
+
+
+def trace_collect() -> dict:
+    """{kind: (launches, total_ms, algorithmic_flops)} for the launches recorded since the reset."""
+    res = {}
+    for k, name in KERNEL_KINDS.items():
+        n, ms, fl = ctypes.c_int64(0), ctypes.c_double(0), ctypes.c_double(0)
+        _check(lib().orpo_trace_collect(k, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)),
+               "orpo_trace_collect")
+        res[name] = (int(n.value), float(ms.value), float(fl.value))
+    return res
+
+
+# ------------------------------------------------------------------------------------------------
+# A preallocated head step: fwd -> loss -> bwd with every buffer and workspace allocated once.
+# ------------------------------------------------------------------------------------------------
+class HeadStep:
+    def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
+                 want_dW=True, ignore_index=IGNORE_INDEX):
+        _need_gpu(h, w, labels, seg_offsets, scales, biases)
+        self.h, self.w, self.labels, self.off = h, w, labels, seg_offsets
+        self.scales, self.biases = scales, biases
+        self.M, self.d = h.shape
+        self.V, self.softcap, self.lam, self.ignore = V, float(softcap), float(lam), ignore_index
+        self.P = (seg_offsets.shape[0] - 1) // 2
+        dev = h.device
+        self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
+        L = lib()
+        self.fws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(self.desc)), dev)
+        self.bws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(self.desc)), dev)
+        self.lws = _workspace(L.orpo_loss_workspace_bytes(self.M, self.P), dev)
+        self.logp = torch.empty(self.M, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(self.M, dtype=torch.float32, device=dev)
+        self.out = torch.empty(5 + 2 * self.P, dtype=torch.float64, device=dev)
+        self.g = torch.empty(self.M, dtype=torch.float32, device=dev)
+        self.dh = torch.empty(self.M, self.d, dtype=torch.float32, device=dev)
+        self.dW = torch.empty(V, self.d, dtype=torch.float32, device=dev) if want_dW else None
+        self.wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
+                         None if biases is None else biases.data_ptr())
+        self.stream = None
+
+    def _s(self):
+        return _stream(self.h.device)
+
+    def forward(self):
+        _check(lib().orpo_head_fwd(ctypes.byref(self.desc), _ptr(self.h), self.wt, _ptr(self.labels),
+                                   _ptr(self.logp), _ptr(self.lse), _ptr(self.fws), self.fws.numel(),
+                                   self._s()), "orpo_head_fwd")
+
+    def loss(self):
+        _check(lib().orpo_loss(self.M, self.P, _ptr(self.off), _ptr(self.logp), _ptr(self.labels),
+                               self.V, self.ignore, self.lam, _ptr(self.out), _ptr(self.g),
+                               _ptr(self.lws), self.lws.numel(), self._s()), "orpo_loss")
+
+    def backward(self):
+        _check(lib().orpo_head_bwd(ctypes.byref(self.desc), _ptr(self.h), self.wt, _ptr(self.labels),
+                                   _ptr(self.lse), _ptr(self.g), _ptr(self.dh), _ptr(self.dW),
+                                   _ptr(self.bws), self.bws.numel(), self._s()), "orpo_head_bwd")
+
+    def step(self):
+        self.forward()
+        self.loss()
+        self.backward()
+
+    def workspace_bytes(self) -> int:
+        return self.fws.numel() + self.bws.numel() + self.lws.numel()

@@ -1,0 +1,108 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/orpo_head.h declares,
+and rejects bad arguments on the host before anything is enqueued (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lm_head_cross_amd import head as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+EINVAL, EUNSUP, ENOWS = -1, -2, -3
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "orpo_head.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(orpo_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = H.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def _desc(M=512, d=256, V=4096, h=H.ORPO_BF16, w=H.ORPO_BF16, cap=0.0, flags=0):
+    return H.Desc(M, d, V, h, w, cap, -100, flags)
+
+
+def test_workspace_sizes():
+    L = H.lib()
+    d = _desc(M=8192, d=2560, V=262144)
+    fws = L.orpo_head_fwd_workspace_bytes(ctypes.byref(d))
+    bws = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
+    assert fws == 256 + 16 * 8192 * 8          # 16 vocabulary splits of 64 tiles, float2 each
+    assert bws == 256 + 8192 * 16384 * 2       # a 256 MiB bf16 coefficient tile
+    # The backward workspace does not grow with M past one chunk.
+    d2 = _desc(M=32768, d=2560, V=262144)
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d2)) == bws
+    assert L.orpo_loss_workspace_bytes(100, 4) == 256 + 512
+    assert L.orpo_loss_workspace_bytes(100, 0) == 0
+    assert L.orpo_head_fwd_workspace_bytes(ctypes.byref(_desc(d=100))) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=100), EUNSUP),                    # d not a multiple of 64
+    (dict(h=H.ORPO_F32, w=H.ORPO_BF16), EUNSUP),
+    (dict(h=H.ORPO_F32, w=H.ORPO_Q4G64), EUNSUP),
+    (dict(h=7), EINVAL),
+    (dict(M=-1), EINVAL),
+    (dict(V=0), EINVAL),
+    (dict(flags=8), EINVAL),
+])
+def test_fwd_rejects_bad_descriptors(kw, code):
+    L = H.lib()
+    d = _desc(**kw)
+    w = H.Weight(16, None, None)
+    assert L.orpo_head_fwd(ctypes.byref(d), 16, w, 16, 16, 16, 4096, 1 << 30, None) == code
+
+
+def test_fwd_rejects_bad_weights_and_workspace():
+    L = H.lib()
+    d = _desc()
+    assert L.orpo_head_fwd(ctypes.byref(d), 16, H.Weight(None, None, None), 16, 16, 16, 4096, 1 << 30, None) == EINVAL
+    assert L.orpo_head_fwd(ctypes.byref(d), 16, H.Weight(16, 16, None), 16, 16, 16, 4096, 1 << 30, None) == EINVAL
+    q = _desc(w=H.ORPO_Q4G64)
+    assert L.orpo_head_fwd(ctypes.byref(q), 16, H.Weight(16, None, None), 16, 16, 16, 4096, 1 << 30, None) == EINVAL
+    assert L.orpo_head_fwd(ctypes.byref(d), 16, H.Weight(16, None, None), 16, 16, 16, None, 1 << 30, None) == ENOWS
+    assert L.orpo_head_fwd(ctypes.byref(d), 16, H.Weight(16, None, None), 16, 16, 16, 4096, 255, None) == ENOWS
+    assert L.orpo_head_fwd(ctypes.byref(d), 16, H.Weight(16, None, None), 16, 16, 16, 4100, 1 << 30, None) == ENOWS
+    assert L.orpo_head_fwd(ctypes.byref(d), None, H.Weight(16, None, None), 16, 16, 16, 4096, 1 << 30, None) == EINVAL
+
+
+def test_bwd_rejects_dW_for_quantised_head():
+    L = H.lib()
+    q = _desc(w=H.ORPO_Q4G64)
+    st = L.orpo_head_bwd(ctypes.byref(q), 16, H.Weight(16, 16, 16), 16, 16, 16, 16, 16, 4096, 1 << 30, None)
+    assert st == EUNSUP
+
+
+def test_loss_rejects_bad_arguments():
+    L = H.lib()
+    assert L.orpo_loss(10, 0, 16, 16, 16, 100, -100, 0.1, 16, 16, 4096, 4096, None) == EINVAL
+    assert L.orpo_loss(-1, 1, 16, 16, 16, 100, -100, 0.1, 16, 16, 4096, 4096, None) == EINVAL
+    assert L.orpo_loss(10, 1, None, 16, 16, 100, -100, 0.1, 16, 16, 4096, 4096, None) == EINVAL
+    assert L.orpo_loss(10, 1, 16, 16, 16, 100, -100, float("nan"), 16, 16, 4096, 4096, None) == EINVAL
+    assert L.orpo_loss(10, 1, 16, 16, 16, 100, -100, 0.1, 16, 16, 4096, 16, None) == ENOWS
+
+
+def test_bwd_tiling_knob_validates_and_resizes():
+    L = H.lib()
+    assert L.orpo_set_bwd_tiling(100, 0) == EINVAL
+    d = _desc(M=4096, d=256, V=4096)
+    try:
+        assert L.orpo_set_bwd_tiling(512, 512 * 1024 * 2) == 0
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 512 * 1024 * 2
+    finally:
+        assert L.orpo_set_bwd_tiling(0, 0) == 0
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 4096 * 4096 * 2
+
+
+def test_status_strings():
+    L = H.lib()
+    assert L.orpo_status_string(0) == b"ok"
+    assert b"workspace" in L.orpo_status_string(ENOWS)

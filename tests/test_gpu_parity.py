@@ -1,0 +1,184 @@
+"""GPU parity: the HIP head (through the C ABI) against the float64 oracle, element by element, on
+the same seeded inputs. Sizes are ones the oracle finishes in seconds but that still span several
+256-wide tiles and ragged tails in M and V; the full-size configurations are covered by
+test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+import torch
+
+from lm_head_cross_amd import head as H
+from lm_head_cross_amd import synth
+from oracle import orpo_oracle as orc
+from tests.gpu_helpers import (TOL_GRAD, assert_parity, dev, rel, run_gpu, run_oracle, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_config(cfg, seed=0):
+    say(f"[case] {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V} cap={cfg.softcap} seed={seed}")
+    inp = synth.make_inputs(cfg, seed=seed, label_device="cuda")
+    gpu = run_gpu(inp)
+    assert gpu["fwd_status"] == 0 and gpu["loss_status"] == 0
+    ora = run_oracle(inp)
+    return assert_parity(gpu, ora, cfg.name)
+
+
+def test_tiny_f32_full():
+    errs = _check_config(synth.CONFIGS[1])
+    # fp32 operands: far inside the gates.
+    assert errs["logp"] < 1e-5 and errs["dh"] < 1e-4 and errs["dW"] < 1e-4
+
+
+def test_minicpm_shape_one_pair():
+    _check_config(synth.reduced(synth.CONFIGS[2], 1))
+
+
+def test_e4b_shape_one_pair():
+    _check_config(synth.reduced(synth.CONFIGS[3], 1))
+
+
+def test_q4_head_one_pair():
+    _check_config(synth.reduced(synth.CONFIGS[4], 1))
+
+
+def test_12b_shape_short_pair():
+    cfg = synth.CONFIGS[5].replace(pairs=1, M=512, len_lo=200, len_hi=256, name="12b-like-short")
+    _check_config(cfg)
+
+
+# ------------------------------------------------------------------------------------------
+# Hand-built shapes: ragged M and V, ignored tokens inside branches, padding, softcap on/off,
+# and the backward's token-chunk x vocabulary-block loop forced to several iterations.
+# ------------------------------------------------------------------------------------------
+def _custom(M, d, V, dtype, cap, lam, seed, pairs=2, q4=False):
+    rng = np.random.default_rng(seed)
+    cfg = synth.HeadConfig(0, f"custom-M{M}-d{d}-V{V}-{dtype}-cap{cap}", M=M, d=d, V=V, pairs=pairs,
+                           len_lo=1, len_hi=M, softcap=cap, lam=lam, dtype=dtype, q4=q4)
+    h64 = rng.standard_normal((M, d))
+    w32 = (rng.standard_normal((V, d)) * (3.0 / np.sqrt(d))).astype(np.float32)
+    if dtype == "f32":
+        h, w = torch.from_numpy(h64.astype(np.float32)), torch.from_numpy(w32)
+    else:
+        h, w = synth.to_bf16(h64), synth.to_bf16(w32)
+    # Branch lengths: ragged, leaving a padded tail.
+    used = max(2 * pairs, (M * 7) // 8)
+    cuts = np.sort(rng.choice(np.arange(1, used), size=2 * pairs - 1, replace=False))
+    off = np.concatenate([[0], cuts, [used]]).astype(np.int32)
+    labels = rng.integers(0, V, size=M).astype(np.int32)
+    labels[used:] = -100
+    # Ignore a few tokens inside branches, but never a whole branch.
+    for b in range(2 * pairs):
+        if off[b + 1] - off[b] >= 3:
+            labels[off[b] + 1] = -100
+    wq = scales = biases = None
+    if q4:
+        wq, scales, biases = synth.encode_q4(w32, 64)
+        w = None
+    return synth.HeadInputs(cfg, seed, h, w, wq, scales, biases, labels, off, np.diff(off))
+
+
+CUSTOM = [
+    (300, 64, 1000, "bf16", 0.0, 0.1),
+    (513, 128, 257, "bf16", 30.0, 0.5),
+    (37, 192, 7, "bf16", 5.0, 1.0),
+    (260, 256, 2000, "f32", 2.0, 0.1),
+    (700, 320, 3001, "bf16", 30.0, 0.2),
+]
+
+
+@pytest.mark.parametrize("M,d,V,dtype,cap,lam", CUSTOM)
+def test_ragged_shapes(M, d, V, dtype, cap, lam):
+    inp = _custom(M, d, V, dtype, cap, lam, seed=M + V)
+    say(f"[case] {inp.cfg.name}")
+    assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name)
+
+
+def test_ragged_q4():
+    inp = _custom(300, 128, 1000, "bf16", 30.0, 0.1, seed=9, q4=True)
+    say(f"[case] {inp.cfg.name} q4")
+    assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name + "-q4")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_chunk_and_block_loop(dtype):
+    # C = 256 tokens and a 512-wide vocabulary block: 3 chunks x 3 blocks.
+    inp = _custom(600, 128, 1500, dtype, 30.0, 0.1, seed=77)
+    esize = 4 if dtype == "f32" else 2
+    say(f"[case] chunk/block loop {dtype}")
+    H.set_bwd_tiling(256, 256 * 512 * esize)
+    try:
+        gpu = run_gpu(inp)
+    finally:
+        H.set_bwd_tiling(0, 0)
+    assert_parity(gpu, run_oracle(inp), "chunked-" + dtype)
+
+
+def test_zero_weights_closed_form():
+    inp = _custom(300, 64, 4096, "bf16", 0.0, 0.1, seed=3)
+    inp.w.zero_()
+    gpu = run_gpu(inp)
+    valid = inp.labels != -100
+    assert np.allclose(gpu["logp"][valid], -np.log(4096.0), rtol=0, atol=2e-6)
+    assert np.all(gpu["logp"][~valid] == 0)
+    assert np.all(gpu["dh"] == 0)
+
+
+def test_deterministic_bitwise():
+    inp = synth.make_inputs(synth.reduced(synth.CONFIGS[2], 1), seed=4, label_device="cuda")
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    for k in ("logp", "lse", "g", "dh", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["loss"] == b["loss"]
+
+
+def test_dw_accumulate_adds():
+    inp = _custom(300, 128, 1000, "bf16", 0.0, 0.1, seed=5)
+    d = dev()
+    h, w = inp.h.to(d), inp.w.to(d)
+    labels = torch.from_numpy(inp.labels).to(d)
+    off = torch.from_numpy(inp.seg_offsets).to(d)
+    logp, lse = H.head_fwd(h, w, labels, 0.0)
+    _, g = H.orpo_loss(logp, labels, off, 1000, 0.1)
+    _, dW1 = H.head_bwd(h, w, labels, lse, g, 0.0)
+    dW2 = dW1.clone()
+    H.head_bwd(h, w, labels, lse, g, 0.0, dW=dW2, accumulate=True)
+    torch.cuda.synchronize()
+    assert rel(dW2.cpu().numpy(), 2 * dW1.cpu().numpy()) < 1e-6
+
+
+def test_status_bits_and_nan_outputs():
+    d = dev()
+    inp = _custom(300, 64, 1000, "bf16", 0.0, 0.1, seed=6)
+    labels = inp.labels.copy()
+    labels[0] = 5000                      # out of range: flagged, treated as ignored
+    lab = torch.from_numpy(labels).to(d)
+    h, w = inp.h.to(d), inp.w.to(d)
+    logp, lse, ws = H.head_fwd(h, w, lab, 0.0, return_ws=True)
+    assert H.read_status(ws) & 1
+    assert logp[0].item() == 0.0
+    # Empty branch: every token of branch 1 ignored.
+    labels2 = inp.labels.copy()
+    labels2[inp.seg_offsets[1]:inp.seg_offsets[2]] = -100
+    lab2 = torch.from_numpy(labels2).to(d)
+    logp2, _ = H.head_fwd(h, w, lab2, 0.0)
+    out, g, lws = H.orpo_loss(logp2, lab2, torch.from_numpy(inp.seg_offsets).to(d), 1000, 0.1,
+                              return_ws=True)
+    assert H.read_status(lws) & 2
+    assert np.isnan(out[0].item())
+    # Non-monotone offsets.
+    bad = inp.seg_offsets.copy()
+    bad[1], bad[2] = bad[2], bad[1]
+    out, g, lws = H.orpo_loss(logp, lab, torch.from_numpy(bad).to(d), 1000, 0.1, return_ws=True)
+    assert H.read_status(lws) & 4
+    assert np.isnan(out[0].item()) and torch.isnan(g).all().item()
+    # The loss epilogue on the GPU's own logp vector matches the oracle's epilogue on it.
+    out, g = H.orpo_loss(logp, lab, torch.from_numpy(inp.seg_offsets).to(d), 1000, 0.1)
+    lv = logp.cpu().numpy().astype(np.float64)
+    lab_ok = np.where((labels >= 0) & (labels < 1000), labels, -100)
+    ell, n = orc.branch_means(lv, lab_ok, inp.seg_offsets)
+    ep = orc.orpo_epilogue(ell, 0.1)
+    gref = orc.token_cotangent(ep["dL_dell"], n, lab_ok, inp.seg_offsets)
+    o = out.cpu().numpy()
+    assert abs(o[0] - ep["loss"]) <= 1e-12 * abs(ep["loss"]) + 1e-13
+    assert rel(g.cpu().numpy(), gref) < 1e-6
