@@ -1,19 +1,28 @@
 // gemm_core.hpp — the CDNA4 (gfx950) MFMA tile engine shared by every head kernel.
 //
 // One workgroup of 512 threads (8 wave64s) computes a 256 x 256 fp32 tile C[m][n] = sum_k
-// A[m][k] B[k][n] with the 32x32 MFMA (bf16: v_mfma_f32_32x32x16_bf16, fp32: 4x
+// A[m][k] B[k][n] with the 32x32 MFMA (bf16: v_mfma_f32_32x32x16_bf16; fp32: 4 x
 // v_mfma_f32_32x32x2f32 per 8-wide k group). Waves sit in a 2 (m) x 4 (n) grid; each owns a
 // 128 x 64 sub-tile = 4 x 2 MFMA blocks = 128 accumulator registers per lane.
 //
-// Operands are staged through LDS in two stages of 128 bytes of K per row (64 bf16 / 32 fp32),
-// double-buffered with one barrier per K step. Each operand tile keeps its global orientation:
-//   K-major  ([rows][k], k contiguous)  -> LDS [256 rows][144 B], fragments via ds_read_b128;
-//   MN-major ([k][cols], cols contiguous) -> LDS [BK rows][cols + pad], fragments via the gfx950
-//            transposing LDS read (ds_read_b64_tr_b16) for bf16, 4 scalar reads for fp32.
+// Operands are staged through LDS, 128 bytes of K per row per stage (64 bf16 / 32 fp32), in two
+// stages with one barrier per K step. Dense operands go global -> LDS directly
+// (buffer_load_dwordx4 ... lds): each wave instruction fills 1 KiB of LDS, lane l writing bytes
+// [16 l, 16 l + 16), and the buffer descriptor's range check returns zeros past the operand's last
+// valid row, so tails need no VALU work and loads need no staging registers. 4-bit weights take a
+// register path that dequantises on the way into LDS.
+//
+// Each operand tile keeps its global orientation in LDS, unpadded and XOR-swizzled per 16-byte
+// chunk (chunk c of row r is stored at chunk c ^ swz(r)):
+//   K-major  ([rows][k], k contiguous):   [256 rows][128 B], swz = (r ^ (r >> 3)) & 7;
+//                                          fragments via ds_read_b128.
+//   MN-major ([k][cols], cols contiguous): bf16 [64 rows][512 B], swz = 10 (r & 3);
+//                                          fragments via the transposing ds_read_b64_tr_b16.
+//                                          fp32 [32 rows][1024 B], swz = 8 ((r >> 2) & 1);
+//                                          fragments via 4 scalar reads.
+// The swizzles keep both the 16-byte fragment reads and the transposing reads on distinct banks.
 // So the forward (A = W, B = h, both K-major), the dh GEMM (A = coeff K-major, B = W N-major) and
-// the dW GEMM (A = coeff M-major, B = h N-major) all run on the same engine without any
-// transposed copy in HBM. Row pitches are padded so that both the 16-byte fragment reads and the
-// transposing reads hit distinct LDS banks.
+// the dW GEMM (A = coeff M-major, B = h N-major) run on one engine with no transposed copy in HBM.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,45 +36,57 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kThreads = 512;
-constexpr int kTile = 256;              // tile extent in m and n
-constexpr int kKBytes = 128;            // bytes of K per stage per row
-constexpr int kKPitch = 144;            // K-major LDS row pitch (128 + 16 pad)
-constexpr int kStageBytes = 36864;      // LDS bytes of one operand stage
-constexpr int kLdsBytes = 4 * kStageBytes;
-constexpr int kKGroups = 4;             // MFMA k groups per stage (bf16: 4 x 16, fp32: 4 x 8)
+constexpr int kTile = 256;                  // tile extent in m and n
+constexpr int kKBytes = 128;                // bytes of K per stage per row
+constexpr int kStageBytes = 32768;          // LDS bytes of one operand stage
+constexpr int kLdsBytes = 4 * kStageBytes;  // A and B, two stages each
+constexpr int kKGroups = 4;                 // MFMA k groups per stage (bf16: 4 x 16, fp32: 4 x 8)
+constexpr uint32_t kBufferFlags = 0x00020000u;   // raw buffer descriptor word 3 (32-bit data format)
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ int swz_k(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_mn16(int r) { return 10 * (r & 3); }
+__device__ __forceinline__ int swz_mn32(int r) { return ((r >> 2) & 1) << 3; }
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Wait until this wave's outstanding vector-memory operations (including LDS-direct loads) are done.
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(uint32_t)n, (int)kBufferFlags);
+}
 
 // ------------------------------------------------------------------------------------------
-// Element policies: storage type, K per stage, MN-major pitch, fragment reads and the MFMA step.
-// A fragment is 16 bytes per lane: for the 32-row block starting at row0, lane l holds row
-// row0 + l % 32 and k slots kg*KG + (l / 32) * KG/2 + [0, KG/2) with KG = 16 (bf16) or 8 (fp32).
-// Any consistent k-slot assignment gives the same sum, as long as A and B use the same one.
+// Element policies: K per stage, fragment reads and the MFMA step. A fragment is 16 bytes per
+// lane: for the 32-row block starting at row0, lane l holds row row0 + l % 32 and k slots
+// kg*KG + (l / 32) * KG/2 + [0, KG/2) with KG = 16 (bf16) or 8 (fp32). Any consistent k-slot
+// assignment gives the same sum, as long as A and B use the same one.
 // ------------------------------------------------------------------------------------------
 struct EBf16 {
   typedef __bf16 T;
   typedef bf16x8 Frag;
   static constexpr int kSize = 2;
-  static constexpr int kBK = 64;        // K elements per stage
-  static constexpr int kMnPitch = 576;  // MN-major LDS row pitch: 256 * 2 + 64 pad
+  static constexpr int kBK = 64;           // K elements per stage
+  static constexpr int kMnRows = 64;       // rows of an MN-major stage
+  static constexpr int kMnChunks = 32;     // 16-byte chunks per MN-major row
 
   static __device__ __forceinline__ Frag frag_k(const char* s, int row0, int kg, int l) {
-    return *(const Frag*)(s + (row0 + (l & 31)) * kKPitch + kg * 32 + (l >> 5) * 16);
+    const int r = row0 + (l & 31), c = kg * 2 + (l >> 5);
+    return *(const Frag*)(s + r * kKBytes + ((c ^ swz_k(r)) << 4));
   }
-  // Transposing read: within each 16-lane group, source lane s reads 4 contiguous columns of row
-  // (k0 + s/4); the hardware hands output lane j, slot i the element j%4 of source lane 4i + j/4,
-  // i.e. column j of row k0 + i. Two reads give the 8 k slots of the lane's column.
+  // Transposing read: within each 16-lane group, source lane q reads 4 contiguous columns of row
+  // (k0 + q/4); the hardware hands output lane j, slot i the element j%4 of source lane 4i + j/4,
+  // i.e. column j of row k0 + i. Two reads (rows k0..k0+3 and k0+4..k0+7) give the lane's 8 k slots.
   static __device__ __forceinline__ Frag frag_mn(const char* s, int col0, int kg, int l) {
     const int g = l >> 4, q = l & 15;
     const int row = kg * 16 + 8 * (g >> 1) + (q >> 2);
     const int col = col0 + 16 * (g & 1) + 4 * (q & 3);
-    const char* p = s + row * kMnPitch + col * 2;
+    const char* p = s + row * (kMnChunks * 16) + (((col >> 3) ^ swz_mn16(row)) << 4) + (col & 7) * 2;
     i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * kMnPitch));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * kMnChunks * 16));
     i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(Frag, v);
   }
@@ -79,18 +100,22 @@ struct EF32 {
   typedef f32x4 Frag;
   static constexpr int kSize = 4;
   static constexpr int kBK = 32;
-  static constexpr int kMnPitch = 1056;  // 256 * 4 + 32 pad
+  static constexpr int kMnRows = 32;
+  static constexpr int kMnChunks = 64;
 
   static __device__ __forceinline__ Frag frag_k(const char* s, int row0, int kg, int l) {
-    return *(const Frag*)(s + (row0 + (l & 31)) * kKPitch + kg * 32 + (l >> 5) * 16);
+    const int r = row0 + (l & 31), c = kg * 2 + (l >> 5);
+    return *(const Frag*)(s + r * kKBytes + ((c ^ swz_k(r)) << 4));
   }
   static __device__ __forceinline__ Frag frag_mn(const char* s, int col0, int kg, int l) {
-    const char* p = s + (kg * 8 + (l >> 5) * 4) * kMnPitch + (col0 + (l & 31)) * 4;
+    const int row = kg * 8 + (l >> 5) * 4;        // rows row .. row+3 share one swizzle
+    const int col = col0 + (l & 31);
+    const char* p = s + row * (kMnChunks * 16) + (((col >> 2) ^ swz_mn32(row)) << 4) + (col & 3) * 4;
     Frag f;
     f[0] = *(const float*)(p);
-    f[1] = *(const float*)(p + kMnPitch);
-    f[2] = *(const float*)(p + 2 * kMnPitch);
-    f[3] = *(const float*)(p + 3 * kMnPitch);
+    f[1] = *(const float*)(p + kMnChunks * 16);
+    f[2] = *(const float*)(p + 2 * kMnChunks * 16);
+    f[3] = *(const float*)(p + 3 * kMnChunks * 16);
     return f;
   }
   static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b) {
@@ -102,40 +127,69 @@ struct EF32 {
 };
 
 // ------------------------------------------------------------------------------------------
-// Global -> register -> LDS loaders. A tile is 2048 chunks of 16 bytes: 4 per thread.
+// Dense loaders: global -> LDS directly. A stage is 2048 chunks of 16 bytes; wave w issues
+// instructions i = 0..3 filling LDS bytes [(4w + i) KiB, +1 KiB), lane l the chunk 64 (4w + i) + l.
 // ------------------------------------------------------------------------------------------
 
-// Dense tile of TR rows x (CPR * 16) bytes of a row-major global matrix; rows >= n_rows and
-// bytes >= row_bytes are zero-filled (row_bytes is a multiple of 16).
-template <int TR, int CPR>
-struct DenseTile {
-  static constexpr int kPer = TR * CPR / kThreads;
-  static_assert(kPer * kThreads == TR * CPR, "tile must split evenly over the workgroup");
-  u32x4 v[kPer];
-
-  __device__ __forceinline__ void load(const char* base, int64_t ld_bytes, int64_t row0,
-                                       int64_t col0_bytes, int64_t n_rows, int64_t row_bytes,
-                                       int tid) {
+// K-major operand: rows [row0, row0 + 256) of a row-major matrix, bytes [kb, kb + 128) of each row.
+struct DmaK {
+  const char* base;
+  int64_t ld, n_rows;
+  uint32_t voff[4];
+  __device__ __forceinline__ void init(const void* b, int64_t ld_bytes, int64_t rows) {
+    base = (const char*)b;
+    ld = ld_bytes;
+    n_rows = rows;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / CPR, cc = c % CPR;
-      const int64_t gr = row0 + r;
-      const int64_t gb = col0_bytes + cc * 16;
-      const bool ok = gr < n_rows && gb < row_bytes;
-      const u32x4 x = *(const u32x4*)(base + (ok ? gr * ld_bytes + gb : 0));
-      v[i] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+      const int j = (4 * w + i) * 64 + l;
+      const int r = j >> 3, c = (j & 7) ^ swz_k(j >> 3);
+      voff[i] = (uint32_t)(r * ld_bytes + c * 16);
     }
   }
-  __device__ __forceinline__ void store(char* s, int pitch, int tid) const {
+  __device__ __forceinline__ void issue(int64_t row0, int64_t kb, char* stage) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * ld + kb, (n_rows - row0) * ld - kb);
+    char* s = stage + (threadIdx.x >> 6) * 4096;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + i * kThreads;
-      *(u32x4*)(s + (c / CPR) * pitch + (c % CPR) * 16) = v[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(s + i * 1024), 16, voff[i], 0, 0, 0);
   }
+  __device__ __forceinline__ void commit(char*) const {}
 };
 
+// MN-major operand: rows [k0, k0 + kMnRows) of a row-major matrix, bytes [cb, cb + kMnChunks*16).
+template <class E>
+struct DmaMN {
+  const char* base;
+  int64_t ld, n_rows;
+  uint32_t voff[4];
+  __device__ __forceinline__ void init(const void* b, int64_t ld_bytes, int64_t rows) {
+    base = (const char*)b;
+    ld = ld_bytes;
+    n_rows = rows;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = (4 * w + i) * 64 + l;
+      const int r = j / E::kMnChunks, p = j % E::kMnChunks;
+      const int c = p ^ (E::kSize == 2 ? swz_mn16(r) : swz_mn32(r));
+      voff[i] = (uint32_t)(r * ld_bytes + c * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(int64_t k0, int64_t cb, char* stage) const {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld + cb, (n_rows - k0) * ld - cb);
+    char* s = stage + (threadIdx.x >> 6) * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(s + i * 1024), 16, voff[i], 0, 0, 0);
+  }
+  __device__ __forceinline__ void commit(char*) const {}
+};
+
+// ------------------------------------------------------------------------------------------
+// 4-bit weights: global -> registers -> dequantise -> LDS.
+// ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -164,11 +218,14 @@ struct Q4Weight {
 };
 
 // 4-bit weights as a K-major operand: 256 vocabulary rows x 64 codes (one group) per stage.
-// Thread tid owns row tid/2, codes [32*(tid%2), +32) of the stage's 64.
-struct Q4KTile {
+// Thread tid owns row tid/2, codes [32*(tid%2), +32) of the stage's 64 = logical chunks 4(tid%2)+w.
+struct Q4K {
+  Q4Weight W;
   u32x4 q;
   float scale, bias;
-  __device__ __forceinline__ void load(const Q4Weight& W, int64_t row0, int64_t k0, int tid) {
+  __device__ __forceinline__ void init(const Q4Weight& w) { W = w; }
+  __device__ __forceinline__ void issue(int64_t row0, int64_t k0, char*) {
+    const int tid = threadIdx.x;
     const int64_t gr = row0 + (tid >> 1);
     const bool ok = gr < W.V;
     const int64_t r = ok ? gr : 0;
@@ -179,22 +236,28 @@ struct Q4KTile {
     scale = ok ? s : 0.f;
     bias = ok ? b : 0.f;
   }
-  __device__ __forceinline__ void store(char* s, int /*pitch*/, int tid) const {
-    char* p = s + (tid >> 1) * kKPitch + (tid & 1) * 64;
+  __device__ __forceinline__ void commit(char* stage) const {
+    const int tid = threadIdx.x, r = tid >> 1;
+    char* row = stage + r * kKBytes;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) *(u32x4*)(p + w * 16) = dequant_word(q[w], scale, bias);
+    for (int w = 0; w < 4; ++w)
+      *(u32x4*)(row + (((tid & 1) * 4 + w) ^ swz_k(r)) * 16) = dequant_word(q[w], scale, bias);
   }
 };
 
 // 4-bit weights as an N-major operand (rows = vocabulary = k, columns = hidden = n): 64 rows x
-// 256 codes per stage. Thread tid owns row tid/8, codes [32*(tid%8), +32) of the tile's 256.
-struct Q4NTile {
+// 256 codes per stage. Thread tid owns row tid/8, codes [32*(tid%8), +32) = chunks 4(tid%8)+w.
+struct Q4N {
+  Q4Weight W;
+  int64_t v_end;             // rows >= v_end read as zero
   u32x4 q;
   float scale, bias;
-  __device__ __forceinline__ void load(const Q4Weight& W, int64_t k0, int64_t n0, int tid) {
+  __device__ __forceinline__ void init(const Q4Weight& w, int64_t vend) { W = w; v_end = vend; }
+  __device__ __forceinline__ void issue(int64_t k0, int64_t n0, char*) {
+    const int tid = threadIdx.x;
     const int64_t gr = k0 + (tid >> 3);
     const int64_t gc = n0 + (tid & 7) * 32;
-    const bool ok = gr < W.V && gc < W.d;
+    const bool ok = gr < v_end && gc < W.d;
     const int64_t r = ok ? gr : 0, c = ok ? gc : 0;
     const u32x4 x = *(const u32x4*)(W.wq + r * (W.d >> 3) + (c >> 3));
     const int64_t gi = r * (W.d >> 6) + (c >> 6);
@@ -203,10 +266,12 @@ struct Q4NTile {
     scale = ok ? s : 0.f;
     bias = ok ? b : 0.f;
   }
-  __device__ __forceinline__ void store(char* s, int pitch, int tid) const {
-    char* p = s + (tid >> 3) * pitch + (tid & 7) * 64;
+  __device__ __forceinline__ void commit(char* stage) const {
+    const int tid = threadIdx.x, r = tid >> 3;
+    char* row = stage + r * (EBf16::kMnChunks * 16);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) *(u32x4*)(p + w * 16) = dequant_word(q[w], scale, bias);
+    for (int w = 0; w < 4; ++w)
+      *(u32x4*)(row + (((tid & 7) * 4 + w) ^ swz_mn16(r)) * 16) = dequant_word(q[w], scale, bias);
   }
 };
 
@@ -241,44 +306,69 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][2]) {
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
 }
 
-// The main loop over n_tiles consecutive output tiles of nk K steps each. `issue(tile, ks)`
-// loads the global tiles of step (tile, ks) into the loaders' registers; `epi(tile, acc)` runs
-// after the tile's last K step (before the loop's barrier; it must not touch LDS), then the
-// accumulators are cleared unless kClear is false (single-tile callers read acc afterwards). The next step's global loads are in flight during each step's MFMAs.
-template <class E, bool AK, bool BK, bool kClear = true, class LA, class LB, class Issue, class Epi>
-__device__ __forceinline__ void gemm_run(char* smem, LA& la, LB& lb, int pa, int pb, int n_tiles,
-                                         int nk, Issue&& issue, Epi&& epi, f32x16 (&acc)[4][2]) {
+// LDS of the engine: four distinct objects (A and B, two stages each), so that the compiler can
+// tell a stage being filled by direct loads from the stage being read and does not make the reads
+// wait for the in-flight loads.
+struct Smem {
+  char* a0;
+  char* a1;
+  char* b0;
+  char* b1;
+};
+#define ORPO_DECLARE_SMEM(name)                                        \
+  __shared__ __attribute__((aligned(1024))) char name##_a0[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char name##_a1[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char name##_b0[kStageBytes]; \
+  __shared__ __attribute__((aligned(1024))) char name##_b1[kStageBytes]; \
+  const Smem name = {name##_a0, name##_a1, name##_b0, name##_b1}
+
+// One K step: compute from (ca, cb) while the next step's loads go into (na, nb).
+template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi>
+__device__ __forceinline__ void gemm_step(int& tile, int& ks, int nk, bool more,
+                                          char* __restrict__ ca, char* __restrict__ cb,
+                                          char* __restrict__ na, char* __restrict__ nb,
+                                          Issue& issue, Commit& commit, Epi& epi,
+                                          f32x16 (&acc)[4][2], int wm, int wn, int l) {
+  int nks = ks + 1, ntile = tile;
+  if (nks == nk) { nks = 0; ++ntile; }
+  if (more) issue(ntile, nks, na, nb);
+  compute_stage<E, AK, BK>(ca, cb, acc, wm, wn, l);
+  if (more) commit(na, nb);
+  if (nks == 0) {
+    epi(tile, acc);
+    if (kClear) zero_acc(acc);
+  }
+  vm_wait();
+  __syncthreads();
+  tile = ntile;
+  ks = nks;
+}
+
+// The main loop over n_tiles consecutive output tiles of nk K steps each.
+//   issue(tile, ks, stageA, stageB): start the loads of step (tile, ks) into the given stages;
+//   commit(stageA, stageB): finish register-staged loads into LDS (no-op for direct loads);
+//   epi(tile, acc): runs after the tile's last K step (before the loop's barrier; it must not touch
+//   LDS), then the accumulators are cleared unless kClear is false (single-tile callers read acc
+//   after the loop). The next step's loads are in flight during each step's MFMAs. The loop is
+//   unrolled by two so that every step reads and fills statically known stages.
+template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi>
+__device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Issue&& issue,
+                                         Commit&& commit, Epi&& epi, f32x16 (&acc)[4][2]) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
-  char* sA0 = smem;
-  char* sA1 = smem + kStageBytes;
-  char* sB0 = smem + 2 * kStageBytes;
-  char* sB1 = smem + 3 * kStageBytes;
   const int total = n_tiles * nk;
   if (total <= 0) return;
-  issue(0, 0);
-  la.store(sA0, pa, tid);
-  lb.store(sB0, pb, tid);
+  issue(0, 0, sm.a0, sm.b0);
+  commit(sm.a0, sm.b0);
+  vm_wait();
   __syncthreads();
   int tile = 0, ks = 0;
-  for (int it = 0; it < total; ++it) {
-    const bool odd = it & 1;
-    int nks = ks + 1, ntile = tile;
-    if (nks == nk) { nks = 0; ++ntile; }
-    const bool more = it + 1 < total;
-    if (more) issue(ntile, nks);
-    compute_stage<E, AK, BK>(odd ? sA1 : sA0, odd ? sB1 : sB0, acc, wm, wn, l);
-    if (more) {
-      la.store(odd ? sA0 : sA1, pa, tid);
-      lb.store(odd ? sB0 : sB1, pb, tid);
-    }
-    if (nks == 0) {
-      epi(tile, acc);
-      if (kClear) zero_acc(acc);
-    }
-    __syncthreads();
-    tile = ntile;
-    ks = nks;
+  for (int it = 0; it < total; it += 2) {
+    gemm_step<E, AK, BK, kClear>(tile, ks, nk, it + 1 < total, sm.a0, sm.b0, sm.a1, sm.b1, issue,
+                                 commit, epi, acc, wm, wn, l);
+    if (it + 1 < total)
+      gemm_step<E, AK, BK, kClear>(tile, ks, nk, it + 2 < total, sm.a1, sm.b1, sm.a0, sm.b0, issue,
+                                   commit, epi, acc, wm, wn, l);
   }
 }
 

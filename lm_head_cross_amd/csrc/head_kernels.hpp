@@ -58,7 +58,7 @@ struct FwdArgs {
 
 template <class E, bool Q4, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  ORPO_DECLARE_SMEM(smem);
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
   const int tb = blockIdx.x % a.n_tb, split = blockIdx.x / a.n_tb;
   const int tile0 = split * a.tiles_per_split;
@@ -81,18 +81,21 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   }
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
 
-  typedef typename std::conditional<Q4, Q4KTile, DenseTile<kTile, 8>>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
   LoaderA la;
-  DenseTile<kTile, 8> lb;
+  DmaK lb;
+  if constexpr (Q4) la.init(a.q4); else la.init(a.w, row_bytes, a.V);
+  lb.init(a.h, row_bytes, a.M);
   const int nk = (int)(a.d / E::kBK);
-  auto issue = [&](int tile, int ks) {
+  auto issue = [&](int tile, int ks, char* sa, char* sb) {
     const int64_t v0 = (int64_t)(tile0 + tile) * kTile;
-    if constexpr (Q4) {
-      la.load(a.q4, v0, (int64_t)ks * E::kBK, tid);
-    } else {
-      la.load((const char*)a.w, row_bytes, v0, (int64_t)ks * kKBytes, a.V, row_bytes, tid);
-    }
-    lb.load((const char*)a.h, row_bytes, t0, (int64_t)ks * kKBytes, a.M, row_bytes, tid);
+    if constexpr (Q4) la.issue(v0, (int64_t)ks * E::kBK, sa);
+    else la.issue(v0, (int64_t)ks * kKBytes, sa);
+    lb.issue(t0, (int64_t)ks * kKBytes, sb);
+  };
+  auto commit = [&](char* sa, char* sb) {
+    la.commit(sa);
+    lb.commit(sb);
   };
   auto epi = [&](int tile, f32x16(&acc)[4][2]) {
     const int64_t vt0 = (int64_t)(tile0 + tile) * kTile;
@@ -100,37 +103,44 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     const bool tail = vt0 + kTile > a.V;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      // u = z * log2e (or (z - cap) * log2e under a softcap), masked to -inf past V. Values are
-      // recomputed from the accumulators in each pass instead of being staged in registers.
-      auto masked = [&](int mb, int r) {
-        return tail && vw0 + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3) >= a.V;
-      };
-      float ref = m[nb];
-      if (!SOFTCAP) {
-        float tmax = kNegInf;
+      // u = z * log2e (or (z - cap) * log2e under a softcap), masked past V on the last tile only
+      // (a uniform branch). Values are recomputed from the accumulators in each pass.
+      const int lim = (int)min<int64_t>(max<int64_t>(a.V - vw0, 0), 128);   // valid rows of the wave
+      auto body = [&](auto masked_tag) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        auto keep = [&](int mb, int r) {
+          return !kMasked || mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3) < lim;
+        };
+        float ref = m[nb];
+        if (!SOFTCAP) {
+          float tmax = kNegInf;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+          for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!masked(mb, r)) tmax = fmaxf(tmax, acc[mb][nb][r]);
-        const float mn = fmaxf(m[nb], tmax * kLog2e);
-        if (mn != kNegInf) {
-          s[nb] *= exp2_(m[nb] - mn);   // m = -inf gives 0
-          m[nb] = mn;
-        }
-        ref = m[nb];
-      }
-      float acc_s = 0.f;
-      if (ref != kNegInf) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float raw = acc[mb][nb][r];
-            const float x = SOFTCAP ? sc.kz * sc.r_of(raw) : raw * kLog2e - ref;
-            acc_s += masked(mb, r) ? 0.f : exp2_(x);
+            for (int r = 0; r < 16; ++r)
+              if (keep(mb, r)) tmax = fmaxf(tmax, acc[mb][nb][r]);
+          const float mn = fmaxf(m[nb], tmax * kLog2e);
+          if (mn != kNegInf) {
+            s[nb] *= exp2_(m[nb] - mn);   // m = -inf gives 0
+            m[nb] = mn;
           }
-      }
+          ref = m[nb];
+        }
+        float acc_s = 0.f;
+        if (ref != kNegInf) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float raw = acc[mb][nb][r];
+              const float x = SOFTCAP ? sc.kz * sc.r_of(raw) : raw * kLog2e - ref;
+              const float e = exp2_(x);
+              acc_s += keep(mb, r) ? e : 0.f;
+            }
+        }
+        return acc_s;
+      };
+      const float acc_s = tail ? body(std::true_type{}) : body(std::false_type{});
       s[nb] += acc_s;
       // Target capture: the one lane holding (v = y, t) writes z[y] to logp[t].
       const int64_t off = (int64_t)y[nb] - vw0;
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   };
   f32x16 acc[4][2];
   zero_acc(acc);
-  gemm_run<E, true, true>(smem, la, lb, kKPitch, kKPitch, n_tiles, nk, issue, epi, acc);
+  gemm_run<E, true, true>(smem, n_tiles, nk, issue, commit, epi, acc);
 
   // Combine the lane pair (l, l ^ 32), then the two m-waves, and write this split's partials.
 #pragma unroll
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
       s[nb] += so;
     }
   }
-  float2* red = (float2*)smem;   // [256 tokens]
+  float2* red = (float2*)smem.a0;   // [256 tokens]
   if (wm == 1 && l < 32) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) red[acc_n(wn, nb, l)] = make_float2(m[nb], s[nb]);
@@ -371,7 +381,7 @@ struct BwdArgs {
 
 template <class E, bool Q4, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  ORPO_DECLARE_SMEM(smem);
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
   const int vt = blockIdx.x % a.n_vt, tt = blockIdx.x / a.n_vt;
   const int64_t vbase = a.v0 + (int64_t)vt * kTile;   // global vocabulary row of tile row 0
@@ -379,22 +389,25 @@ __global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
   const int64_t t_end = min(a.M, a.c0 + a.C_cur);
   const int64_t row_bytes = a.d * E::kSize;
 
-  typedef typename std::conditional<Q4, Q4KTile, DenseTile<kTile, 8>>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
   LoaderA la;
-  DenseTile<kTile, 8> lb;
+  DmaK lb;
+  if constexpr (Q4) la.init(a.q4); else la.init(a.w, row_bytes, a.V);
+  lb.init(a.h, row_bytes, t_end);
   const int nk = (int)(a.d / E::kBK);
-  auto issue = [&](int, int ks) {
-    if constexpr (Q4) {
-      la.load(a.q4, vbase, (int64_t)ks * E::kBK, tid);
-    } else {
-      la.load((const char*)a.w, row_bytes, vbase, (int64_t)ks * kKBytes, a.V, row_bytes, tid);
-    }
-    lb.load((const char*)a.h, row_bytes, tbase, (int64_t)ks * kKBytes, t_end, row_bytes, tid);
+  auto issue = [&](int, int ks, char* sa, char* sb) {
+    if constexpr (Q4) la.issue(vbase, (int64_t)ks * E::kBK, sa);
+    else la.issue(vbase, (int64_t)ks * kKBytes, sa);
+    lb.issue(tbase, (int64_t)ks * kKBytes, sb);
+  };
+  auto commit = [&](char* sa, char* sb) {
+    la.commit(sa);
+    lb.commit(sb);
   };
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, true, true, false>(smem, la, lb, kKPitch, kKPitch, 1, nk, issue, nop, acc);
+  gemm_run<E, true, true, false>(smem, 1, nk, issue, commit, nop, acc);
 
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
   typedef typename E::T T;
@@ -476,7 +489,7 @@ __device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, 
 
 template <class E, bool Q4>
 __global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  ORPO_DECLARE_SMEM(smem);
   const int tid = threadIdx.x;
   const int64_t row_bytes = a.d * E::kSize;
   const int64_t cpitch = a.BVb * E::kSize;            // coefficient tile row pitch (bytes)
@@ -490,20 +503,23 @@ __global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
     const int64_t i0 = (int64_t)it * kTile, j0 = (int64_t)jt * kTile;
     const int64_t kv = ((a.BV_cur + kTile - 1) / kTile) * kTile;   // coefficient columns written
     const int nk = (int)((kv + E::kBK - 1) / E::kBK);
-    DenseTile<kTile, 8> la;   // coeff [i][v], K-major
-    typedef typename std::conditional<Q4, Q4NTile, DenseTile<E::kBK, kTile * E::kSize / 16>>::type LoaderB;
-    LoaderB lb;               // W [v][j], N-major
-    auto issue = [&](int, int ks) {
+    const int64_t v_end = min(a.V, a.v0 + a.BV_cur);
+    DmaK la;                                                         // coeff [i][v], K-major
+    la.init(a.coeff, cpitch, a.C_cur);
+    typedef typename std::conditional<Q4, Q4N, DmaMN<E>>::type LoaderB;
+    LoaderB lb;                                                      // W [v][j], N-major
+    if constexpr (Q4) lb.init(a.q4, v_end); else lb.init(a.w, row_bytes, v_end);
+    auto issue = [&](int, int ks, char* sa, char* sb) {
       const int64_t k0 = (int64_t)ks * E::kBK;
-      la.load((const char*)a.coeff, cpitch, i0, k0 * E::kSize, a.C_cur, kv * E::kSize, tid);
-      if constexpr (Q4) {
-        lb.load(a.q4, a.v0 + k0, j0, tid);
-      } else {
-        lb.load((const char*)a.w, row_bytes, a.v0 + k0, j0 * E::kSize,
-                min(a.V, a.v0 + a.BV_cur), row_bytes, tid);
-      }
+      la.issue(i0, k0 * E::kSize, sa);
+      if constexpr (Q4) lb.issue(a.v0 + k0, j0, sb);
+      else lb.issue(a.v0 + k0, j0 * E::kSize, sb);
     };
-    gemm_run<E, true, false, false>(smem, la, lb, kKPitch, E::kMnPitch, 1, nk, issue, nop, acc);
+    auto commit = [&](char* sa, char* sb) {
+      la.commit(sa);
+      lb.commit(sb);
+    };
+    gemm_run<E, true, false, false>(smem, 1, nk, issue, commit, nop, acc);
     store_out<E>(a.dh, a.d, a.c0 + i0, t_end, j0, a.d, a.dh_first != 0, acc);
   } else {
     // m = vocabulary (block rows), n = hidden, k = token of the chunk.
@@ -511,14 +527,20 @@ __global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
     const int vt = bid / a.n_jt, jt = bid % a.n_jt;
     const int64_t vl0 = (int64_t)vt * kTile, j0 = (int64_t)jt * kTile;
     const int nk = (int)((a.C_cur + E::kBK - 1) / E::kBK);
-    DenseTile<E::kBK, kTile * E::kSize / 16> la;   // coeff [i][v], M-major
-    DenseTile<E::kBK, kTile * E::kSize / 16> lb;   // h [i][j], N-major
-    auto issue = [&](int, int ks) {
+    DmaMN<E> la;                                                     // coeff [i][v], M-major
+    la.init(a.coeff, cpitch, a.C_cur);
+    DmaMN<E> lb;                                                     // h [t][j], N-major
+    lb.init(a.h, row_bytes, t_end);
+    auto issue = [&](int, int ks, char* sa, char* sb) {
       const int64_t k0 = (int64_t)ks * E::kBK;
-      la.load((const char*)a.coeff, cpitch, k0, vl0 * E::kSize, a.C_cur, cpitch, tid);
-      lb.load((const char*)a.h, row_bytes, a.c0 + k0, j0 * E::kSize, t_end, row_bytes, tid);
+      la.issue(k0, vl0 * E::kSize, sa);
+      lb.issue(a.c0 + k0, j0 * E::kSize, sb);
     };
-    gemm_run<E, false, false, false>(smem, la, lb, E::kMnPitch, E::kMnPitch, 1, nk, issue, nop, acc);
+    auto commit = [&](char* sa, char* sb) {
+      la.commit(sa);
+      lb.commit(sb);
+    };
+    gemm_run<E, false, false, false>(smem, 1, nk, issue, commit, nop, acc);
     store_out<E>(a.dW, a.d, a.v0 + vl0, min(a.V, a.v0 + a.BV_cur), j0, a.d, a.dw_first != 0, acc);
   }
 }
