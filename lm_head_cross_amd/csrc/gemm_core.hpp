@@ -372,6 +372,15 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
   }
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with
+// its own L2. xcd_remap(b, n) is a bijection of [0, n) under which every XCD processes one
+// contiguous range of logical tiles, so the ~32 tiles an XCD runs at once share operand slices in
+// its L2 instead of each slice being fetched into several L2s.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b & 7, i = b >> 3, q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + i;
+}
+
 // Position of accumulator element r of block (mb, nb) in the 256 x 256 tile.
 __device__ __forceinline__ int acc_m(int wm, int mb, int r, int l) {
   return wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);

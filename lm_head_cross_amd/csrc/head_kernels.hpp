@@ -499,7 +499,8 @@ __global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
   auto nop = [](int, f32x16(&)[4][2]) {};
   if ((int)blockIdx.x < a.n_dh) {
     // m = token (C rows), n = hidden, k = vocabulary of the block.
-    const int it = blockIdx.x / a.n_jt, jt = blockIdx.x % a.n_jt;
+    const int t = xcd_remap(blockIdx.x, a.n_dh);
+    const int it = t / a.n_jt, jt = t % a.n_jt;
     const int64_t i0 = (int64_t)it * kTile, j0 = (int64_t)jt * kTile;
     const int64_t kv = ((a.BV_cur + kTile - 1) / kTile) * kTile;   // coefficient columns written
     const int nk = (int)((kv + E::kBK - 1) / E::kBK);
@@ -523,8 +524,8 @@ __global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
     store_out<E>(a.dh, a.d, a.c0 + i0, t_end, j0, a.d, a.dh_first != 0, acc);
   } else {
     // m = vocabulary (block rows), n = hidden, k = token of the chunk.
-    const int bid = blockIdx.x - a.n_dh;
-    const int vt = bid / a.n_jt, jt = bid % a.n_jt;
+    const int t = xcd_remap(blockIdx.x - a.n_dh, a.n_dw);
+    const int vt = t / a.n_jt, jt = t % a.n_jt;
     const int64_t vl0 = (int64_t)vt * kTile, j0 = (int64_t)jt * kTile;
     const int nk = (int)((a.C_cur + E::kBK - 1) / E::kBK);
     DmaMN<E> la;                                                     // coeff [i][v], M-major
