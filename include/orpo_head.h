@@ -81,7 +81,8 @@ typedef struct {
 
 /* Workspace sizes in bytes (0 on invalid arguments). The forward workspace grows as 256 + 8 * NBLK
  * * M (per-token partials over NBLK vocabulary splits, like lse it is O(M)); the backward
- * workspace is a fixed-size coefficient tile, independent of M beyond one token chunk. */
+ * workspace holds two coefficient tiles of fixed size (double-buffered), independent of M beyond
+ * one token chunk. */
 size_t orpo_head_fwd_workspace_bytes(const orpo_head_desc* desc);
 size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc);
 size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs);
@@ -144,27 +145,29 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
                           const int32_t* labels, const float* lse, const float* g, float* dh,
                           float* dW, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Backward tiling: the token chunk C (a multiple of 256, default 8192) and the byte budget of the
- * coefficient tile [C, BVb] (default 256 MiB; BVb is the largest multiple of 256 that fits, at
- * least 256). 0 restores a default. Process-wide; call it only while no call of this library is in
+/* Backward tiling: the token chunk C (a multiple of 256, default 8192) and the byte budget of one
+ * coefficient tile [C, BVb] (default 256 MiB, two are used; BVb is the largest multiple of 256
+ * that fits, at least 256). 0 restores a default. Process-wide; call it only while no call of this library is in
  * flight, and size workspaces after it. Returns ORPO_EINVAL for a chunk that is not a multiple of
  * 256 or a negative value. */
 orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes);
 
 /* Kernel tracing (a profiling aid). While enabled, every kernel this library launches is bracketed
  * by a pair of HIP events recorded on the launch's stream (up to max_launches launches), tagged with
- * its kind and its algorithmic floating-point work (2*d flops per (token, vocabulary) product of
- * the forward and coefficient GEMMs, 4*d for the fused dh/dW launch; 0 for merge and loss).
+ * its kind and its algorithmic floating-point work (2*d flops per (token, vocabulary) product for
+ * the forward and for coefficient tiles, 4*d for dh + dW tiles (2*d for dh alone); 0 for merge and
+ * loss).
  * orpo_trace_collect waits for the recorded events of one kind and returns their totals;
  * orpo_trace_reset starts a new record.
  * Process-wide and not thread-safe; enabling allocates events (host API only, no device memory). */
 typedef enum {
-  ORPO_K_FWD = 0,    /* forward logits + online softmax             */
-  ORPO_K_MERGE = 1,  /* cross-split merge -> lse, logp              */
-  ORPO_K_LOSS = 2,   /* segmented means + ORPO epilogue + g         */
-  ORPO_K_COEFF = 3,  /* backward logit recompute + coefficients     */
-  ORPO_K_DHDW = 4,   /* backward dh and dW GEMMs                    */
-  ORPO_K_COUNT = 5
+  ORPO_K_FWD = 0,    /* forward logits + online softmax                                  */
+  ORPO_K_MERGE = 1,  /* cross-split merge -> lse, logp                                   */
+  ORPO_K_LOSS = 2,   /* segmented means + ORPO epilogue + g                              */
+  ORPO_K_COEFF = 3,  /* backward launch with coefficient tiles only (first of a pass)    */
+  ORPO_K_DHDW = 4,   /* backward launch with dh / dW tiles only (last of a pass)         */
+  ORPO_K_BWD = 5,    /* backward launch with both (all the others)                       */
+  ORPO_K_COUNT = 6
 } orpo_kernel_kind;
 orpo_status orpo_trace_enable(int32_t max_launches);   /* 0 disables and releases the events */
 orpo_status orpo_trace_collect(int32_t kind, int64_t* launches, double* total_ms, double* flops);

@@ -4,8 +4,10 @@
 //                   workgroup's vocabulary split, label-logit capture -> per-split (max, sum) partials.
 //   merge_kernel  : partials of all splits -> lse, logp = z[y] - lse.
 //   loss_kernel   : segmented per-branch means (f64), scalar ORPO epilogue (f64), cotangent g.
-//   coeff_kernel  : recompute a logit tile, coeff = g (onehot - softmax) sech^2 -> coefficient tile.
-//   dhdw_kernel   : dh (+)= coeff . W_blk and dW_blk (+)= coeff^T . h_chunk from one coefficient tile.
+//   bwd_kernel    : one launch of the backward pipeline: coefficient tiles (recompute a logit tile,
+//                   coeff = g (onehot - softmax) sech^2) of one (token chunk, vocabulary block) item
+//                   and the dh (+)= coeff . W_blk and dW_blk (+)= coeff^T . h_chunk tiles of the
+//                   previous item.
 //
 // Sources: "Training — design" §1 "The objective" and §5.1 "The head"; its older revision "ORPO
 // training — design", "Memory & speed optimization", lever 1 and the "Implementation spec — fused
@@ -355,9 +357,22 @@ __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Backward phase 1: recompute a 256 x 256 logit tile (m = vocabulary, n = token) and write its
-// coefficients to the tile [C][BVb] (token-major) in the workspace.
+// Backward. The work is a sequence of items (token chunk c0 of C_cur tokens) x (vocabulary block v0
+// of BV_cur rows). Item i's coefficients go to coefficient buffer i % 2; launch i holds the
+// coefficient tiles of item i together with the dh / dW tiles of item i - 1 (which read buffer
+// (i - 1) % 2, written by the previous launch), longest tiles first, so the short coefficient tiles
+// fill the tail of the long GEMM tiles. Every accumulation into dh and dW has a fixed order.
 // ------------------------------------------------------------------------------------------
+struct BwdItem {
+  int64_t c0, C_cur;      // token chunk [c0, c0 + C_cur)
+  int64_t v0, BV_cur;     // vocabulary block [v0, v0 + BV_cur)
+  void* coeff;            // [C, BVb] of E::T, token-major
+  int32_t n_tiles;        // tiles of this item in the launch (coefficient: n_vt * n_tt; GEMM: dh + dW)
+  int32_t n_vt, n_tt;     // 256-tiles along vocabulary and tokens
+  int32_t n_dh;           // dh tiles (GEMM item); dW tiles are n_tiles - n_dh
+  int32_t dh_first, dw_first;
+};
+
 struct BwdArgs {
   const void* h;
   const void* w;
@@ -367,26 +382,27 @@ struct BwdArgs {
   const float* g;
   float* dh;              // [M, d]
   float* dW;              // [V, d] or null
-  void* coeff;            // [C, BVb] of E::T
   int64_t M, d, V;
-  int64_t c0, C_cur;      // token chunk [c0, c0 + C_cur)
-  int64_t v0, BV_cur;     // vocabulary block [v0, v0 + BV_cur)
-  int64_t BVb;            // row pitch of the coefficient tile (elements)
+  int64_t BVb;            // row pitch of a coefficient buffer (elements)
   float cap;
   int32_t ignore_index;
-  int32_t n_vt, n_tt;     // coefficient tiles along vocabulary and tokens
-  int32_t n_dh, n_dw, n_jt;
-  int32_t dh_first, dw_first;
+  int32_t n_jt;           // 256-tiles along d
+  BwdItem gm;             // dh / dW tiles (n_tiles = 0: none)
+  BwdItem cf;             // coefficient tiles (n_tiles = 0: none)
 };
 
+// Phase 1: recompute a 256 x 256 logit tile (m = vocabulary, n = token) and write its coefficients
+// coeff = g (onehot - softmax) sech^2 (bf16 or fp32) to the item's coefficient buffer.
 template <class E, bool Q4, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
-  ORPO_DECLARE_SMEM(smem);
+__device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it,
+                                           int bid) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
-  const int vt = blockIdx.x % a.n_vt, tt = blockIdx.x / a.n_vt;
-  const int64_t vbase = a.v0 + (int64_t)vt * kTile;   // global vocabulary row of tile row 0
-  const int64_t tbase = a.c0 + (int64_t)tt * kTile;   // global token of tile column 0
-  const int64_t t_end = min(a.M, a.c0 + a.C_cur);
+  // Plain round-robin order: consecutive tiles step along the vocabulary, so an XCD's ~32
+  // concurrent tiles form a ~(8 vocabulary x 4 token) group sharing 12 operand slices.
+  const int vt = bid % it.n_vt, tt = bid / it.n_vt;
+  const int64_t vbase = it.v0 + (int64_t)vt * kTile;  // global vocabulary row of tile row 0
+  const int64_t tbase = it.c0 + (int64_t)tt * kTile;  // global token of tile column 0
+  const int64_t t_end = min(a.M, it.c0 + it.C_cur);
   const int64_t row_bytes = a.d * E::kSize;
 
   typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
@@ -411,18 +427,18 @@ __global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
 
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
   typedef typename E::T T;
-  T* out = (T*)a.coeff;
+  T* out = (T*)it.coeff;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = acc_n(wn, nb, l);
-    const int64_t t = tbase + n;
-    const bool tv = t < t_end;
-    const int y = tv ? a.labels[t] : a.ignore_index;
+    const int64_t tk = tbase + n;
+    const bool tv = tk < t_end;
+    const int y = tv ? a.labels[tk] : a.ignore_index;
     const bool yv = tv && y != a.ignore_index && y >= 0 && (int64_t)y < a.V;   // else: ignored
-    const float gt = yv ? a.g[t] : 0.f;
-    const float L2 = yv ? a.lse[t] * kLog2e : 0.f;
-    const int64_t yo = (int64_t)y - vbase;            // label row within this tile
-    T* row = out + (t - a.c0) * a.BVb + (vbase - a.v0);
+    const float gt = yv ? a.g[tk] : 0.f;
+    const float L2 = yv ? a.lse[tk] * kLog2e : 0.f;
+    const int64_t yo = (int64_t)y - vbase;             // label row within this tile
+    T* row = out + (tk - it.c0) * a.BVb + (vbase - it.v0);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -447,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
           if (vbase + mm >= a.V || gt == 0.f) c = 0.f;
           vals[ri] = c;
         }
-        // 4 consecutive vocabulary entries of token t.
+        // 4 consecutive vocabulary entries of token tk.
         const int m0 = acc_m(wm, mb, rg * 4, l);
         if constexpr (sizeof(T) == 2) {
           u32x2 pk;
@@ -461,10 +477,6 @@ __global__ __launch_bounds__(kThreads) void coeff_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// Backward phase 2: one launch holds n_dh tiles of dh[c0 + i][j] (+)= sum_v coeff[i][v] W[v0 + v][j]
-// and n_dw tiles of dW[v0 + v][j] (+)= sum_i coeff[i][v] h[c0 + i][j].
-// ------------------------------------------------------------------------------------------
 template <class E>
 __device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, int64_t n_rows,
                                           int64_t col0, int64_t n_cols, bool first,
@@ -487,63 +499,88 @@ __device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, 
   }
 }
 
+// Phase 2a: dh[c0 + i][j] (+)= sum_v coeff[i][v] W[v0 + v][j]   (m = token, n = hidden, k = vocabulary)
 template <class E, bool Q4>
-__global__ __launch_bounds__(kThreads) void dhdw_kernel(BwdArgs a) {
-  ORPO_DECLARE_SMEM(smem);
+__device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid) {
   const int tid = threadIdx.x;
   const int64_t row_bytes = a.d * E::kSize;
-  const int64_t cpitch = a.BVb * E::kSize;            // coefficient tile row pitch (bytes)
-  const int64_t t_end = min(a.M, a.c0 + a.C_cur);
+  const int64_t cpitch = a.BVb * E::kSize;
+  const int64_t t_end = min(a.M, it.c0 + it.C_cur);
+  const int t = xcd_remap(bid, it.n_dh);
+  const int ti = t / a.n_jt, jt = t % a.n_jt;
+  const int64_t i0 = (int64_t)ti * kTile, j0 = (int64_t)jt * kTile;
+  const int64_t kv = ((it.BV_cur + kTile - 1) / kTile) * kTile;   // coefficient columns written
+  const int nk = (int)((kv + E::kBK - 1) / E::kBK);
+  const int64_t v_end = min(a.V, it.v0 + it.BV_cur);
+  DmaK la;                                                          // coeff [i][v], K-major
+  la.init(it.coeff, cpitch, it.C_cur);
+  typedef typename std::conditional<Q4, Q4N, DmaMN<E>>::type LoaderB;
+  LoaderB lb;                                                       // W [v][j], N-major
+  if constexpr (Q4) lb.init(a.q4, v_end); else lb.init(a.w, row_bytes, v_end);
+  auto issue = [&](int, int ks, char* sa, char* sb) {
+    const int64_t k0 = (int64_t)ks * E::kBK;
+    la.issue(i0, k0 * E::kSize, sa);
+    if constexpr (Q4) lb.issue(it.v0 + k0, j0, sb);
+    else lb.issue(it.v0 + k0, j0 * E::kSize, sb);
+  };
+  auto commit = [&](char* sa, char* sb) {
+    la.commit(sa);
+    lb.commit(sb);
+  };
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  if ((int)blockIdx.x < a.n_dh) {
-    // m = token (C rows), n = hidden, k = vocabulary of the block.
-    const int t = xcd_remap(blockIdx.x, a.n_dh);
-    const int it = t / a.n_jt, jt = t % a.n_jt;
-    const int64_t i0 = (int64_t)it * kTile, j0 = (int64_t)jt * kTile;
-    const int64_t kv = ((a.BV_cur + kTile - 1) / kTile) * kTile;   // coefficient columns written
-    const int nk = (int)((kv + E::kBK - 1) / E::kBK);
-    const int64_t v_end = min(a.V, a.v0 + a.BV_cur);
-    DmaK la;                                                         // coeff [i][v], K-major
-    la.init(a.coeff, cpitch, a.C_cur);
-    typedef typename std::conditional<Q4, Q4N, DmaMN<E>>::type LoaderB;
-    LoaderB lb;                                                      // W [v][j], N-major
-    if constexpr (Q4) lb.init(a.q4, v_end); else lb.init(a.w, row_bytes, v_end);
-    auto issue = [&](int, int ks, char* sa, char* sb) {
-      const int64_t k0 = (int64_t)ks * E::kBK;
-      la.issue(i0, k0 * E::kSize, sa);
-      if constexpr (Q4) lb.issue(a.v0 + k0, j0, sb);
-      else lb.issue(a.v0 + k0, j0 * E::kSize, sb);
-    };
-    auto commit = [&](char* sa, char* sb) {
-      la.commit(sa);
-      lb.commit(sb);
-    };
-    gemm_run<E, true, false, false>(smem, 1, nk, issue, commit, nop, acc);
-    store_out<E>(a.dh, a.d, a.c0 + i0, t_end, j0, a.d, a.dh_first != 0, acc);
-  } else {
-    // m = vocabulary (block rows), n = hidden, k = token of the chunk.
-    const int t = xcd_remap(blockIdx.x - a.n_dh, a.n_dw);
-    const int vt = t / a.n_jt, jt = t % a.n_jt;
-    const int64_t vl0 = (int64_t)vt * kTile, j0 = (int64_t)jt * kTile;
-    const int nk = (int)((a.C_cur + E::kBK - 1) / E::kBK);
-    DmaMN<E> la;                                                     // coeff [i][v], M-major
-    la.init(a.coeff, cpitch, a.C_cur);
-    DmaMN<E> lb;                                                     // h [t][j], N-major
-    lb.init(a.h, row_bytes, t_end);
-    auto issue = [&](int, int ks, char* sa, char* sb) {
-      const int64_t k0 = (int64_t)ks * E::kBK;
-      la.issue(k0, vl0 * E::kSize, sa);
-      lb.issue(a.c0 + k0, j0 * E::kSize, sb);
-    };
-    auto commit = [&](char* sa, char* sb) {
-      la.commit(sa);
-      lb.commit(sb);
-    };
-    gemm_run<E, false, false, false>(smem, 1, nk, issue, commit, nop, acc);
-    store_out<E>(a.dW, a.d, a.v0 + vl0, min(a.V, a.v0 + a.BV_cur), j0, a.d, a.dw_first != 0, acc);
+  gemm_run<E, true, false, false>(smem, 1, nk, issue, commit, nop, acc);
+  (void)tid;
+  store_out<E>(a.dh, a.d, it.c0 + i0, t_end, j0, a.d, it.dh_first != 0, acc);
+}
+
+// Phase 2b: dW[v0 + v][j] (+)= sum_i coeff[i][v] h[c0 + i][j]   (m = vocabulary, n = hidden, k = token)
+template <class E>
+__device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid) {
+  const int64_t row_bytes = a.d * E::kSize;
+  const int64_t cpitch = a.BVb * E::kSize;
+  const int64_t t_end = min(a.M, it.c0 + it.C_cur);
+  const int t = xcd_remap(bid, it.n_tiles - it.n_dh);
+  const int vt = t / a.n_jt, jt = t % a.n_jt;
+  const int64_t vl0 = (int64_t)vt * kTile, j0 = (int64_t)jt * kTile;
+  const int nk = (int)((it.C_cur + E::kBK - 1) / E::kBK);
+  DmaMN<E> la;                                                      // coeff [i][v], M-major
+  la.init(it.coeff, cpitch, it.C_cur);
+  DmaMN<E> lb;                                                      // h [t][j], N-major
+  lb.init(a.h, row_bytes, t_end);
+  auto issue = [&](int, int ks, char* sa, char* sb) {
+    const int64_t k0 = (int64_t)ks * E::kBK;
+    la.issue(k0, vl0 * E::kSize, sa);
+    lb.issue(it.c0 + k0, j0 * E::kSize, sb);
+  };
+  auto commit = [&](char* sa, char* sb) {
+    la.commit(sa);
+    lb.commit(sb);
+  };
+  f32x16 acc[4][2];
+  zero_acc(acc);
+  auto nop = [](int, f32x16(&)[4][2]) {};
+  gemm_run<E, false, false, false>(smem, 1, nk, issue, commit, nop, acc);
+  store_out<E>(a.dW, a.d, it.v0 + vl0, min(a.V, it.v0 + it.BV_cur), j0, a.d, it.dw_first != 0, acc);
+}
+
+// One launch of the backward pipeline: [dh tiles of gm | dW tiles of gm | coefficient tiles of cf].
+template <class E, bool Q4, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
+  ORPO_DECLARE_SMEM(smem);
+  int b = blockIdx.x;
+  if (b < a.gm.n_dh) {
+    dh_tile<E, Q4>(smem, a, a.gm, b);
+    return;
   }
+  b -= a.gm.n_dh;
+  if (b < a.gm.n_tiles - a.gm.n_dh) {
+    if constexpr (!Q4) dw_tile<E>(smem, a, a.gm, b);
+    return;
+  }
+  b -= a.gm.n_tiles - a.gm.n_dh;
+  coeff_tile<E, Q4, SOFTCAP>(smem, a, a.cf, b);
 }
 
 }  // namespace orpo

@@ -128,7 +128,7 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
   p.C = std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), kTile) * kTile, g_chunk);
   const int64_t by_budget = std::max<int64_t>(kTile, int64_t(g_coeff_budget) / (p.C * esize) / kTile * kTile);
   p.BVb = std::min<int64_t>(cdiv(d->V, kTile) * kTile, by_budget);
-  p.ws = kHeader + size_t(p.C) * size_t(p.BVb) * size_t(esize);
+  p.ws = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize);
   return p;
 }
 
@@ -140,16 +140,13 @@ orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
 }
 
 template <class E, bool Q4, bool SC>
-orpo_status launch_coeff(const BwdArgs& a, int grid, hipStream_t st) {
-  TraceScope ts(ORPO_K_COEFF, 2.0 * double(a.C_cur) * double(a.BV_cur) * double(a.d), st);
-  hipLaunchKernelGGL((coeff_kernel<E, Q4, SC>), dim3(grid), dim3(kThreads), 0, st, a);
-  return launched();
-}
-
-template <class E, bool Q4>
-orpo_status launch_dhdw(const BwdArgs& a, int grid, hipStream_t st) {
-  TraceScope ts(ORPO_K_DHDW, (a.n_dw ? 4.0 : 2.0) * double(a.C_cur) * double(a.BV_cur) * double(a.d), st);
-  hipLaunchKernelGGL((dhdw_kernel<E, Q4>), dim3(grid), dim3(kThreads), 0, st, a);
+orpo_status launch_bwd(const BwdArgs& a, int grid, hipStream_t st) {
+  const double cf = 2.0 * double(a.cf.C_cur) * double(a.cf.BV_cur) * double(a.d) * (a.cf.n_tiles > 0);
+  const double gm = (a.gm.n_tiles > a.gm.n_dh ? 4.0 : 2.0) * double(a.gm.C_cur) * double(a.gm.BV_cur) *
+                    double(a.d) * (a.gm.n_tiles > 0);
+  const int kind = a.gm.n_tiles == 0 ? ORPO_K_COEFF : (a.cf.n_tiles == 0 ? ORPO_K_DHDW : ORPO_K_BWD);
+  TraceScope ts(kind, cf + gm, st);
+  hipLaunchKernelGGL((bwd_kernel<E, Q4, SC>), dim3(grid), dim3(kThreads), 0, st, a);
   return launched();
 }
 
@@ -278,7 +275,6 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.g = g;
   a.dh = dh;
   a.dW = dW;
-  a.coeff = (char*)ws + kHeader;
   a.M = desc->M;
   a.d = desc->d;
   a.V = desc->V;
@@ -288,31 +284,40 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.n_jt = (int)cdiv(desc->d, kTile);
   const bool sc = desc->softcap > 0.f;
   const bool acc_dw = (desc->flags & ORPO_DW_ACCUMULATE) != 0;
-  for (int64_t c0 = 0; c0 < desc->M; c0 += p.C) {
-    for (int64_t v0 = 0; v0 < desc->V; v0 += p.BVb) {
-      a.c0 = c0;
-      a.C_cur = std::min(p.C, desc->M - c0);
-      a.v0 = v0;
-      a.BV_cur = std::min(p.BVb, desc->V - v0);
-      a.n_vt = (int)cdiv(a.BV_cur, kTile);
-      a.n_tt = (int)cdiv(a.C_cur, kTile);
-      a.n_dh = a.n_tt * a.n_jt;
-      a.n_dw = dW ? a.n_vt * a.n_jt : 0;
-      a.dh_first = v0 == 0;
-      a.dw_first = c0 == 0 && !acc_dw;
-      const int gc = a.n_vt * a.n_tt, gd = a.n_dh + a.n_dw;
-      if (k == kF32) {
-        st = sc ? launch_coeff<EF32, false, true>(a, gc, stream) : launch_coeff<EF32, false, false>(a, gc, stream);
-        if (st == ORPO_OK) st = launch_dhdw<EF32, false>(a, gd, stream);
-      } else if (k == kBf16) {
-        st = sc ? launch_coeff<EBf16, false, true>(a, gc, stream) : launch_coeff<EBf16, false, false>(a, gc, stream);
-        if (st == ORPO_OK) st = launch_dhdw<EBf16, false>(a, gd, stream);
-      } else {
-        st = sc ? launch_coeff<EBf16, true, true>(a, gc, stream) : launch_coeff<EBf16, true, false>(a, gc, stream);
-        if (st == ORPO_OK) st = launch_dhdw<EBf16, true>(a, gd, stream);
-      }
-      if (st != ORPO_OK) return st;
+  const size_t esize = k == kF32 ? 4 : 2;
+  char* buf[2] = {(char*)ws + kHeader, (char*)ws + kHeader + size_t(p.C) * size_t(p.BVb) * esize};
+  const int64_t n_blocks = cdiv(desc->V, p.BVb);
+  const int64_t n_items = cdiv(desc->M, p.C) * n_blocks;
+  // Item i = (chunk i / n_blocks, block i % n_blocks); launch i = coefficients of item i + dh/dW of item i-1.
+  auto make_item = [&](int64_t i, bool gemm) {
+    BwdItem it{};
+    if (i < 0 || i >= n_items) return it;   // n_tiles = 0: absent
+    const int64_t c = i / n_blocks, blk = i % n_blocks;
+    it.c0 = c * p.C;
+    it.C_cur = std::min(p.C, desc->M - it.c0);
+    it.v0 = blk * p.BVb;
+    it.BV_cur = std::min(p.BVb, desc->V - it.v0);
+    it.coeff = buf[i % 2];
+    it.n_vt = (int)cdiv(it.BV_cur, kTile);
+    it.n_tt = (int)cdiv(it.C_cur, kTile);
+    it.dh_first = blk == 0;
+    it.dw_first = c == 0 && !acc_dw;
+    if (gemm) {
+      it.n_dh = it.n_tt * a.n_jt;
+      it.n_tiles = it.n_dh + (dW ? it.n_vt * a.n_jt : 0);
+    } else {
+      it.n_tiles = it.n_vt * it.n_tt;
     }
+    return it;
+  };
+  for (int64_t i = 0; i <= n_items; ++i) {
+    a.cf = make_item(i, false);
+    a.gm = make_item(i - 1, true);
+    const int grid = a.cf.n_tiles + a.gm.n_tiles;
+    if (k == kF32) st = sc ? launch_bwd<EF32, false, true>(a, grid, stream) : launch_bwd<EF32, false, false>(a, grid, stream);
+    else if (k == kBf16) st = sc ? launch_bwd<EBf16, false, true>(a, grid, stream) : launch_bwd<EBf16, false, false>(a, grid, stream);
+    else st = sc ? launch_bwd<EBf16, true, true>(a, grid, stream) : launch_bwd<EBf16, true, false>(a, grid, stream);
+    if (st != ORPO_OK) return st;
   }
   return ORPO_OK;
 }

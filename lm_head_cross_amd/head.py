@@ -54,7 +54,7 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "orpo_trace_reset": (ctypes.c_int, []),
 }
-KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw"}
+KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw", 5: "bwd"}
 _lib = None
 
 

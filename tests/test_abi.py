@@ -36,7 +36,7 @@ def test_workspace_sizes():
     fws = L.orpo_head_fwd_workspace_bytes(ctypes.byref(d))
     bws = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
     assert fws == 256 + 16 * 8192 * 8          # 16 vocabulary splits of 64 tiles, float2 each
-    assert bws == 256 + 8192 * 16384 * 2       # a 256 MiB bf16 coefficient tile
+    assert bws == 256 + 2 * 8192 * 16384 * 2   # two 256 MiB bf16 coefficient tiles
     # The backward workspace does not grow with M past one chunk.
     d2 = _desc(M=32768, d=2560, V=262144)
     assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d2)) == bws
@@ -96,10 +96,10 @@ def test_bwd_tiling_knob_validates_and_resizes():
     d = _desc(M=4096, d=256, V=4096)
     try:
         assert L.orpo_set_bwd_tiling(512, 512 * 1024 * 2) == 0
-        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 512 * 1024 * 2
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 2 * 512 * 1024 * 2
     finally:
         assert L.orpo_set_bwd_tiling(0, 0) == 0
-    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 4096 * 4096 * 2
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 2 * 4096 * 4096 * 2
 
 
 def test_status_strings():
