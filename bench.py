@@ -127,11 +127,18 @@ def main():
 
     # Dominant kernel: the kind with the most traced time; achieved = its algorithmic FLOPs per
     # launch over its average launch time (HIP events on the library's launch stream).
+    from lm_head_cross_amd import prof_summary
     kinds = {k: v for k, v in tr.items() if v[0] > 0}
     dom = max(kinds, key=lambda k: kinds[k][1])
     n_l, tot_ms, fl = kinds[dom]
     avg_ms = tot_ms / n_l
     achieved = (fl / n_l) / (avg_ms / 1e3)
+    traffic = None
+    tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                         f"{cfg.name}_traffic.txt")
+    t = prof_summary.read_traffic(tfile)
+    if t is not None and t[0] == dom:
+        traffic = round(t[1])
     per_kernel = {k: {"launches_per_step": v[0] / args.steps, "avg_ms": v[1] / max(v[0], 1),
                       "ms_per_step": v[1] / args.steps,
                       "tflops": (v[2] / (v[1] / 1e3) / 1e12) if v[1] > 0 and v[2] > 0 else None}
@@ -147,7 +154,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or (256 if cfg.M * cfg.V * cfg.d > 1e12 else min(cfg.M, 1024))
+        # About 4e12 FLOP of float64 oracle work (10-30 s on the host), rounded to 128 tokens.
+        auto = int(4e12 / (6 * cfg.V * cfg.d)) // 128 * 128
+        rows = args.cpu_rows or max(128, min(cfg.M, auto))
         print(f"[bench] oracle cpu baseline on {rows} rows", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp, rows)
 
@@ -184,7 +193,8 @@ def main():
             "peak": round(peak_flops / 1e12, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak_flops, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         },
         "cpu_baseline": cpu,
     }

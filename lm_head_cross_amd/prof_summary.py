@@ -1,0 +1,132 @@
+"""Summaries of rocprofv3 output for `profiles/`, and the HBM-traffic figure bench.py reports.
+
+  python -m lm_head_cross_amd.prof_summary stats  KERNEL_STATS.csv  OUT.md  "<command>"
+  python -m lm_head_cross_amd.prof_summary traffic FETCH.csv WRITE.csv KERNEL_SUBSTRING OUT.txt "<commands>" [KIND]
+
+`traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same counters read for the
+plain 1 GiB device copy that `bench.py --copy-calibration` runs, averages them over the dispatches of
+the named kernel, and records a hash of the kernel sources, so that bench.py reports the figure only
+while the kernels are unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def kernel_stats_md(stats_csv: str, title: str, command: str) -> str:
+    out = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+           "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in _rows(stats_csv):
+        name = r["Name"] if len(r["Name"]) <= 70 else r["Name"][:67] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.2f}% |")
+    trace = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    if os.path.exists(trace):
+        groups = {}
+        for r in _rows(trace):
+            if "bwd_kernel" not in r["Kernel_Name"]:
+                continue
+            wg = int(r.get("Grid_Size_X", r.get("Grid_Size", "0"))) // int(r.get("Workgroup_Size_X", r.get("Workgroup_Size", "512")))
+            groups.setdefault(wg, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        if groups:
+            out += ["", "Backward launches by grid size (workgroups): the mixed launches (coefficient tiles of",
+                    "one item + dh/dW tiles of the previous) are the ones bench.py reports as `bwd`.", "",
+                    "| workgroups | launches | avg (us) |", "|---|---|---|"]
+            for wg in sorted(groups, reverse=True):
+                v = groups[wg]
+                out.append(f"| {wg} | {len(v)} | {sum(v) / len(v):.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(rows, counter, substr, grid=None):
+    vals = [float(r["Counter_Value"]) * 1024 for r in rows
+            if r["Counter_Name"] == counter and substr in r["Kernel_Name"]
+            and (grid is None or int(r["Grid_Size"]) == grid)]
+    return vals
+
+
+def _copy_scale(rows, counter):
+    vals = _per_dispatch(rows, counter, "copyBuffer")
+    big = [v for v in vals if v > COPY_BYTES / 4]
+    if not big:
+        raise SystemExit(f"no 1 GiB copy found for {counter}: run bench.py with --copy-calibration")
+    return COPY_BYTES / (sum(big) / len(big))
+
+
+def traffic_txt(fetch_csv, write_csv, substr, commands, kind=None) -> str:
+    fr, wr = _rows(fetch_csv), _rows(write_csv)
+    fs, ws = _copy_scale(fr, "FETCH_SIZE"), _copy_scale(wr, "WRITE_SIZE")
+    grid = None
+    if kind is None:
+        kind = substr
+    else:   # the most frequent grid size of the kernel = its steady-state (mixed) launches
+        sizes = [int(r["Grid_Size"]) for r in fr if substr in r["Kernel_Name"]]
+        grid = max(set(sizes), key=sizes.count)
+    f = _per_dispatch(fr, "FETCH_SIZE", substr, grid)
+    w = _per_dispatch(wr, "WRITE_SIZE", substr, grid)
+    if not f or not w:
+        raise SystemExit(f"kernel {substr!r} not found")
+    fetch = fs * sum(f) / len(f)
+    write = ws * sum(w) / len(w)
+    return "\n".join([
+        f"kernel: {kind}",
+        f"kernel_name: {substr}" + (f" (grid {grid} threads)" if grid else ""),
+        f"source_hash: {source_hash()}",
+        f"dispatches: {len(f)}",
+        f"fetch_scale: {fs:.4f}",
+        f"write_scale: {ws:.4f}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"traffic_bytes_per_launch: {fetch + write:.0f}",
+        f"commands: {commands}",
+    ]) + "\n"
+
+
+def read_traffic(path: str):
+    """(kernel, bytes per launch) if `path` exists and was taken on the current kernel sources."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    return kv.get("kernel"), float(kv["traffic_bytes_per_launch"])
+
+
+def main(argv):
+    if argv[1] == "stats":
+        open(argv[3], "w").write(kernel_stats_md(argv[2], os.path.basename(argv[3]), argv[4]))
+    elif argv[1] == "traffic":
+        kind = argv[7] if len(argv) > 7 else None
+        open(argv[5], "w").write(traffic_txt(argv[2], argv[3], argv[4], argv[6], kind))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv)
