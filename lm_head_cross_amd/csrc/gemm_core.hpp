@@ -126,6 +126,12 @@ struct EF32 {
   }
 };
 
+// One direct global -> LDS load: 16 bytes per lane, lane l's data lands at LDS byte (lds + 16 l);
+// bytes past the descriptor's range read as zero.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
 // ------------------------------------------------------------------------------------------
 // Dense loaders: global -> LDS directly. A stage is 2048 chunks of 16 bytes; wave w issues
 // instructions i = 0..3 filling LDS bytes [(4w + i) KiB, +1 KiB), lane l the chunk 64 (4w + i) + l.
@@ -152,8 +158,7 @@ struct DmaK {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * ld + kb, (n_rows - row0) * ld - kb);
     char* s = stage + (threadIdx.x >> 6) * 4096;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(s + i * 1024), 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i]);
   }
   __device__ __forceinline__ void commit(char*) const {}
 };
@@ -181,8 +186,7 @@ struct DmaMN {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld + cb, (n_rows - k0) * ld - cb);
     char* s = stage + (threadIdx.x >> 6) * 4096;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(s + i * 1024), 16, voff[i], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i]);
   }
   __device__ __forceinline__ void commit(char*) const {}
 };
@@ -222,22 +226,26 @@ struct Q4Weight {
 struct Q4K {
   Q4Weight W;
   u32x4 q;
-  float scale, bias;
+  uint16_t sbits, bbits;     // bf16 bits of the group's scale and bias
+  bool ok_;                  // the row (and column) is inside the weight
   __device__ __forceinline__ void init(const Q4Weight& w) { W = w; }
   __device__ __forceinline__ void issue(int64_t row0, int64_t k0, char*) {
     const int tid = threadIdx.x;
     const int64_t gr = row0 + (tid >> 1);
     const bool ok = gr < W.V;
     const int64_t r = ok ? gr : 0;
-    const u32x4 x = *(const u32x4*)(W.wq + r * (W.d >> 3) + (k0 >> 3) + (tid & 1) * 4);
+    q = *(const u32x4*)(W.wq + r * (W.d >> 3) + (k0 >> 3) + (tid & 1) * 4);
     const int64_t gi = r * (W.d >> 6) + (k0 >> 6);
-    const float s = bf16_bits_to_f32(W.scales[gi]), b = bf16_bits_to_f32(W.biases[gi]);
-    q = ok ? x : u32x4{0u, 0u, 0u, 0u};
-    scale = ok ? s : 0.f;
-    bias = ok ? b : 0.f;
+    sbits = W.scales[gi];
+    bbits = W.biases[gi];
+    ok_ = ok;
   }
+  // Rows past the vocabulary were loaded from row 0 (in bounds) and are zeroed here, at commit, so
+  // that nothing consumes the loaded registers before the stage's MFMAs have been issued.
   __device__ __forceinline__ void commit(char* stage) const {
     const int tid = threadIdx.x, r = tid >> 1;
+    const float scale = ok_ ? bf16_bits_to_f32(sbits) : 0.f;
+    const float bias = ok_ ? bf16_bits_to_f32(bbits) : 0.f;
     char* row = stage + r * kKBytes;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
@@ -251,7 +259,8 @@ struct Q4N {
   Q4Weight W;
   int64_t v_end;             // rows >= v_end read as zero
   u32x4 q;
-  float scale, bias;
+  uint16_t sbits, bbits;     // bf16 bits of the group's scale and bias
+  bool ok_;                  // the row (and column) is inside the weight
   __device__ __forceinline__ void init(const Q4Weight& w, int64_t vend) { W = w; v_end = vend; }
   __device__ __forceinline__ void issue(int64_t k0, int64_t n0, char*) {
     const int tid = threadIdx.x;
@@ -259,15 +268,16 @@ struct Q4N {
     const int64_t gc = n0 + (tid & 7) * 32;
     const bool ok = gr < v_end && gc < W.d;
     const int64_t r = ok ? gr : 0, c = ok ? gc : 0;
-    const u32x4 x = *(const u32x4*)(W.wq + r * (W.d >> 3) + (c >> 3));
+    q = *(const u32x4*)(W.wq + r * (W.d >> 3) + (c >> 3));
     const int64_t gi = r * (W.d >> 6) + (c >> 6);
-    const float s = bf16_bits_to_f32(W.scales[gi]), b = bf16_bits_to_f32(W.biases[gi]);
-    q = ok ? x : u32x4{0u, 0u, 0u, 0u};
-    scale = ok ? s : 0.f;
-    bias = ok ? b : 0.f;
+    sbits = W.scales[gi];
+    bbits = W.biases[gi];
+    ok_ = ok;
   }
   __device__ __forceinline__ void commit(char* stage) const {
     const int tid = threadIdx.x, r = tid >> 3;
+    const float scale = ok_ ? bf16_bits_to_f32(sbits) : 0.f;
+    const float bias = ok_ ? bf16_bits_to_f32(bbits) : 0.f;
     char* row = stage + r * (EBf16::kMnChunks * 16);
 #pragma unroll
     for (int w = 0; w < 4; ++w)
