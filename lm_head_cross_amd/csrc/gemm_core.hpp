@@ -47,7 +47,10 @@ constexpr int kLdsBytes = 4 * kStageBytes;  // A and B, two stages each
 constexpr int kKGroups = 4;                 // MFMA k groups per stage (bf16: 4 x 16, fp32: 4 x 8)
 constexpr uint32_t kBufferFlags = 0x00020000u;   // raw buffer descriptor word 3 (32-bit data format)
 
-__device__ __forceinline__ int swz_k(int r) { return (r ^ (r >> 3)) & 7; }
+// LDS swizzles (16-byte chunk index XOR a function of the row). K-major: row r's chunk c sits at
+// c ^ (r & 7), so the 8 consecutive rows one ds_read_b128 phase touches hit 8 distinct bank groups,
+// and rows 32 apart share the swizzle (a fragment's 32-row blocks are constant offsets apart).
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
 __device__ __forceinline__ int swz_mn16(int r) { return 10 * (r & 3); }
 __device__ __forceinline__ int swz_mn32(int r) { return ((r >> 2) & 1) << 3; }
 
@@ -289,21 +292,54 @@ struct Q4N {
 // Compute one LDS stage into the wave's 4 x 2 accumulator blocks.
 // ------------------------------------------------------------------------------------------
 template <class E, bool AK, bool BK>
-__device__ __forceinline__ void compute_stage(const char* sa, const char* sb, f32x16 (&acc)[4][2],
-                                              int wm, int wn, int l) {
+__device__ __forceinline__ void load_frags(const char* sa, const char* sb, int kg, int wm, int wn,
+                                           int l, typename E::Frag (&a)[4],
+                                           typename E::Frag (&b)[2]) {
+  // In the order the MFMAs consume them: b0, a0, b1, then a1..a3.
+  b[0] = BK ? E::frag_k(sb, wn * 64, kg, l) : E::frag_mn(sb, wn * 64, kg, l);
+  a[0] = AK ? E::frag_k(sa, wm * 128, kg, l) : E::frag_mn(sa, wm * 128, kg, l);
+  b[1] = BK ? E::frag_k(sb, wn * 64 + 32, kg, l) : E::frag_mn(sb, wn * 64 + 32, kg, l);
 #pragma unroll
-  for (int kg = 0; kg < kKGroups; ++kg) {
-    typename E::Frag a[4], b[2];
+  for (int mb = 1; mb < 4; ++mb)
+    a[mb] = AK ? E::frag_k(sa, wm * 128 + mb * 32, kg, l) : E::frag_mn(sa, wm * 128 + mb * 32, kg, l);
+}
+
+// Instruction counts of one K group, for the scheduling pattern below: LDS reads per fragment
+// (one ds_read_b128 for K-major; two transposing reads (bf16) or four dword reads (fp32) for
+// MN-major) and MFMA instructions per fragment pair.
+template <class E, bool K>
+constexpr int reads_per_frag() { return K ? 1 : (E::kSize == 2 ? 2 : 4); }
+template <class E>
+constexpr int mfma_per_mma() { return E::kSize == 2 ? 1 : 4; }
+
+// The MFMAs of one K group: the wave's 4 x 2 blocks of 32 x 32.
+template <class E>
+__device__ __forceinline__ void mma_group(f32x16 (&acc)[4][2], const typename E::Frag (&a)[4],
+                                          const typename E::Frag (&b)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      a[mb] = AK ? E::frag_k(sa, wm * 128 + mb * 32, kg, l) : E::frag_mn(sa, wm * 128 + mb * 32, kg, l);
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      b[nb] = BK ? E::frag_k(sb, wn * 64 + nb * 32, kg, l) : E::frag_mn(sb, wn * 64 + nb * 32, kg, l);
+    for (int nb = 0; nb < 2; ++nb) E::mma(acc[mb][nb], a[mb], b[nb]);
+}
+
+// Pins the order of the LDS reads and MFMAs of kGroups K groups, each group's MFMAs interleaved
+// with the reads of the group after it, spread over the first three quarters of the MFMAs so that
+// the last read has a few MFMAs' time to land before its group starts.
+template <class E, bool AK, bool BK, int kGroups>
+__device__ __forceinline__ void sched_groups() {
+  constexpr int kReads = 4 * reads_per_frag<E, AK>() + 2 * reads_per_frag<E, BK>();
+  constexpr int kMfma = 8 * mfma_per_mma<E>();
+  constexpr int kSpan = kMfma * 3 / 4;
+  static_assert(kReads <= 2 * kSpan, "at most two reads between MFMAs");
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+  for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) E::mma(acc[mb][nb], a[mb], b[nb]);
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int n = i < kSpan ? (i + 1) * kReads / kSpan - i * kReads / kSpan : 0;
+      if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
   }
 }
 
@@ -332,35 +368,84 @@ struct Smem {
   __shared__ __attribute__((aligned(1024))) char name##_b1[kStageBytes]; \
   const Smem name = {name##_a0, name##_a1, name##_b0, name##_b1}
 
-// One K step: compute from (ca, cb) while the next step's loads go into (na, nb).
+// Fragments of two K groups: group kg lives in set kg & 1.
+template <class E>
+struct FragSets {
+  typename E::Frag a[2][4], b[2][2];
+};
+
+// One K step s, reading stage (ca, cb); stage (na, nb) holds step s + 1. The workgroup barrier
+// sits before the last K group rather than at the end of the step: by then every wave holds that
+// group's fragments in registers, so its MFMAs run while the next stage's first fragments are read,
+// and the MFMA pipe does not idle on an LDS round trip after each barrier.
+//   region 1: MFMAs of groups 0..2, each with the next group's reads;
+//   barrier:  this stage is no longer read by anyone, stage s + 1 is in LDS (own loads waited
+//             first, register-staged loads committed first); the loads of step s + 2 then go into
+//             this stage;
+//   region 2: MFMAs of group 3 with the reads of step s + 1's group 0 (issued unconditionally; on
+//             the last step they read a stale stage and are never used), then the epilogue if the
+//             step ends a tile.
 template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi>
-__device__ __forceinline__ void gemm_step(int& tile, int& ks, int nk, bool more,
-                                          char* __restrict__ ca, char* __restrict__ cb,
-                                          char* __restrict__ na, char* __restrict__ nb,
-                                          Issue& issue, Commit& commit, Epi& epi,
-                                          f32x16 (&acc)[4][2], int wm, int wn, int l) {
-  int nks = ks + 1, ntile = tile;
-  if (nks == nk) { nks = 0; ++ntile; }
-  if (more) issue(ntile, nks, na, nb);
-  compute_stage<E, AK, BK>(ca, cb, acc, wm, wn, l);
-  if (more) commit(na, nb);
-  if (nks == 0) {
-    epi(tile, acc);
+__device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __restrict__ ca,
+                                          char* __restrict__ cb, char* __restrict__ na,
+                                          char* __restrict__ nb, Issue& issue, Commit& commit,
+                                          Epi& epi, FragSets<E>& f, f32x16 (&acc)[4][2], int wm,
+                                          int wn, int l) {
+#pragma unroll
+  for (int kg = 0; kg < kKGroups - 1; ++kg) {
+    load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
+    mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1]);
+  }
+  sched_groups<E, AK, BK, kKGroups - 1>();
+  if (s + 1 < total) commit(na, nb);
+  vm_wait();
+  __syncthreads();
+  if (s + 2 < total) issue((s + 2) / nk, (s + 2) % nk, ca, cb);
+  load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+  mma_group<E>(acc, f.a[(kKGroups - 1) & 1], f.b[(kKGroups - 1) & 1]);
+  sched_groups<E, AK, BK, 1>();
+  if ((s + 1) % nk == 0) {
+    epi(s / nk, acc);
+    if (kClear) zero_acc(acc);
+  }
+}
+
+// One K step with the barrier at its end, for stages read with transposing instructions (there the
+// barrier before the last group measured slower): the next step's loads are issued first, then the
+// MFMAs of the four groups with each group's reads one group ahead (left to the compiler's
+// schedule), then the step's epilogue, wait and barrier.
+template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi>
+__device__ __forceinline__ void gemm_step_end(int s, int total, int nk, char* __restrict__ ca,
+                                              char* __restrict__ cb, char* __restrict__ na,
+                                              char* __restrict__ nb, Issue& issue, Commit& commit,
+                                              Epi& epi, f32x16 (&acc)[4][2], int wm, int wn,
+                                              int l) {
+  if (s + 1 < total) issue((s + 1) / nk, (s + 1) % nk, na, nb);
+  FragSets<E> f;
+  load_frags<E, AK, BK>(ca, cb, 0, wm, wn, l, f.a[0], f.b[0]);
+#pragma unroll
+  for (int kg = 0; kg < kKGroups; ++kg) {
+    if (kg + 1 < kKGroups)
+      load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
+    mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1]);
+  }
+  if (s + 1 < total) commit(na, nb);
+  if ((s + 1) % nk == 0) {
+    epi(s / nk, acc);
     if (kClear) zero_acc(acc);
   }
   vm_wait();
   __syncthreads();
-  tile = ntile;
-  ks = nks;
 }
 
-// The main loop over n_tiles consecutive output tiles of nk K steps each.
+// The main loop over n_tiles consecutive output tiles of nk K steps each (step s is K step s % nk
+// of tile s / nk).
 //   issue(tile, ks, stageA, stageB): start the loads of step (tile, ks) into the given stages;
 //   commit(stageA, stageB): finish register-staged loads into LDS (no-op for direct loads);
-//   epi(tile, acc): runs after the tile's last K step (before the loop's barrier; it must not touch
-//   LDS), then the accumulators are cleared unless kClear is false (single-tile callers read acc
-//   after the loop). The next step's loads are in flight during each step's MFMAs. The loop is
-//   unrolled by two so that every step reads and fills statically known stages.
+//   epi(tile, acc): runs after the tile's last K step (it must not touch LDS), then the
+//   accumulators are cleared unless kClear is false (single-tile callers read acc after the loop).
+// Two stages: step s + 1's loads are in flight during step s's MFMAs. The loop is unrolled by two
+// so that every step reads and fills statically known stages.
 template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi>
 __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Issue&& issue,
                                          Commit&& commit, Epi&& epi, f32x16 (&acc)[4][2]) {
@@ -372,13 +457,26 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
   commit(sm.a0, sm.b0);
   vm_wait();
   __syncthreads();
-  int tile = 0, ks = 0;
+  if constexpr (!(AK && BK)) {
+    // Transposing reads: barrier at the end of each step.
+    for (int it = 0; it < total; it += 2) {
+      gemm_step_end<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit,
+                                       epi, acc, wm, wn, l);
+      if (it + 1 < total)
+        gemm_step_end<E, AK, BK, kClear>(it + 1, total, nk, sm.a1, sm.b1, sm.a0, sm.b0, issue,
+                                         commit, epi, acc, wm, wn, l);
+    }
+    return;
+  }
+  if (total > 1) issue(1 / nk, 1 % nk, sm.a1, sm.b1);
+  FragSets<E> f;
+  load_frags<E, AK, BK>(sm.a0, sm.b0, 0, wm, wn, l, f.a[0], f.b[0]);
   for (int it = 0; it < total; it += 2) {
-    gemm_step<E, AK, BK, kClear>(tile, ks, nk, it + 1 < total, sm.a0, sm.b0, sm.a1, sm.b1, issue,
-                                 commit, epi, acc, wm, wn, l);
+    gemm_step<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit, epi, f,
+                                 acc, wm, wn, l);
     if (it + 1 < total)
-      gemm_step<E, AK, BK, kClear>(tile, ks, nk, it + 2 < total, sm.a1, sm.b1, sm.a0, sm.b0, issue,
-                                   commit, epi, acc, wm, wn, l);
+      gemm_step<E, AK, BK, kClear>(it + 1, total, nk, sm.a1, sm.b1, sm.a0, sm.b0, issue, commit,
+                                   epi, f, acc, wm, wn, l);
   }
 }
 

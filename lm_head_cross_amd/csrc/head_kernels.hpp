@@ -107,11 +107,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     for (int nb = 0; nb < 2; ++nb) {
       // u = z * log2e (or (z - cap) * log2e under a softcap), masked past V on the last tile only
       // (a uniform branch). Values are recomputed from the accumulators in each pass.
-      const int lim = (int)min<int64_t>(max<int64_t>(a.V - vw0, 0), 128);   // valid rows of the wave
+      // Valid rows of the wave, less this lane's row offset 4 (l / 32), so that each element's test
+      // compares a compile-time constant (nothing per element is kept live across the K loop).
+      const int lim = (int)min<int64_t>(max<int64_t>(a.V - vw0, 0), 128) - 4 * (l >> 5);
       auto body = [&](auto masked_tag) {
         constexpr bool kMasked = decltype(masked_tag)::value;
         auto keep = [&](int mb, int r) {
-          return !kMasked || mb * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3) < lim;
+          return !kMasked || mb * 32 + 8 * (r >> 2) + (r & 3) < lim;
         };
         float ref = m[nb];
         if (!SOFTCAP) {

@@ -41,6 +41,9 @@ def kernel_stats_md(stats_csv: str, title: str, command: str) -> str:
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{float(r['Percentage']):.2f}% |")
+    out += ["", "Outside `orpo::`: the library GEMM (`Cijk_*`) and reduction kernels are the synthetic",
+            "input generator's argmax label pass, run before any timed step; `__amd_rocclr_*` are the",
+            "HIP runtime's own fills and copies (buffer setup, reading the loss back)."]
     trace = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
     if os.path.exists(trace):
         groups = {}
