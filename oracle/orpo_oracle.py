@@ -250,6 +250,87 @@ def token_cotangent(dL_dell, n, labels, seg_offsets, ignore_index: int = IGNORE_
 
 
 # --------------------------------------------------------------------------------------------
+# Full-scope NLL (prompt + chosen response)
+# --------------------------------------------------------------------------------------------
+def span_means_full(logp, labels, seg_offsets, ignore_index: int = IGNORE_INDEX):
+    """Per pair p: the spans [prompt, chosen, rejected] = segments 3p, 3p+1, 3p+2 of seg_offsets
+    (3P+1 entries). Returns (mean [3P], n [3P]); a prompt span may hold no valid token (its mean is
+    then reported as 0 and has no weight), the two responses may not."""
+    logp = np.asarray(logp, dtype=np.float64)
+    labels = np.asarray(labels).astype(np.int64)
+    off = np.asarray(seg_offsets).astype(np.int64)
+    M = logp.shape[0]
+    ns = off.shape[0] - 1
+    if ns < 3 or ns % 3:
+        raise OracleError("need 3P (>= 3) spans: prompt, chosen, rejected per pair")
+    if off[0] < 0 or off[-1] > M or np.any(np.diff(off) < 0):
+        raise OracleError("segment offsets must be monotone within [0, M]")
+    mean = np.zeros(ns)
+    n = np.zeros(ns, dtype=np.int64)
+    for b in range(ns):
+        ts = [t for t in range(off[b], off[b + 1]) if labels[t] != ignore_index]
+        if not ts:
+            if b % 3 == 0:
+                continue
+            raise OracleError(f"response span {b} has no valid token")
+        n[b] = len(ts)
+        mean[b] = math.fsum(logp[t] for t in ts) / len(ts)
+    return mean, n
+
+
+def orpo_epilogue_full(mean, n, lam: float):
+    """ORPO with the full-scope NLL, from the span means of span_means_full.
+
+    Training — design, §1 "The objective", the sft_scope `full` option: the chosen sequence's NLL
+    is the token mean over its supervised prompt positions and its response, combined from the two
+    span means as NLL_full = -((P-1) pm + M lw) / ((P-1) + M), where P-1 is the number of
+    supervised prompt positions (here n_q, the prompt span's valid tokens), M the response's (n_w)
+    and pm the prompt span's mean. The odds-ratio term keeps the response-only means lw, lr in both
+    scopes, and lam weights only it. Batch reduction as for the response scope: mean over pairs.
+
+    Gradient: dNLL_full/dpm = -n_q / (n_q + n_w), dNLL_full/dlw = -n_w / (n_q + n_w), plus the OR
+    term's d/dlw and d/dlr exactly as in orpo_epilogue. Returns the dict of orpo_epilogue with
+    `nll` the full-scope value, plus pm [P], n_q [P] and dL_dmean [3P].
+    """
+    mean = np.asarray(mean, dtype=np.float64)
+    n = np.asarray(n).astype(np.int64)
+    if mean.ndim != 1 or mean.shape[0] < 3 or mean.shape[0] % 3:
+        raise OracleError("need 3P span means")
+    P = mean.shape[0] // 3
+    ell = np.zeros(2 * P)
+    ell[0::2] = mean[1::3]
+    ell[1::2] = mean[2::3]
+    ep = orpo_epilogue(ell, lam)       # OR term, metrics, and its d/dlw, d/dlr
+    pm, n_q, n_w = mean[0::3], n[0::3], n[1::3]
+    nll_p = np.zeros(P)
+    dl = np.zeros(3 * P)
+    for p in range(P):
+        tot = n_q[p] + n_w[p]
+        nll_p[p] = -(n_q[p] * pm[p] + n_w[p] * ep["lw"][p]) / tot
+        dl[3 * p] = -(n_q[p] / tot) / P
+        # orpo_epilogue's chosen term is (-1 - lam (1 - sigma) f_w) / P; swap its -1 for -n_w / tot
+        dl[3 * p + 1] = ep["dL_dell"][2 * p] + (1.0 - n_w[p] / tot) / P
+        dl[3 * p + 2] = ep["dL_dell"][2 * p + 1]
+    nll = math.fsum(nll_p) / P
+    out = dict(ep)
+    out.update(loss=nll + lam * ep["or"], nll=nll, pm=pm.copy(), n_q=n_q.copy(), dL_dmean=dl)
+    del out["dL_dell"]
+    return out
+
+
+def token_cotangent_full(dL_dmean, n, labels, seg_offsets, ignore_index: int = IGNORE_INDEX):
+    """g_t = (dL/dmean_s) / n_s for a valid token t of span s (prompt, chosen or rejected), else 0."""
+    labels = np.asarray(labels).astype(np.int64)
+    off = np.asarray(seg_offsets).astype(np.int64)
+    g = np.zeros(labels.shape[0])
+    for s_ in range(off.shape[0] - 1):
+        for t in range(off[s_], off[s_ + 1]):
+            if labels[t] != ignore_index and n[s_] > 0:
+                g[t] = dL_dmean[s_] / n[s_]
+    return g
+
+
+# --------------------------------------------------------------------------------------------
 # Backward: coeff, dh, dW
 # --------------------------------------------------------------------------------------------
 def backward(h, W, labels, lse, g, cap: float = 0.0, ignore_index: int = IGNORE_INDEX,
@@ -308,3 +389,24 @@ def loss_value(h, W, labels, seg_offsets, cap: float, lam: float,
     logp, _ = forward(h, W, labels, cap, ignore_index)
     ell, _ = branch_means(logp, labels, seg_offsets, ignore_index)
     return orpo_epilogue(ell, lam)["loss"]
+
+
+def head_step_full(h, W, labels, seg_offsets, cap: float, lam: float,
+                   ignore_index: int = IGNORE_INDEX, want_dW: bool = True):
+    """head_step with the full-scope NLL: seg_offsets holds [prompt, chosen, rejected] per pair."""
+    logp, lse = forward(h, W, labels, cap, ignore_index)
+    mean, n = span_means_full(logp, labels, seg_offsets, ignore_index)
+    ep = orpo_epilogue_full(mean, n, lam)
+    g = token_cotangent_full(ep["dL_dmean"], n, labels, seg_offsets, ignore_index)
+    dh, dW = backward(h, W, labels, lse, g, cap, ignore_index, want_dW)
+    out = dict(ep)
+    out.update(logp=logp, lse=lse, mean=mean, n=n, g=g, dh=dh, dW=dW)
+    return out
+
+
+def loss_value_full(h, W, labels, seg_offsets, cap: float, lam: float,
+                    ignore_index: int = IGNORE_INDEX) -> float:
+    """The full-scope scalar loss alone (used by the finite-difference pins)."""
+    logp, _ = forward(h, W, labels, cap, ignore_index)
+    mean, n = span_means_full(logp, labels, seg_offsets, ignore_index)
+    return orpo_epilogue_full(mean, n, lam)["loss"]

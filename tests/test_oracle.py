@@ -354,3 +354,113 @@ def test_q4_dequant_group_boundaries():
     bias = np.array([[0, _bf16_bits(-0.25)]] * V, dtype=np.uint16)
     w = orc.dequant_q4(words, scale, bias, 64)
     assert np.all(w[:, :64] == 3.0) and np.all(w[:, 64:] == 5.75)
+
+
+# ----------------------------------------------------------------------------- full-scope NLL
+# Training — design, §1 "The objective", sft_scope `full`: the chosen sequence's NLL is the token
+# mean of -logp over its supervised prompt positions and its response; the odds ratio keeps the
+# response-only means.
+def _full_problem(seed, cap, prompt_ignored=False):
+    rng = _rng(300 + seed)
+    M, d, V = 16, 5, 9
+    h = rng.standard_normal((M, d))
+    W = rng.standard_normal((V, d)) * (1.5 if cap else 0.8)
+    labels = rng.integers(0, V, size=M)
+    labels[1] = -100            # an ignored prompt position
+    labels[9] = -100            # an ignored token of the second pair's chosen response
+    labels[15] = -100           # tail padding
+    off = np.array([0, 3, 5, 7, 8, 11, 14])   # pair 0: prompt 3, chosen 2, rejected 2; pair 1: 1, 3, 3
+    if prompt_ignored:
+        labels[7] = -100        # pair 1's prompt span holds no valid token
+    return h, W, labels, off
+
+
+def test_full_nll_is_the_pooled_token_mean():
+    # Definition check without the combine formula: -mean of logp over the union of the prompt's
+    # and the chosen response's valid tokens, per pair, then the mean over pairs.
+    rng = _rng(7)
+    logp = -rng.exponential(2.0, size=20)
+    labels = rng.integers(0, 50, size=20)
+    labels[[2, 11]] = -100
+    off = np.array([0, 4, 9, 12, 13, 17, 20])
+    mean, n = orc.span_means_full(logp, labels, off)
+    ep = orc.orpo_epilogue_full(mean, n, 0.3)
+    per_pair = []
+    for p in range(2):
+        toks = [t for t in range(off[3 * p], off[3 * p + 2]) if labels[t] != -100]
+        per_pair.append(-float(np.mean(logp[toks])))
+    assert ep["nll"] == pytest.approx(np.mean(per_pair), rel=1e-14)
+    # The odds-ratio side and the metrics use the response means only.
+    ell = np.array([mean[1], mean[2], mean[4], mean[5]])
+    ref = orc.orpo_epilogue(ell, 0.3)
+    for k in ("or", "accuracy", "margin"):
+        assert ep[k] == pytest.approx(ref[k], rel=1e-15, abs=1e-15)
+    assert ep["loss"] == pytest.approx(ep["nll"] + 0.3 * ref["or"], rel=1e-15)
+
+
+def test_full_scope_worked_values():
+    # Prompt logp = ln 1/2 at three positions, chosen ln 1/4 at one, rejected ln 1/4 at two:
+    # NLL = (3 ln 2 + ln 4) / 4 = 5 ln2 / 4; lw = lr => log-odds 0, L_OR = ln 2, accuracy 0.
+    logp = np.log([0.5, 0.5, 0.5, 0.25, 0.25, 0.25])
+    labels = np.zeros(6, dtype=np.int64)
+    mean, n = orc.span_means_full(logp, labels, [0, 3, 4, 6])
+    ep = orc.orpo_epilogue_full(mean, n, 0.5)
+    assert ep["nll"] == pytest.approx(5 * LN2 / 4, rel=1e-15)
+    assert ep["or"] == pytest.approx(LN2, rel=1e-15)
+    assert ep["loss"] == pytest.approx(5 * LN2 / 4 + 0.5 * LN2, rel=1e-15)
+    assert ep["accuracy"] == 0.0 and ep["margin"] == pytest.approx(0.0, abs=1e-15)
+    # dL/dpm = -3/4, so every prompt token's cotangent is -1/4 (one pair).
+    g = orc.token_cotangent_full(ep["dL_dmean"], n, labels, [0, 3, 4, 6])
+    assert np.allclose(g[:3], -0.25, rtol=0, atol=1e-15)
+
+
+def test_empty_prompt_reduces_to_response_scope():
+    # With no valid prompt position the full scope is the response scope: same loss and metrics (the
+    # combine's n_w lw / n_w may round differently in the last place) and the same cotangent.
+    h, W, labels, off = _full_problem(1, 2.0, prompt_ignored=True)
+    labels[[0, 2]] = -100                  # pair 0's prompt fully ignored as well
+    full = orc.head_step_full(h, W, labels, off, 2.0, 0.2)
+    # Response-scope branches chosen_0, rejected_0, chosen_1, rejected_1; pair 1's ignored prompt
+    # position (off[3]) falls inside chosen_1's range and counts for nothing.
+    resp = orc.head_step(h, W, labels, off[[1, 2, 3, 5, 6]], 2.0, 0.2)
+    for k in ("loss", "nll", "or", "accuracy", "margin"):
+        assert full[k] == pytest.approx(resp[k], rel=4e-16, abs=0), k
+    assert np.array_equal(full["g"], resp["g"])
+    assert np.array_equal(full["dh"], resp["dh"]) and np.array_equal(full["dW"], resp["dW"])
+
+
+@pytest.mark.parametrize("cap,lam", [(0.0, 0.1), (2.0, 0.0), (2.0, 1.0)])
+def test_full_scope_gradients_match_central_finite_differences(cap, lam):
+    h, W, labels, off = _full_problem(int(cap * 10 + lam * 7), cap)
+    out = orc.head_step_full(h, W, labels, off, cap, lam)
+    eps = 1e-6
+
+    def fd(arr, which):
+        grad = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            a = arr.copy()
+            a[idx] += eps
+            hp, wp = (a, W) if which == "h" else (h, a)
+            lp = orc.loss_value_full(hp, wp, labels, off, cap, lam)
+            a[idx] -= 2 * eps
+            hm, wm = (a, W) if which == "h" else (h, a)
+            lm = orc.loss_value_full(hm, wm, labels, off, cap, lam)
+            grad[idx] = (lp - lm) / (2 * eps)
+        return grad
+
+    gh = fd(h, "h")
+    gw = fd(W, "W")
+    assert np.linalg.norm(out["dh"] - gh) <= 1e-6 * np.linalg.norm(gh)
+    assert np.linalg.norm(out["dW"] - gw) <= 1e-6 * np.linalg.norm(gw)
+    assert np.all(out["dh"][[1, 9, 15]] == 0.0)
+    assert np.all(out["dh"][[0, 2, 7]] != 0.0)       # prompt positions now carry gradient
+
+
+def test_full_scope_span_errors():
+    logp = np.full(6, -1.0)
+    labels = np.zeros(6, dtype=np.int64)
+    with pytest.raises(orc.OracleError):
+        orc.span_means_full(logp, labels, [0, 2, 4])          # not 3P spans
+    labels[2:4] = -100
+    with pytest.raises(orc.OracleError):
+        orc.span_means_full(logp, labels, [0, 2, 4, 6])       # chosen response has no valid token
