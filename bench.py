@@ -50,13 +50,16 @@ def cpu_baseline(inp, rows: int):
         W = inp.w.float().numpy()
     h = inp.h[:rows].float().numpy()
     labels = inp.labels[:rows].copy()
-    # The sample is treated as one chosen/rejected pair split in half (the loss epilogue is a
-    # negligible part of the oracle's time; the three [rows, V] x d products dominate).
-    half = rows // 2
-    off = np.array([0, half, rows], dtype=np.int32)
+    # The sample is treated as one pair (the loss epilogue is a negligible part of the oracle's
+    # time; the three [rows, V] x d products dominate).
     labels[labels == synth.IGNORE_INDEX] = 0
     t0 = time.perf_counter()
-    out = orc.head_step(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
+    if cfg.scope == "full":     # one pair: prompt, chosen, rejected thirds
+        off = np.array([0, rows // 3, 2 * rows // 3, rows], dtype=np.int32)
+        out = orc.head_step_full(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
+    else:
+        off = np.array([0, rows // 2, rows], dtype=np.int32)
+        out = orc.head_step(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
     dt = time.perf_counter() - t0
     assert math.isfinite(out["loss"])
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -97,7 +100,7 @@ def main():
     inputs_bytes = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                      want_dW=not cfg.q4)
+                      want_dW=not cfg.q4, scope=cfg.scope)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -175,7 +178,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": cfg.name, "M": cfg.M, "valid_tokens": n_valid, "d": cfg.d, "V": cfg.V,
-            "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam,
+            "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam, "nll_scope": cfg.scope,
             "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
             "parallelism": "single GPU",
         },

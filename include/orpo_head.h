@@ -82,7 +82,7 @@ typedef struct {
 /* Workspace sizes in bytes (0 on invalid arguments). The forward workspace grows as 256 + 8 * NBLK
  * * M (per-token partials over NBLK vocabulary splits, like lse it is O(M)); the backward
  * workspace holds two coefficient tiles of fixed size (double-buffered), independent of M beyond
- * one token chunk. */
+ * one token chunk. The loss workspace (O(n_pairs)) serves both orpo_loss and orpo_loss_full. */
 size_t orpo_head_fwd_workspace_bytes(const orpo_head_desc* desc);
 size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc);
 size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs);
@@ -126,6 +126,30 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
 orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, const float* logp,
                       const int32_t* labels, int64_t V, int32_t ignore_index, double lambda,
                       double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * orpo_loss_full — orpo_loss with the full-scope NLL: the chosen sequence's NLL covers its
+ * supervised prompt positions as well as the response.
+ *   Spans per pair p: prompt [off[3p], off[3p+1]), chosen [off[3p+1], off[3p+2]), rejected
+ *   [off[3p+2], off[3p+3]). With n_q, n_w the valid-token counts and pm, lw the means of the prompt
+ *   and chosen spans: NLL_p = -(n_q pm + n_w lw) / (n_q + n_w), the pages' combination
+ *   -((P-1) pm + M lw) / ((P-1) + M) with P-1 supervised prompt positions and M response tokens;
+ *   nll = mean_p NLL_p. The odds ratio, accuracy and margin use the response means lw, lr exactly
+ *   as in orpo_loss, and lambda weights only the odds ratio. g_t = (dloss/dmean_s) / n_s for a
+ *   valid token of span s, prompt tokens included. ("Training — design" §1 "The objective", the
+ *   sft_scope `full` option.)
+ *   seg_offsets    (device) int32 [3*n_pairs + 1], monotone within [0, M]
+ *   out            (device) double [5 + 3*n_pairs] out: loss, nll, or, accuracy, margin, then
+ *                  lw[n_pairs], lr[n_pairs], then pm[n_pairs] (0 for a prompt span without a valid
+ *                  token)
+ *   Other arguments, the workspace size and the error behaviour as for orpo_loss. A prompt span
+ *   without a valid token is allowed (it then weighs nothing and every result equals orpo_loss's on
+ *   the two response spans); a response span without one sets ORPO_STATUS_EMPTY_BRANCH.
+ */
+orpo_status orpo_loss_full(int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
+                           const float* logp, const int32_t* labels, int64_t V,
+                           int32_t ignore_index, double lambda, double* out, float* g, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
 
 /*
  * orpo_head_bwd — dh = coeff . W and dW = coeff^T . h, recomputing the logits tile by tile.

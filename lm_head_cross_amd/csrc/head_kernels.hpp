@@ -254,39 +254,47 @@ __device__ __forceinline__ double log1mexp_d(double x, bool* clamped) {
 struct LossArgs {
   int64_t M, V;
   int32_t P;
-  const int32_t* off;     // [2P+1]
+  int32_t S;              // spans per pair: 2 = (chosen, rejected), 3 = (prompt, chosen, rejected)
+  const int32_t* off;     // [S P + 1]
   const float* logp;
   const int32_t* labels;
   int32_t ignore_index;
   double lam;
-  double* out;            // [5 + 2P]
+  double* out;            // [5 + 2P] (S = 2) or [5 + 3P] (S = 3)
   float* g;               // [M]
-  double* ell;            // ws [2P]
-  double* dl;             // ws [2P]  dL/d ell
-  int64_t* cnt;           // ws [2P]
-  double* pair;           // ws [4P]: log_odds, L_OR, then accuracy bit
+  double* ell;            // ws [S P] span means
+  double* sum;            // ws [S P] span sums
+  double* dl;             // ws [S P] dL / d ell
+  int64_t* cnt;           // ws [S P]
+  double* pair;           // ws [3P]: log_odds, L_OR, accuracy bit
   uint32_t* status;
 };
 
+// Span means, the scalar ORPO epilogue and the per-token cotangent, in one workgroup. With S = 3 the
+// NLL is the full-scope one: per pair, the token mean of -logp over the prompt span and the chosen
+// response together, -(sum_q + sum_w) / (n_q + n_w), i.e. the combination -((P-1) pm + M lw) /
+// ((P-1) + M) of the two span means (Training — design, §1 "The objective", sft_scope `full`); the
+// odds ratio keeps the response means. A prompt span without a valid token is allowed (weight 0,
+// reported mean 0); then every result equals the S = 2 one bit for bit.
 __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
   __shared__ int bad;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  const int nb = 2 * a.P;
+  const int S = a.S, ns = S * a.P, nout = 5 + (S == 3 ? 3 : 2) * a.P;
   if (tid == 0) {
-    int b = a.off[0] < 0 || (int64_t)a.off[nb] > a.M;
-    for (int i = 0; i < nb; ++i) b |= a.off[i + 1] < a.off[i];
+    int b = a.off[0] < 0 || (int64_t)a.off[ns] > a.M;
+    for (int i = 0; i < ns; ++i) b |= a.off[i + 1] < a.off[i];
     bad = b;
     *a.status = b ? kStatusBadOffsets : 0u;
   }
   __syncthreads();
   const double nan = __builtin_nan("");
   if (bad) {
-    for (int i = tid; i < 5 + nb; i += 1024) a.out[i] = nan;
+    for (int i = tid; i < nout; i += 1024) a.out[i] = nan;
     for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
     return;
   }
-  // Branch sums: wave w takes branches w, w + 16, ...
-  for (int b = w; b < nb; b += 16) {
+  // Span sums: wave w takes spans w, w + 16, ...
+  for (int b = w; b < ns; b += 16) {
     double sum = 0.0;
     long long n = 0;
     for (int64_t t = a.off[b] + l; t < a.off[b + 1]; t += 64) {
@@ -302,15 +310,18 @@ __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
       n += __shfl_xor(n, o);
     }
     if (l == 0) {
+      const bool prompt = S == 3 && b % 3 == 0;
       a.cnt[b] = n;
-      a.ell[b] = n > 0 ? sum / (double)n : nan;
-      if (n == 0) atomicOr(a.status, kStatusEmptyBranch);
+      a.sum[b] = sum;
+      a.ell[b] = n > 0 ? sum / (double)n : (prompt ? 0.0 : nan);
+      if (n == 0 && !prompt) atomicOr(a.status, kStatusEmptyBranch);
     }
   }
   __syncthreads();
-  // Per pair: log-odds, L_OR, and dL/d ell for both branches.
+  // Per pair: log-odds, L_OR, and dL/d ell for every span.
   for (int p = tid; p < a.P; p += 1024) {
-    const double lw = a.ell[2 * p], lr = a.ell[2 * p + 1];
+    const int cw_i = S * p + S - 2, cr_i = S * p + S - 1;
+    const double lw = a.ell[cw_i], lr = a.ell[cr_i];
     bool cw, cr;
     const double ow = log1mexp_d(lw, &cw), orr = log1mexp_d(lr, &cr);
     const double z = (lw - lr) - (ow - orr);
@@ -318,8 +329,15 @@ __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
     const double oms = z >= 0 ? exp(-z) / (1.0 + exp(-z)) : 1.0 / (1.0 + exp(z));   // 1 - sigmoid(z)
     const double fw = cw ? 1.0 : -1.0 / expm1(lw);
     const double fr = cr ? 1.0 : -1.0 / expm1(lr);
-    a.dl[2 * p] = (-1.0 - a.lam * oms * fw) / (double)a.P;
-    a.dl[2 * p + 1] = (a.lam * oms * fr) / (double)a.P;
+    if (S == 3) {
+      const double tot = (double)(a.cnt[3 * p] + a.cnt[3 * p + 1]);
+      a.dl[3 * p] = -((double)a.cnt[3 * p] / tot) / (double)a.P;
+      a.dl[cw_i] = (-((double)a.cnt[cw_i] / tot) - a.lam * oms * fw) / (double)a.P;
+      a.out[5 + 2 * a.P + p] = a.ell[3 * p];
+    } else {
+      a.dl[cw_i] = (-1.0 - a.lam * oms * fw) / (double)a.P;
+    }
+    a.dl[cr_i] = (a.lam * oms * fr) / (double)a.P;
     a.pair[p] = z;
     a.pair[a.P + p] = lor;
     a.pair[2 * a.P + p] = lw > lr ? 1.0 : 0.0;
@@ -330,7 +348,10 @@ __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
   if (tid == 0) {
     double nll = 0.0, orv = 0.0, acc = 0.0, mar = 0.0;
     for (int p = 0; p < a.P; ++p) {
-      nll -= a.ell[2 * p];
+      if (S == 3)
+        nll -= (a.sum[3 * p] + a.sum[3 * p + 1]) / (double)(a.cnt[3 * p] + a.cnt[3 * p + 1]);
+      else
+        nll -= a.ell[2 * p];
       orv += a.pair[a.P + p];
       acc += a.pair[2 * a.P + p];
       mar += a.pair[p];
@@ -342,12 +363,12 @@ __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
     a.out[3] = acc / P;
     a.out[4] = mar / P;
   }
-  // g_t = (dL/d ell_b) / n_b for a valid token of branch b (binary search over the offsets).
+  // g_t = (dL/d ell_s) / n_s for a valid token of span s (binary search over the offsets).
   for (int64_t t = tid; t < a.M; t += 1024) {
     float gv = 0.f;
-    const int y = t < a.M ? a.labels[t] : a.ignore_index;
-    if (t >= a.off[0] && t < a.off[nb] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
-      int lo = 0, hi = nb;   // find b with off[b] <= t < off[b+1]
+    const int y = a.labels[t];
+    if (t >= a.off[0] && t < a.off[ns] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
+      int lo = 0, hi = ns;   // find s with off[s] <= t < off[s+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if ((int64_t)a.off[mid] <= t) lo = mid; else hi = mid;

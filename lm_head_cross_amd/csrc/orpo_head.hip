@@ -178,7 +178,8 @@ size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc) {
 
 size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs) {
   if (M < 0 || n_pairs < 1) return 0;
-  return kHeader + round_up(size_t(n_pairs) * (2 * 3 + 3) * 8, 256);
+  // Up to 3 spans per pair: means, sums, dL/dmean, counts (3P each) and 3P per-pair terms.
+  return kHeader + round_up(size_t(n_pairs) * 15 * 8, 256);
 }
 
 orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
@@ -223,10 +224,12 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
   return launched();
 }
 
-orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, const float* logp,
-                      const int32_t* labels, int64_t V, int32_t ignore_index, double lambda,
-                      double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+static orpo_status loss_impl(int32_t S, int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
+                             const float* logp, const int32_t* labels, int64_t V,
+                             int32_t ignore_index, double lambda, double* out, float* g, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   if (M < 0 || M > INT32_MAX || n_pairs < 1 || V <= 0 || V > INT32_MAX) return ORPO_EINVAL;
+  if (n_pairs > INT32_MAX / 3) return ORPO_EINVAL;
   if (!seg_offsets || !out || (M > 0 && (!logp || !labels || !g))) return ORPO_EINVAL;
   if (!(lambda == lambda)) return ORPO_EINVAL;
   const size_t need = orpo_loss_workspace_bytes(M, n_pairs);
@@ -235,6 +238,7 @@ orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, co
   a.M = M;
   a.V = V;
   a.P = n_pairs;
+  a.S = S;
   a.off = seg_offsets;
   a.logp = logp;
   a.labels = labels;
@@ -243,14 +247,31 @@ orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, co
   a.out = out;
   a.g = g;
   double* base = (double*)((char*)ws + kHeader);
+  const size_t P3 = 3 * size_t(n_pairs);
   a.ell = base;
-  a.dl = base + 2 * size_t(n_pairs);
-  a.cnt = (int64_t*)(base + 4 * size_t(n_pairs));
-  a.pair = base + 6 * size_t(n_pairs);
+  a.sum = base + P3;
+  a.dl = base + 2 * P3;
+  a.cnt = (int64_t*)(base + 3 * P3);
+  a.pair = base + 4 * P3;
   a.status = (uint32_t*)ws;
   TraceScope ts(ORPO_K_LOSS, 0.0, stream);
   hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, stream, a);
   return launched();
+}
+
+orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, const float* logp,
+                      const int32_t* labels, int64_t V, int32_t ignore_index, double lambda,
+                      double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return loss_impl(2, M, n_pairs, seg_offsets, logp, labels, V, ignore_index, lambda, out, g, ws,
+                   ws_bytes, stream);
+}
+
+orpo_status orpo_loss_full(int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
+                           const float* logp, const int32_t* labels, int64_t V,
+                           int32_t ignore_index, double lambda, double* out, float* g, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  return loss_impl(3, M, n_pairs, seg_offsets, logp, labels, V, ignore_index, lambda, out, g, ws,
+                   ws_bytes, stream);
 }
 
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,

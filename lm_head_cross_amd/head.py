@@ -43,6 +43,9 @@ _SIGS = {
     "orpo_head_fwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "orpo_loss": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P]),
+    "orpo_loss_full": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
+                                      ctypes.c_int32, ctypes.c_double, _P, _P, _P, ctypes.c_size_t,
+                                      _P]),
     "orpo_head_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
     "orpo_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
@@ -141,17 +144,25 @@ def head_fwd(h, w, labels, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None, 
     return (logp, lse, ws) if return_ws else (logp, lse)
 
 
-def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, return_ws=False):
-    """out (float64 [5 + 2P]: loss, nll, or, accuracy, margin, lw[P], lr[P]) and g[M] (float32)."""
+SCOPES = {"response": 2, "full": 3}   # spans per pair in seg_offsets
+
+
+def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, return_ws=False,
+              scope="response"):
+    """out (float64) and g[M] (float32). scope "response": seg_offsets [2P+1] = (chosen, rejected)
+    per pair, out = [loss, nll, or, accuracy, margin, lw[P], lr[P]]; scope "full": seg_offsets
+    [3P+1] = (prompt, chosen, rejected) per pair, the NLL over prompt + chosen, out adds pm[P]."""
     _need_gpu(logp, labels, seg_offsets)
+    S = SCOPES[scope]
     M = logp.shape[0]
-    P = (seg_offsets.shape[0] - 1) // 2
+    P = (seg_offsets.shape[0] - 1) // S
     L = lib()
     ws = _workspace(L.orpo_loss_workspace_bytes(M, P), logp.device)
-    out = torch.empty(5 + 2 * P, dtype=torch.float64, device=logp.device)
+    out = torch.empty(5 + (S if S == 3 else 2) * P, dtype=torch.float64, device=logp.device)
     g = torch.empty(M, dtype=torch.float32, device=logp.device)
-    _check(L.orpo_loss(M, P, _ptr(seg_offsets), _ptr(logp), _ptr(labels), V, ignore_index, float(lam),
-                       _ptr(out), _ptr(g), _ptr(ws), ws.numel(), _stream(logp.device)), "orpo_loss")
+    fn = L.orpo_loss_full if S == 3 else L.orpo_loss
+    _check(fn(M, P, _ptr(seg_offsets), _ptr(logp), _ptr(labels), V, ignore_index, float(lam),
+              _ptr(out), _ptr(g), _ptr(ws), ws.numel(), _stream(logp.device)), "orpo_loss")
     return (out, g, ws) if return_ws else (out, g)
 
 
@@ -204,13 +215,14 @@ def trace_collect() -> dict:
 # ------------------------------------------------------------------------------------------------
 class HeadStep:
     def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
-                 want_dW=True, ignore_index=IGNORE_INDEX):
+                 want_dW=True, ignore_index=IGNORE_INDEX, scope="response"):
         _need_gpu(h, w, labels, seg_offsets, scales, biases)
         self.h, self.w, self.labels, self.off = h, w, labels, seg_offsets
         self.scales, self.biases = scales, biases
         self.M, self.d = h.shape
         self.V, self.softcap, self.lam, self.ignore = V, float(softcap), float(lam), ignore_index
-        self.P = (seg_offsets.shape[0] - 1) // 2
+        self.S = SCOPES[scope]
+        self.P = (seg_offsets.shape[0] - 1) // self.S
         dev = h.device
         self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
         L = lib()
@@ -219,7 +231,7 @@ class HeadStep:
         self.lws = _workspace(L.orpo_loss_workspace_bytes(self.M, self.P), dev)
         self.logp = torch.empty(self.M, dtype=torch.float32, device=dev)
         self.lse = torch.empty(self.M, dtype=torch.float32, device=dev)
-        self.out = torch.empty(5 + 2 * self.P, dtype=torch.float64, device=dev)
+        self.out = torch.empty(5 + (3 if self.S == 3 else 2) * self.P, dtype=torch.float64, device=dev)
         self.g = torch.empty(self.M, dtype=torch.float32, device=dev)
         self.dh = torch.empty(self.M, self.d, dtype=torch.float32, device=dev)
         self.dW = torch.empty(V, self.d, dtype=torch.float32, device=dev) if want_dW else None
@@ -236,9 +248,10 @@ class HeadStep:
                                    self._s()), "orpo_head_fwd")
 
     def loss(self):
-        _check(lib().orpo_loss(self.M, self.P, _ptr(self.off), _ptr(self.logp), _ptr(self.labels),
-                               self.V, self.ignore, self.lam, _ptr(self.out), _ptr(self.g),
-                               _ptr(self.lws), self.lws.numel(), self._s()), "orpo_loss")
+        fn = lib().orpo_loss_full if self.S == 3 else lib().orpo_loss
+        _check(fn(self.M, self.P, _ptr(self.off), _ptr(self.logp), _ptr(self.labels), self.V,
+                  self.ignore, self.lam, _ptr(self.out), _ptr(self.g), _ptr(self.lws),
+                  self.lws.numel(), self._s()), "orpo_loss")
 
     def backward(self):
         _check(lib().orpo_head_bwd(ctypes.byref(self.desc), _ptr(self.h), self.wt, _ptr(self.labels),

@@ -45,6 +45,17 @@ class HeadConfig:
     lam: float
     dtype: str = "bf16"      # "f32" or "bf16" (h and W)
     q4: bool = False         # W as 4-bit group-encoded (group 64 along d)
+    prompt_lo: int = 0       # prompt span lengths U[prompt_lo, prompt_hi] per pair; prompt_hi = 0:
+    prompt_hi: int = 0       # no prompt spans (response-scope NLL)
+
+    @property
+    def scope(self) -> str:
+        """NLL scope of the workload: "full" (prompt + chosen) when it has prompt spans."""
+        return "full" if self.prompt_hi > 0 else "response"
+
+    @property
+    def spans_per_pair(self) -> int:
+        return 3 if self.prompt_hi > 0 else 2
 
     def replace(self, **kw) -> "HeadConfig":
         return dataclasses.replace(self, **kw)
@@ -61,12 +72,16 @@ CONFIGS = {
                   len_hi=384, softcap=30.0, lam=0.1, q4=True),
     5: HeadConfig(5, "12b-like-bf16-softcap30", M=32768, d=3840, V=262144, pairs=32, len_lo=256,
                   len_hi=768, softcap=30.0, lam=0.2),
+    # The e4b head with the full-scope NLL: each pair's chosen sequence also carries its prompt span.
+    6: HeadConfig(6, "e4b-bf16-softcap30-fullnll", M=8192, d=2560, V=262144, pairs=16, len_lo=144,
+                  len_hi=240, softcap=30.0, lam=0.1, prompt_lo=64, prompt_hi=128),
 }
 
 
 def reduced(cfg: HeadConfig, pairs: int = 1) -> HeadConfig:
     """Same d, V, softcap and distributions with only `pairs` pairs; M = the largest packing."""
-    return cfg.replace(pairs=pairs, M=2 * pairs * cfg.len_hi, name=cfg.name + f"-{pairs}pair")
+    return cfg.replace(pairs=pairs, M=pairs * (2 * cfg.len_hi + cfg.prompt_hi),
+                       name=cfg.name + f"-{pairs}pair")
 
 
 def _streams(key: int, seed: int):
@@ -146,8 +161,8 @@ class HeadInputs:
     scales: torch.Tensor | None     # [V, d/64] bfloat16 (q4 only)
     biases: torch.Tensor | None     # [V, d/64] bfloat16 (q4 only)
     labels: np.ndarray              # [M] int32, -100 for padding
-    seg_offsets: np.ndarray         # [2P+1] int32
-    lengths: np.ndarray             # [2P] int64
+    seg_offsets: np.ndarray         # [2P+1] int32 ([3P+1] with prompt spans)
+    lengths: np.ndarray             # [2P] int64 ([3P])
 
     @property
     def n_valid(self) -> int:
@@ -158,6 +173,15 @@ def make_inputs(cfg: HeadConfig, seed: int = 0, label_device: str = "cpu") -> He
     r_len, r_h, r_w, r_coin, r_uni = _streams(cfg.key, seed)
     M, d, V = cfg.M, cfg.d, cfg.V
     lens = draw_lengths(r_len, 2 * cfg.pairs, cfg.len_lo, cfg.len_hi, M)
+    if cfg.prompt_hi > 0:
+        # Spans per pair: prompt, chosen, rejected (prompt lengths drawn after the responses', so a
+        # workload without prompts draws exactly what it did before prompts existed).
+        resp = lens
+        prompts = r_len.integers(cfg.prompt_lo, cfg.prompt_hi + 1, size=cfg.pairs).astype(np.int64)
+        lens = np.stack([prompts, resp[0::2], resp[1::2]], axis=1).reshape(-1)
+        tot = int(lens.sum())
+        if tot > M:
+            lens = np.maximum(1, (lens * M) // tot)
     off = seg_offsets_from_lengths(lens)
 
     h64 = r_h.standard_normal((M, d))

@@ -62,7 +62,7 @@ def run_gpu(inp: synth.HeadInputs, want_dW=None, g_override=None):
     labels = torch.from_numpy(inp.labels).to(d)
     off = torch.from_numpy(inp.seg_offsets).to(d)
     logp, lse, fws = H.head_fwd(h, w, labels, cfg.softcap, scales=sc, biases=bi, return_ws=True)
-    out, g, lws = H.orpo_loss(logp, labels, off, cfg.V, cfg.lam, return_ws=True)
+    out, g, lws = H.orpo_loss(logp, labels, off, cfg.V, cfg.lam, return_ws=True, scope=cfg.scope)
     gg = g if g_override is None else g_override.to(d)
     dh, dW = H.head_bwd(h, w, labels, lse, gg, cfg.softcap, want_dW=want_dW, scales=sc, biases=bi)
     torch.cuda.synchronize()
@@ -72,6 +72,7 @@ def run_gpu(inp: synth.HeadInputs, want_dW=None, g_override=None):
         "logp": logp.cpu().numpy(), "lse": lse.cpu().numpy(), "g": g.cpu().numpy(),
         "loss": o[0], "nll": o[1], "or": o[2], "accuracy": o[3], "margin": o[4],
         "lw": o[5:5 + P], "lr": o[5 + P:5 + 2 * P],
+        "pm": o[5 + 2 * P:5 + 3 * P] if cfg.scope == "full" else None,
         "dh": dh.cpu().numpy(), "dW": None if dW is None else dW.cpu().numpy(),
         "fwd_status": H.read_status(fws), "loss_status": H.read_status(lws),
     }
@@ -82,8 +83,8 @@ def run_oracle(inp: synth.HeadInputs, want_dW=None):
         want_dW = not inp.cfg.q4
     W = oracle_weight(inp)
     h = inp.h.float().numpy().astype(np.float64)
-    return orc.head_step(h, W, inp.labels, inp.seg_offsets, inp.cfg.softcap, inp.cfg.lam,
-                         want_dW=want_dW)
+    step = orc.head_step_full if inp.cfg.scope == "full" else orc.head_step
+    return step(h, W, inp.labels, inp.seg_offsets, inp.cfg.softcap, inp.cfg.lam, want_dW=want_dW)
 
 
 def assert_parity(gpu, ora, label=""):
@@ -101,9 +102,12 @@ def assert_parity(gpu, ora, label=""):
     }
     if ora.get("dW") is not None and gpu.get("dW") is not None:
         errs["dW"] = rel(gpu["dW"], ora["dW"])
+    if gpu.get("pm") is not None:
+        errs["pm"] = rel(gpu["pm"], ora["pm"])
     say(f"[parity {label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k in ("logp", "lse", "lw", "lr", "loss", "nll", "g"):
-        assert errs[k] <= TOL_SCALAR, (k, errs[k])
+    for k in ("logp", "lse", "lw", "lr", "loss", "nll", "g", "pm"):
+        if k in errs:
+            assert errs[k] <= TOL_SCALAR, (k, errs[k])
     # The odds-ratio term and the margin are gated by what the 1e-3 branch-mean gate implies for
     # them: |d log_odds| <= F(lw)|d lw| + F(lr)|d lr| with F(l) = 1/(1 - e^l) and |d softplus(-z)/dz|
     # = 1 - sigmoid(z), so a branch-mean error of TOL * |ell| allows these absolute errors.

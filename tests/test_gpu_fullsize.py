@@ -32,7 +32,7 @@ def _sample_rows(inp, n_per_branch=2, seed=0):
     return np.unique(np.array(rows, dtype=np.int64))
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5])
+@pytest.mark.parametrize("key", [2, 3, 4, 5, 6])
 def test_full_size_sampled_parity(key):
     cfg = synth.CONFIGS[key]
     say(f"[fullsize] {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}")
@@ -47,7 +47,7 @@ def test_full_size_sampled_parity(key):
     labels = torch.from_numpy(inp.labels).to(d)
     off = torch.from_numpy(inp.seg_offsets).to(d)
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                      want_dW=not cfg.q4)
+                      want_dW=not cfg.q4, scope=cfg.scope)
     step.forward()
     step.loss()
     torch.cuda.synchronize()
@@ -68,10 +68,16 @@ def test_full_size_sampled_parity(key):
     assert e_logp <= TOL_SCALAR and e_lse <= TOL_SCALAR
 
     # Loss epilogue on the GPU's logp vector, in float64.
-    ell, n = orc.branch_means(logp, inp.labels, inp.seg_offsets)
-    ep = orc.orpo_epilogue(ell, cfg.lam)
-    gref = orc.token_cotangent(ep["dL_dell"], n, inp.labels, inp.seg_offsets)
     P = cfg.pairs
+    if cfg.scope == "full":
+        mean, n = orc.span_means_full(logp, inp.labels, inp.seg_offsets)
+        ep = orc.orpo_epilogue_full(mean, n, cfg.lam)
+        gref = orc.token_cotangent_full(ep["dL_dmean"], n, inp.labels, inp.seg_offsets)
+        assert np.allclose(out[5 + 2 * P:5 + 3 * P], ep["pm"], rtol=1e-9, atol=1e-12)
+    else:
+        ell, n = orc.branch_means(logp, inp.labels, inp.seg_offsets)
+        ep = orc.orpo_epilogue(ell, cfg.lam)
+        gref = orc.token_cotangent(ep["dL_dell"], n, inp.labels, inp.seg_offsets)
     for i, k in enumerate(("loss", "nll", "or", "accuracy", "margin")):
         assert abs(out[i] - ep[k]) <= 1e-9 * max(1.0, abs(ep[k])), k
     assert np.allclose(out[5:5 + P], ep["lw"], rtol=1e-9, atol=1e-12)

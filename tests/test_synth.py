@@ -48,3 +48,21 @@ def test_q4_encoding_roundtrip_error_is_half_a_step():
     inside = (w - lo) <= 15 * step
     err = np.abs(deq - w)
     assert np.all(err[inside] <= 0.5 * step[inside] * (1 + 1e-2) + 1e-7)
+
+
+def test_prompt_spans_layout():
+    # The full-NLL workload: per pair (prompt, chosen, rejected), prompt lengths in their range (up to
+    # the packing scale), responses in theirs, all within M; the response-scope draws are unchanged
+    # by the prompt option (same seed, same response lengths before any packing scale).
+    cfg = synth.reduced(synth.CONFIGS[6], 3).replace(d=256, V=4096)   # layout only: small head
+    inp = synth.make_inputs(cfg, seed=2)
+    assert cfg.scope == "full" and cfg.spans_per_pair == 3
+    off = inp.seg_offsets
+    assert off.shape == (3 * 3 + 1,) and off[0] == 0 and off[-1] <= cfg.M
+    assert np.all(np.diff(off) >= 1)
+    lens = np.diff(off)
+    assert np.all((lens[0::3] >= 1) & (lens[0::3] <= cfg.prompt_hi))
+    base = synth.make_inputs(cfg.replace(prompt_lo=0, prompt_hi=0), seed=2)
+    assert base.seg_offsets.shape == (2 * 3 + 1,)
+    resp = np.stack([lens[1::3], lens[2::3]], axis=1).reshape(-1)
+    assert np.array_equal(resp, np.diff(base.seg_offsets))
