@@ -6,15 +6,18 @@
 // 128 x 64 sub-tile = 4 x 2 MFMA blocks = 128 accumulator registers per lane.
 //
 // Operands are staged through LDS, 128 bytes of K per row per stage (64 bf16 / 32 fp32), in two
-// stages with one barrier per K step. Dense operands go global -> LDS directly
-// (buffer_load_dwordx4 ... lds): each wave instruction fills 1 KiB of LDS, lane l writing bytes
-// [16 l, 16 l + 16), and the buffer descriptor's range check returns zeros past the operand's last
-// valid row, so tails need no VALU work and loads need no staging registers. 4-bit weights take a
-// register path that dequantises on the way into LDS.
+// stages. Dense operands go global -> LDS directly (buffer_load_dwordx4 ... lds): each wave
+// instruction fills 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16), and the buffer
+// descriptor's range check returns zeros past the operand's last valid row, so tails need no VALU
+// work and loads need no staging registers. 4-bit weights take a register path that dequantises on
+// the way into LDS. Within a K step the fragments of K group g + 1 are read while group g's MFMAs
+// run (one read between consecutive MFMAs, pinned with sched_group_barrier); for K-major x K-major
+// stages the step's barrier sits before its last K group (gemm_step), for the others at its end
+// (gemm_step_end).
 //
 // Each operand tile keeps its global orientation in LDS, unpadded and XOR-swizzled per 16-byte
 // chunk (chunk c of row r is stored at chunk c ^ swz(r)):
-//   K-major  ([rows][k], k contiguous):   [256 rows][128 B], swz = (r ^ (r >> 3)) & 7;
+//   K-major  ([rows][k], k contiguous):   [256 rows][128 B], swz = r & 7;
 //                                          fragments via ds_read_b128.
 //   MN-major ([k][cols], cols contiguous): bf16 [64 rows][512 B], swz = 10 (r & 3);
 //                                          fragments via the transposing ds_read_b64_tr_b16.
