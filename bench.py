@@ -31,15 +31,42 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    ap.add_argument("--objective", default="orpo", choices=["orpo", "simpo", "dpo", "grpo"],
+                    help="the loss between the head's forward and backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
 
 
-def cpu_baseline(inp, rows: int):
+def _objective_inputs(objective: str, cfg, off: np.ndarray, n_valid_per_span: np.ndarray, M: int,
+                      seed: int) -> dict:
+    """Seeded synthetic inputs of the sibling objectives (parameters and cached reference values);
+    timing only. SimPO beta 2, gamma 0.5; DPO beta 0.1 with reference sums near the head's scale;
+    GRPO clip 0.2, KL weight 0.04, groups of 4 completions; the sampling and reference policies'
+    log-probs are filled in by main() from the policy's own forward plus seeded noise."""
+    import numpy as np
+    rng = np.random.default_rng(9000 + seed)
+    if objective == "simpo":
+        return {"beta": 2.0, "gamma": 0.5}
+    if objective == "dpo":
+        ref = -7.7 * n_valid_per_span + rng.normal(0.0, 5.0, size=n_valid_per_span.shape)
+        return {"beta": 0.1, "ref_sums": ref}
+    if objective == "grpo":
+        S = len(off) - 1
+        rewards = rng.normal(size=S + (-S) % 4)
+        r = rewards.reshape(-1, 4)
+        adv = ((r - r.mean(axis=1, keepdims=True)) / (r.std(axis=1, keepdims=True) + 1e-6)).reshape(-1)[:S]
+        return {"clip_eps": 0.2, "beta": 0.04, "advantages": adv.astype(np.float32),
+                "old_noise": rng.normal(0.0, 0.1, size=M).astype(np.float32),
+                "ref_noise": rng.normal(0.0, 0.2, size=M).astype(np.float32)}
+    return {}
+
+
+def cpu_baseline(inp, rows: int, objective: str):
     """The float64 oracle as it stands, on a bounded sample of the same batch, on the host cores."""
     import numpy as np
     from threadpoolctl import threadpool_info
+    from oracle import objectives as ob
     from oracle import orpo_oracle as orc
     from lm_head_cross_amd import synth
 
@@ -54,19 +81,34 @@ def cpu_baseline(inp, rows: int):
     # time; the three [rows, V] x d products dominate).
     labels[labels == synth.IGNORE_INDEX] = 0
     t0 = time.perf_counter()
-    if cfg.scope == "full":     # one pair: prompt, chosen, rejected thirds
+    if objective == "orpo" and cfg.scope == "full":     # prompt, chosen, rejected thirds
         off = np.array([0, rows // 3, 2 * rows // 3, rows], dtype=np.int32)
         out = orc.head_step_full(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
-    else:
+    elif objective == "orpo":
         off = np.array([0, rows // 2, rows], dtype=np.int32)
         out = orc.head_step(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
+    else:
+        off = np.array([0, rows // 2, rows], dtype=np.int32)
+        logp, lse = orc.forward(h, W, labels, cfg.softcap)
+        sums, n = ob.span_stats(logp, labels, off)
+        if objective == "simpo":
+            ep = ob.simpo_epilogue(sums[0::2] / n[0::2], sums[1::2] / n[1::2], 2.0, 0.5)
+            g = ob.pairwise_cotangent("simpo", ep, n, labels, off)
+        elif objective == "dpo":
+            ep = ob.dpo_epilogue(sums[0::2], sums[1::2], sums[0::2] - 1.0, sums[1::2], 0.1)
+            g = ob.pairwise_cotangent("dpo", ep, n, labels, off)
+        else:
+            ep = ob.grpo_loss(logp, logp - 0.1, logp + 0.1, labels, off, np.array([1.0, -1.0]), 0.2, 0.04)
+            g = ep["g"]
+        orc.backward(h, W, labels, lse, g, cfg.softcap, want_dW=not cfg.q4)
+        out = ep
     dt = time.perf_counter() - t0
     assert math.isfinite(out["loss"])
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {
         "value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
         "sample": f"first {rows} tokens of the same batch (full V={cfg.V}, d={cfg.d}), float64 "
-                  f"forward + loss + backward{' + dW' if not cfg.q4 else ''}; {dt:.1f} s",
+                  f"forward + {objective} loss + backward{' + dW' if not cfg.q4 else ''}; {dt:.1f} s",
     }
 
 
@@ -99,8 +141,25 @@ def main():
     torch.cuda.synchronize()
     inputs_bytes = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
+    obj = None
+    if args.objective != "orpo":
+        if cfg.scope == "full":
+            print("sibling objectives take (chosen, rejected) spans: use a response-scope workload",
+                  file=sys.stderr)
+            sys.exit(2)
+        n_span = np.array([int((inp.labels[a:b] != synth.IGNORE_INDEX).sum())
+                           for a, b in zip(inp.seg_offsets[:-1], inp.seg_offsets[1:])], dtype=np.float64)
+        o = _objective_inputs(args.objective, cfg, inp.seg_offsets, n_span, cfg.M, args.seed)
+        obj = {k: (torch.from_numpy(v).to(dev) if isinstance(v, np.ndarray) else v) for k, v in o.items()}
+        if args.objective == "grpo":   # old / reference log-probs: the policy's own, perturbed
+            pre = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
+                             want_dW=False)
+            pre.forward()
+            obj["old_logp"] = pre.logp + obj.pop("old_noise")
+            obj["ref_logp"] = pre.logp + obj.pop("ref_noise")
+            del pre
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                      want_dW=not cfg.q4, scope=cfg.scope)
+                      want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -161,7 +220,7 @@ def main():
         auto = int(4e12 / (6 * cfg.V * cfg.d)) // 128 * 128
         rows = args.cpu_rows or max(128, min(cfg.M, auto))
         print(f"[bench] oracle cpu baseline on {rows} rows", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, rows)
+        cpu = cpu_baseline(inp, rows, args.objective)
 
     line = {
         "metric": "ORPO head fwd+bwd tokens/s (d=2560,V=262144); % bf16 MFMA peak; peak GB",
@@ -179,6 +238,7 @@ def main():
         "config": {
             "workload": cfg.name, "M": cfg.M, "valid_tokens": n_valid, "d": cfg.d, "V": cfg.V,
             "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam, "nll_scope": cfg.scope,
+            "objective": args.objective,
             "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
             "parallelism": "single GPU",
         },

@@ -152,6 +152,62 @@ orpo_status orpo_loss_full(int64_t M, int32_t n_pairs, const int32_t* seg_offset
                            size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Sibling objectives on the same per-token log-probs (orpo_head_fwd's logp) and the same backward
+ * (orpo_head_bwd takes their g). Workspace for both entry points below:
+ * orpo_objective_workspace_bytes(M, n_spans) with n_spans = 2 * n_pairs or n_seqs.
+ */
+size_t orpo_objective_workspace_bytes(int64_t M, int32_t n_spans);
+
+typedef enum { ORPO_PREF_SIMPO = 1, ORPO_PREF_DPO = 2 } orpo_pref_kind;
+
+/*
+ * orpo_pref_loss — pairwise preference losses (chosen span 2p, rejected span 2p+1 of seg_offsets,
+ * [2*n_pairs + 1] monotone within [0, M]; only valid labels count, as in orpo_loss).
+ *   ORPO_PREF_SIMPO: lw, lr = mean logp of each span; per pair
+ *     L = softplus(-beta ((lw - lr) - gamma)); accuracy = mean 1[lw > lr]; margin = mean (lw - lr).
+ *     ("Training — design" §8.3 "Objective variants and data".)
+ *   ORPO_PREF_DPO: sw, sr = summed logp of each span (the sequence log-prob); with the cached
+ *     reference sums ref_sums (device double [2*n_pairs], same span order),
+ *     Delta = beta [(sw - ref_w) - (sr - ref_r)], L = -log sigmoid(Delta); accuracy = mean
+ *     1[Delta > 0]; margin = mean Delta. gamma is unused. (The post-training design page, "Stage
+ *     P1 — DPO": seq_logprob as a per-sequence sum, the DPO loss, only policy terms carry
+ *     gradient.)
+ *   loss = mean over pairs. g_t = dloss/dlogp_t: dL/dlw / n_w for SimPO (a mean), dL/dsw for DPO (a
+ *   sum); 0 for ignored / off-span tokens.
+ *   out   (device) double [3 + 2*n_pairs]: loss, accuracy, margin, then the chosen values [n_pairs]
+ *         (lw or sw), then the rejected ones [n_pairs]
+ *   Errors and status bits as for orpo_loss (ORPO_EINVAL also for an unknown kind or a DPO call
+ *   without ref_sums).
+ */
+orpo_status orpo_pref_loss(int32_t kind, int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
+                           const float* logp, const int32_t* labels, int64_t V,
+                           int32_t ignore_index, double beta, double gamma, const double* ref_sums,
+                           double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * orpo_grpo_loss — GRPO's clipped policy-gradient loss with the k3 KL term, per completion token
+ * (the post-training design page, "Stage P3 — GRPO", (c) and (d)).
+ *   Completion s covers tokens [seg_offsets[s], seg_offsets[s+1]) (int32 [n_seqs + 1], monotone
+ *   within [0, M]); only its valid labels count. With rho_t = exp(logp_t - old_logp_t) and the
+ *   completion's advantage A_s (advantages: device float [n_seqs], e.g. group-normalised rewards):
+ *     pg_t = -min(rho_t A_s, clip(rho_t, 1 - clip_eps, 1 + clip_eps) A_s),
+ *     k3_t = exp(ref_t - logp_t) - (ref_t - logp_t) - 1,
+ *     loss = mean_s [ mean_{t in s} (pg_t + beta k3_t) ]   (per-completion token mean, then mean).
+ *   g_t = (dpg_t + beta dk3_t) / (n_s n_seqs): dpg_t = -A_s rho_t where the unclipped term is the
+ *   minimum (ties included), 0 where the clipped one is; dk3_t = 1 - exp(ref_t - logp_t).
+ *   old_logp, ref_logp (device) float [M]: the sampling policy's and the reference's log-probs of
+ *   the same tokens (inputs; no gradient flows into them).
+ *   out   (device) double [4]: loss, pg (mean policy-gradient term), kl (mean k3), clip fraction
+ *         (share of valid tokens whose clipped term is the strict minimum)
+ *   Errors and status bits as for orpo_loss (an empty completion sets ORPO_STATUS_EMPTY_BRANCH).
+ */
+orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets,
+                           const float* logp, const float* old_logp, const float* ref_logp,
+                           const float* advantages, const int32_t* labels, int64_t V,
+                           int32_t ignore_index, double clip_eps, double beta, double* out,
+                           float* g, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * orpo_head_bwd — dh = coeff . W and dW = coeff^T . h, recomputing the logits tile by tile.
  *   coeff_tv = g_t * (1[v = y_t] - exp(z_tv - lse_t)) * sech^2(raw_tv / softcap)   (sech^2 = 1
  *   without a softcap). ("ORPO training — design", the spec's backward: recompute each vocabulary

@@ -1,0 +1,260 @@
+// objective_kernels.hpp — scalar epilogues of the sibling objectives that reuse the head's forward
+// (per-token log-probs) and backward (per-token cotangent g). Each runs in one 1024-thread
+// workgroup, in float64, with fixed-order reductions (results are bitwise repeatable).
+#pragma once
+#include "head_kernels.hpp"
+
+namespace orpo {
+
+enum : int32_t { kPrefSimpo = 1, kPrefDpo = 2 };
+
+__device__ __forceinline__ double softplus_d(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+__device__ __forceinline__ double sigmoid_d(double x) {
+  return x >= 0 ? 1.0 / (1.0 + exp(-x)) : exp(x) / (1.0 + exp(x));
+}
+
+// Checks that off[0..n] is monotone within [0, M]; sets the status word; true when it is not.
+__device__ __forceinline__ bool check_offsets(const int32_t* off, int n, int64_t M, uint32_t* status,
+                                              int* bad) {
+  if (threadIdx.x == 0) {
+    int b = off[0] < 0 || (int64_t)off[n] > M;
+    for (int i = 0; i < n; ++i) b |= off[i + 1] < off[i];
+    *bad = b;
+    *status = b ? kStatusBadOffsets : 0u;
+  }
+  __syncthreads();
+  return *bad != 0;
+}
+
+// Sum of logp over the valid tokens of span s and their count, one wave per span (fixed order).
+__device__ __forceinline__ void span_sum(const int32_t* off, int s, const float* logp,
+                                         const int32_t* labels, int32_t ignore, int64_t V,
+                                         double* sum_out, long long* n_out) {
+  const int l = threadIdx.x & 63;
+  double sum = 0.0;
+  long long n = 0;
+  for (int64_t t = off[s] + l; t < off[s + 1]; t += 64) {
+    const int y = labels[t];
+    if (y != ignore && y >= 0 && (int64_t)y < V) {
+      sum += (double)logp[t];
+      ++n;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o);
+    n += __shfl_xor(n, o);
+  }
+  *sum_out = sum;
+  *n_out = n;
+}
+
+// Span index of token t (off[s] <= t < off[s+1]) by binary search over off[0..n].
+__device__ __forceinline__ int span_of(const int32_t* off, int n, int64_t t) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)off[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+struct PrefArgs {
+  int32_t kind;           // kPrefSimpo or kPrefDpo
+  int64_t M, V;
+  int32_t P;
+  const int32_t* off;     // [2P+1]: chosen 2p, rejected 2p+1
+  const float* logp;
+  const int32_t* labels;
+  int32_t ignore_index;
+  double beta, gamma;
+  const double* ref;      // [2P] reference sequence sums (DPO)
+  double* out;            // [3 + 2P]: loss, accuracy, margin, v_w[P], v_r[P]
+  float* g;
+  double* val;            // ws [2P]: per-span value (mean for SimPO, sum for DPO)
+  double* dv;             // ws [2P]: dL/dvalue
+  long long* cnt;         // ws [2P]
+  double* pair;           // ws [3P]: loss term, accuracy bit, margin term
+  uint32_t* status;
+};
+
+// SimPO (Training — design, §8.3 "Objective variants and data"): per pair
+// L = softplus(-beta ((lw - lr) - gamma)) on the length-normalised means. DPO (the post-training
+// design's "Stage P1 — DPO"): Delta = beta [(s_w - ref_w) - (s_r - ref_r)] on per-sequence sums,
+// L = -log sigma(Delta). loss = mean over pairs; g_t = dL/dvalue_s / n_s (SimPO) or dL/dvalue_s
+// (DPO) for a valid token of span s.
+__global__ __launch_bounds__(1024) void pref_loss_kernel(PrefArgs a) {
+  __shared__ int bad;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, ns = 2 * a.P;
+  const double nan = __builtin_nan("");
+  if (check_offsets(a.off, ns, a.M, a.status, &bad)) {
+    for (int i = tid; i < 3 + ns; i += 1024) a.out[i] = nan;
+    for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
+    return;
+  }
+  for (int s = w; s < ns; s += 16) {
+    double sum;
+    long long n;
+    span_sum(a.off, s, a.logp, a.labels, a.ignore_index, a.V, &sum, &n);
+    if (l == 0) {
+      a.cnt[s] = n;
+      a.val[s] = n == 0 ? nan : (a.kind == kPrefSimpo ? sum / (double)n : sum);
+      if (n == 0) atomicOr(a.status, kStatusEmptyBranch);
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < a.P; p += 1024) {
+    const double vw = a.val[2 * p], vr = a.val[2 * p + 1];
+    double u, margin, acc;
+    if (a.kind == kPrefSimpo) {
+      u = a.beta * ((vw - vr) - a.gamma);
+      margin = vw - vr;
+      acc = vw > vr ? 1.0 : 0.0;
+    } else {
+      u = a.beta * ((vw - a.ref[2 * p]) - (vr - a.ref[2 * p + 1]));
+      margin = u;
+      acc = u > 0 ? 1.0 : 0.0;
+    }
+    const double d = -a.beta * sigmoid_d(-u) / (double)a.P;
+    a.dv[2 * p] = d;
+    a.dv[2 * p + 1] = -d;
+    a.pair[p] = softplus_d(-u);
+    a.pair[a.P + p] = acc;
+    a.pair[2 * a.P + p] = margin;
+    a.out[3 + p] = vw;
+    a.out[3 + a.P + p] = vr;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double lo = 0.0, ac = 0.0, mg = 0.0;
+    for (int p = 0; p < a.P; ++p) {
+      lo += a.pair[p];
+      ac += a.pair[a.P + p];
+      mg += a.pair[2 * a.P + p];
+    }
+    a.out[0] = lo / (double)a.P;
+    a.out[1] = ac / (double)a.P;
+    a.out[2] = mg / (double)a.P;
+  }
+  for (int64_t t = tid; t < a.M; t += 1024) {
+    float gv = 0.f;
+    const int y = a.labels[t];
+    if (t >= a.off[0] && t < a.off[ns] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
+      const int s = span_of(a.off, ns, t);
+      gv = (float)(a.kind == kPrefSimpo ? a.dv[s] / (double)a.cnt[s] : a.dv[s]);
+    }
+    a.g[t] = gv;
+  }
+}
+
+struct GrpoArgs {
+  int64_t M, V;
+  int32_t S;              // completions
+  const int32_t* off;     // [S+1]
+  const float* logp;
+  const float* old_logp;
+  const float* ref_logp;
+  const float* adv;       // [S]
+  const int32_t* labels;
+  int32_t ignore_index;
+  double eps, beta;
+  double* out;            // [4]: loss, pg, kl, clip fraction
+  float* g;
+  double* pg;             // ws [S] per-completion mean of the policy-gradient term
+  double* kl;             // ws [S] per-completion mean k3
+  long long* cnt;         // ws [S]
+  long long* clipped;     // ws [S]
+  uint32_t* status;
+};
+
+// One token's policy-gradient term, k3 term and their derivatives w.r.t. logp (the post-training
+// design's "Stage P3 — GRPO", (d)): rho = exp(logp - old); pg = -min(rho A, clip(rho, 1-eps, 1+eps) A);
+// k3 = exp(ref - logp) - (ref - logp) - 1. d pg / d logp = -A rho where the unclipped term is the
+// minimum (ties included), else 0; d k3 / d logp = 1 - exp(ref - logp).
+struct GrpoToken {
+  double pg, k3, dpg, dk3;
+  bool clipped;
+};
+__device__ __forceinline__ GrpoToken grpo_token(double lp, double old, double ref, double A, double eps) {
+  GrpoToken r;
+  const double rho = exp(lp - old);
+  const double un = rho * A, cl = fmin(fmax(rho, 1.0 - eps), 1.0 + eps) * A;
+  r.clipped = un > cl;
+  r.pg = -(r.clipped ? cl : un);
+  r.dpg = r.clipped ? 0.0 : -A * rho;
+  const double d = ref - lp, ed = exp(d);
+  r.k3 = ed - d - 1.0;
+  r.dk3 = 1.0 - ed;
+  return r;
+}
+
+// loss = mean over completions of (mean over the completion's valid tokens of pg + beta k3);
+// g_t = (dpg + beta dk3) / (n_s S).
+__global__ __launch_bounds__(1024) void grpo_loss_kernel(GrpoArgs a) {
+  __shared__ int bad;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const double nan = __builtin_nan("");
+  if (check_offsets(a.off, a.S, a.M, a.status, &bad)) {
+    for (int i = tid; i < 4; i += 1024) a.out[i] = nan;
+    for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
+    return;
+  }
+  for (int s = w; s < a.S; s += 16) {
+    double pg = 0.0, kl = 0.0;
+    long long n = 0, c = 0;
+    const double A = (double)a.adv[s];
+    for (int64_t t = a.off[s] + l; t < a.off[s + 1]; t += 64) {
+      const int y = a.labels[t];
+      if (y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
+        const GrpoToken r = grpo_token(a.logp[t], a.old_logp[t], a.ref_logp[t], A, a.eps);
+        pg += r.pg;
+        kl += r.k3;
+        ++n;
+        c += r.clipped;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      pg += __shfl_xor(pg, o);
+      kl += __shfl_xor(kl, o);
+      n += __shfl_xor(n, o);
+      c += __shfl_xor(c, o);
+    }
+    if (l == 0) {
+      a.cnt[s] = n;
+      a.clipped[s] = c;
+      a.pg[s] = n ? pg / (double)n : nan;
+      a.kl[s] = n ? kl / (double)n : nan;
+      if (n == 0) atomicOr(a.status, kStatusEmptyBranch);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double pg = 0.0, kl = 0.0;
+    long long n = 0, c = 0;
+    for (int s = 0; s < a.S; ++s) {
+      pg += a.pg[s];
+      kl += a.kl[s];
+      n += a.cnt[s];
+      c += a.clipped[s];
+    }
+    pg /= (double)a.S;
+    kl /= (double)a.S;
+    a.out[0] = pg + a.beta * kl;
+    a.out[1] = pg;
+    a.out[2] = kl;
+    a.out[3] = n ? (double)c / (double)n : nan;
+  }
+  for (int64_t t = tid; t < a.M; t += 1024) {
+    float gv = 0.f;
+    const int y = a.labels[t];
+    if (t >= a.off[0] && t < a.off[a.S] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
+      const int s = span_of(a.off, a.S, t);
+      const GrpoToken r = grpo_token(a.logp[t], a.old_logp[t], a.ref_logp[t], (double)a.adv[s], a.eps);
+      gv = (float)((r.dpg + a.beta * r.dk3) / ((double)a.cnt[s] * (double)a.S));
+    }
+    a.g[t] = gv;
+  }
+}
+
+}  // namespace orpo

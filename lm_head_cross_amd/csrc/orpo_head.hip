@@ -9,7 +9,7 @@
 #include <vector>
 
 #include "../../include/orpo_head.h"
-#include "head_kernels.hpp"
+#include "objective_kernels.hpp"
 
 namespace {
 
@@ -272,6 +272,87 @@ orpo_status orpo_loss_full(int64_t M, int32_t n_pairs, const int32_t* seg_offset
                            size_t ws_bytes, hipStream_t stream) {
   return loss_impl(3, M, n_pairs, seg_offsets, logp, labels, V, ignore_index, lambda, out, g, ws,
                    ws_bytes, stream);
+}
+
+size_t orpo_objective_workspace_bytes(int64_t M, int32_t n_spans) {
+  if (M < 0 || n_spans < 1) return 0;
+  return kHeader + round_up(size_t(n_spans) * 8 * 8, 256);
+}
+
+orpo_status orpo_pref_loss(int32_t kind, int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
+                           const float* logp, const int32_t* labels, int64_t V,
+                           int32_t ignore_index, double beta, double gamma, const double* ref_sums,
+                           double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (kind != ORPO_PREF_SIMPO && kind != ORPO_PREF_DPO) return ORPO_EINVAL;
+  if (M < 0 || M > INT32_MAX || n_pairs < 1 || n_pairs > INT32_MAX / 2 || V <= 0 || V > INT32_MAX)
+    return ORPO_EINVAL;
+  if (!seg_offsets || !out || (M > 0 && (!logp || !labels || !g))) return ORPO_EINVAL;
+  if (kind == ORPO_PREF_DPO && !ref_sums) return ORPO_EINVAL;
+  if (!(beta == beta) || !(gamma == gamma)) return ORPO_EINVAL;
+  if (!ws || ws_bytes < orpo_objective_workspace_bytes(M, 2 * n_pairs) || (uintptr_t)ws % 256)
+    return ORPO_ENOWS;
+  PrefArgs a;
+  a.kind = kind;
+  a.M = M;
+  a.V = V;
+  a.P = n_pairs;
+  a.off = seg_offsets;
+  a.logp = logp;
+  a.labels = labels;
+  a.ignore_index = ignore_index;
+  a.beta = beta;
+  a.gamma = gamma;
+  a.ref = ref_sums;
+  a.out = out;
+  a.g = g;
+  double* base = (double*)((char*)ws + kHeader);
+  const size_t P = size_t(n_pairs);
+  a.val = base;
+  a.dv = base + 2 * P;
+  a.cnt = (long long*)(base + 4 * P);
+  a.pair = base + 6 * P;
+  a.status = (uint32_t*)ws;
+  TraceScope ts(ORPO_K_LOSS, 0.0, stream);
+  hipLaunchKernelGGL(pref_loss_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return launched();
+}
+
+orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets,
+                           const float* logp, const float* old_logp, const float* ref_logp,
+                           const float* advantages, const int32_t* labels, int64_t V,
+                           int32_t ignore_index, double clip_eps, double beta, double* out,
+                           float* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (M < 0 || M > INT32_MAX || n_seqs < 1 || V <= 0 || V > INT32_MAX) return ORPO_EINVAL;
+  if (!seg_offsets || !out || !advantages) return ORPO_EINVAL;
+  if (M > 0 && (!logp || !old_logp || !ref_logp || !labels || !g)) return ORPO_EINVAL;
+  if (!(clip_eps >= 0.0) || !(beta == beta)) return ORPO_EINVAL;
+  if (!ws || ws_bytes < orpo_objective_workspace_bytes(M, n_seqs) || (uintptr_t)ws % 256)
+    return ORPO_ENOWS;
+  GrpoArgs a;
+  a.M = M;
+  a.V = V;
+  a.S = n_seqs;
+  a.off = seg_offsets;
+  a.logp = logp;
+  a.old_logp = old_logp;
+  a.ref_logp = ref_logp;
+  a.adv = advantages;
+  a.labels = labels;
+  a.ignore_index = ignore_index;
+  a.eps = clip_eps;
+  a.beta = beta;
+  a.out = out;
+  a.g = g;
+  double* base = (double*)((char*)ws + kHeader);
+  const size_t S = size_t(n_seqs);
+  a.pg = base;
+  a.kl = base + S;
+  a.cnt = (long long*)(base + 2 * S);
+  a.clipped = (long long*)(base + 3 * S);
+  a.status = (uint32_t*)ws;
+  TraceScope ts(ORPO_K_LOSS, 0.0, stream);
+  hipLaunchKernelGGL(grpo_loss_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return launched();
 }
 
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,

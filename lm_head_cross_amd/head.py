@@ -46,6 +46,13 @@ _SIGS = {
     "orpo_loss_full": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
                                       ctypes.c_int32, ctypes.c_double, _P, _P, _P, ctypes.c_size_t,
                                       _P]),
+    "orpo_objective_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
+    "orpo_pref_loss": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_double,
+                                      ctypes.c_double, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "orpo_grpo_loss": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_double,
+                                      ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P]),
     "orpo_head_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
     "orpo_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
@@ -213,25 +220,74 @@ def trace_collect() -> dict:
 # ------------------------------------------------------------------------------------------------
 # A preallocated head step: fwd -> loss -> bwd with every buffer and workspace allocated once.
 # ------------------------------------------------------------------------------------------------
+PREF_KINDS = {"simpo": 1, "dpo": 2}
+
+
+def pref_loss(kind, logp, labels, seg_offsets, V, beta, gamma=0.0, ref_sums=None,
+              ignore_index=IGNORE_INDEX, return_ws=False):
+    """SimPO ("simpo": mean log-probs, margin gamma) or DPO ("dpo": sequence sums against the cached
+    reference sums ref_sums [2P] float64) over chosen/rejected spans seg_offsets [2P+1].
+    Returns out (float64 [3 + 2P]: loss, accuracy, margin, chosen values, rejected values), g."""
+    _need_gpu(logp, labels, seg_offsets, ref_sums)
+    M = logp.shape[0]
+    P = (seg_offsets.shape[0] - 1) // 2
+    L = lib()
+    ws = _workspace(L.orpo_objective_workspace_bytes(M, 2 * P), logp.device)
+    out = torch.empty(3 + 2 * P, dtype=torch.float64, device=logp.device)
+    g = torch.empty(M, dtype=torch.float32, device=logp.device)
+    _check(L.orpo_pref_loss(PREF_KINDS[kind], M, P, _ptr(seg_offsets), _ptr(logp), _ptr(labels), V,
+                            ignore_index, float(beta), float(gamma), _ptr(ref_sums), _ptr(out),
+                            _ptr(g), _ptr(ws), ws.numel(), _stream(logp.device)), "orpo_pref_loss")
+    return (out, g, ws) if return_ws else (out, g)
+
+
+def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip_eps, beta,
+              ignore_index=IGNORE_INDEX, return_ws=False):
+    """GRPO's clipped policy gradient + beta * k3 KL over completions seg_offsets [S+1] with one
+    advantage each. Returns out (float64 [4]: loss, pg, kl, clip fraction), g."""
+    _need_gpu(logp, old_logp, ref_logp, advantages, labels, seg_offsets)
+    M = logp.shape[0]
+    S = seg_offsets.shape[0] - 1
+    L = lib()
+    ws = _workspace(L.orpo_objective_workspace_bytes(M, S), logp.device)
+    out = torch.empty(4, dtype=torch.float64, device=logp.device)
+    g = torch.empty(M, dtype=torch.float32, device=logp.device)
+    _check(L.orpo_grpo_loss(M, S, _ptr(seg_offsets), _ptr(logp), _ptr(old_logp), _ptr(ref_logp),
+                            _ptr(advantages), _ptr(labels), V, ignore_index, float(clip_eps),
+                            float(beta), _ptr(out), _ptr(g), _ptr(ws), ws.numel(),
+                            _stream(logp.device)), "orpo_grpo_loss")
+    return (out, g, ws) if return_ws else (out, g)
+
+
 class HeadStep:
     def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
-                 want_dW=True, ignore_index=IGNORE_INDEX, scope="response"):
+                 want_dW=True, ignore_index=IGNORE_INDEX, scope="response", objective="orpo",
+                 obj=None):
+        """One head step: forward -> loss -> backward on preallocated buffers.
+
+        objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
+        backward, with its parameters and inputs in `obj`: "simpo" {beta, gamma}, "dpo" {beta,
+        ref_sums [2P] float64}, "grpo" {clip_eps, beta, old_logp [M], ref_logp [M], advantages [S]
+        float32, seg_offsets are then [S+1] completions}."""
         _need_gpu(h, w, labels, seg_offsets, scales, biases)
         self.h, self.w, self.labels, self.off = h, w, labels, seg_offsets
         self.scales, self.biases = scales, biases
         self.M, self.d = h.shape
         self.V, self.softcap, self.lam, self.ignore = V, float(softcap), float(lam), ignore_index
-        self.S = SCOPES[scope]
+        self.objective, self.obj = objective, dict(obj or {})
+        self.S = SCOPES[scope] if objective == "orpo" else (1 if objective == "grpo" else 2)
         self.P = (seg_offsets.shape[0] - 1) // self.S
         dev = h.device
         self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
         L = lib()
         self.fws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(self.desc)), dev)
         self.bws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(self.desc)), dev)
-        self.lws = _workspace(L.orpo_loss_workspace_bytes(self.M, self.P), dev)
+        self.lws = _workspace(L.orpo_loss_workspace_bytes(self.M, self.P) if objective == "orpo"
+                              else L.orpo_objective_workspace_bytes(self.M, self.S * self.P), dev)
         self.logp = torch.empty(self.M, dtype=torch.float32, device=dev)
         self.lse = torch.empty(self.M, dtype=torch.float32, device=dev)
-        self.out = torch.empty(5 + (3 if self.S == 3 else 2) * self.P, dtype=torch.float64, device=dev)
+        n_out = {"orpo": 5 + (3 if self.S == 3 else 2) * self.P, "grpo": 4}.get(objective, 3 + 2 * self.P)
+        self.out = torch.empty(n_out, dtype=torch.float64, device=dev)
         self.g = torch.empty(self.M, dtype=torch.float32, device=dev)
         self.dh = torch.empty(self.M, self.d, dtype=torch.float32, device=dev)
         self.dW = torch.empty(V, self.d, dtype=torch.float32, device=dev) if want_dW else None
@@ -248,6 +304,22 @@ class HeadStep:
                                    self._s()), "orpo_head_fwd")
 
     def loss(self):
+        o = self.obj
+        if self.objective in PREF_KINDS:
+            _check(lib().orpo_pref_loss(PREF_KINDS[self.objective], self.M, self.P, _ptr(self.off),
+                                        _ptr(self.logp), _ptr(self.labels), self.V, self.ignore,
+                                        float(o["beta"]), float(o.get("gamma", 0.0)),
+                                        _ptr(o.get("ref_sums")), _ptr(self.out), _ptr(self.g),
+                                        _ptr(self.lws), self.lws.numel(), self._s()), "orpo_pref_loss")
+            return
+        if self.objective == "grpo":
+            _check(lib().orpo_grpo_loss(self.M, self.P, _ptr(self.off), _ptr(self.logp),
+                                        _ptr(o["old_logp"]), _ptr(o["ref_logp"]),
+                                        _ptr(o["advantages"]), _ptr(self.labels), self.V,
+                                        self.ignore, float(o["clip_eps"]), float(o["beta"]),
+                                        _ptr(self.out), _ptr(self.g), _ptr(self.lws),
+                                        self.lws.numel(), self._s()), "orpo_grpo_loss")
+            return
         fn = lib().orpo_loss_full if self.S == 3 else lib().orpo_loss
         _check(fn(self.M, self.P, _ptr(self.off), _ptr(self.logp), _ptr(self.labels), self.V,
                   self.ignore, self.lam, _ptr(self.out), _ptr(self.g), _ptr(self.lws),

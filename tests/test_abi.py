@@ -106,3 +106,22 @@ def test_status_strings():
     L = H.lib()
     assert L.orpo_status_string(0) == b"ok"
     assert b"workspace" in L.orpo_status_string(ENOWS)
+
+
+def test_objective_entry_points_reject_bad_arguments():
+    L = H.lib()
+    assert L.orpo_objective_workspace_bytes(100, 8) == 256 + 512
+    assert L.orpo_objective_workspace_bytes(100, 0) == 0
+    ws = 1 << 20
+    # kind, M, P, off, logp, labels, V, ignore, beta, gamma, ref, out, g, ws, bytes, stream
+    assert L.orpo_pref_loss(3, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, 16, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_pref_loss(2, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, None, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_pref_loss(1, 10, 0, 16, 16, 16, 100, -100, 0.1, 0.0, None, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_pref_loss(1, 10, 1, 16, 16, 16, 100, -100, float("nan"), 0.0, None, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_pref_loss(1, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, None, 16, 16, ws, 16, None) == ENOWS
+    # M, S, off, logp, old, ref, adv, labels, V, ignore, eps, beta, out, g, ws, bytes, stream
+    assert L.orpo_grpo_loss(10, 0, 16, 16, 16, 16, 16, 16, 100, -100, 0.2, 0.1, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_grpo_loss(10, 1, 16, 16, 16, 16, None, 16, 100, -100, 0.2, 0.1, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_grpo_loss(10, 1, 16, 16, None, 16, 16, 16, 100, -100, 0.2, 0.1, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_grpo_loss(10, 1, 16, 16, 16, 16, 16, 16, 100, -100, -1.0, 0.1, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_grpo_loss(10, 1, 16, 16, 16, 16, 16, 16, 100, -100, 0.2, 0.1, 16, 16, ws, 16, None) == ENOWS
