@@ -367,6 +367,54 @@ def backward(h, W, labels, lse, g, cap: float = 0.0, ignore_index: int = IGNORE_
     return dh, dW
 
 
+def backward_filtered(h, W, labels, lse, g, cap: float, eps: float,
+                      ignore_index: int = IGNORE_INDEX, tok_block: int = 256, k_slice: int = 64):
+    """The backward with the coefficient filter: dh and dW from coefficients whose negligible
+    blocks are dropped.
+
+    Steel flash-CCE — handoff, Glossary E "Backward approximations": the coefficient filter skips
+    the gradient GEMM's chunks whose whole coefficient block is below eps (ORPO training — design,
+    the flash-CCE status notes, give its default 1e-5 and its measured effect on real data). The
+    chunks here are the K slices of the two gradient GEMMs: for dh (K = vocabulary) a block is
+    tok_block tokens x k_slice vocabulary entries, for dW (K = tokens) tok_block vocabulary entries
+    x k_slice tokens, aligned to multiples of their sizes from index 0. A block is dropped when
+    max |coeff| over it is < eps. eps = 0 is the exact backward. Returns (dh, dW, kept_dh, kept_dw)
+    with the kept fractions of the blocks.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels = np.asarray(labels).astype(np.int64)
+    lse = np.asarray(lse, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    M, V = h.shape[0], W.shape[0]
+    valid = _check_labels(labels, V, ignore_index)
+    raw = h @ W.T
+    p = np.exp(softcap(raw, cap) - lse[:, None])
+    onehot = np.zeros_like(raw)
+    for t in range(M):
+        if valid[t]:
+            onehot[t, labels[t]] = 1.0
+    coeff = g[:, None] * (onehot - p) * softcap_slope(raw, cap)
+    a = np.abs(coeff)
+
+    def block_mask(rows_per, cols_per):
+        keep = np.zeros_like(a, dtype=bool)
+        n_keep = n_all = 0
+        for r0 in range(0, M, rows_per):
+            for c0 in range(0, V, cols_per):
+                k = a[r0:r0 + rows_per, c0:c0 + cols_per].max() >= eps
+                keep[r0:r0 + rows_per, c0:c0 + cols_per] = k
+                n_keep += int(k)
+                n_all += 1
+        return keep, n_keep / max(n_all, 1)
+
+    keep_dh, f_dh = block_mask(tok_block, k_slice)       # (tokens, vocabulary) blocks
+    keep_dw, f_dw = block_mask(k_slice, tok_block)       # (tokens, vocabulary) = (64, 256) blocks
+    dh = np.where(keep_dh, coeff, 0.0) @ W
+    dW = np.where(keep_dw, coeff, 0.0).T @ h
+    return dh, dW, f_dh, f_dw
+
+
 # --------------------------------------------------------------------------------------------
 # The whole head step
 # --------------------------------------------------------------------------------------------

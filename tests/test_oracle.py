@@ -464,3 +464,77 @@ def test_full_scope_span_errors():
     labels[2:4] = -100
     with pytest.raises(orc.OracleError):
         orc.span_means_full(logp, labels, [0, 2, 4, 6])       # chosen response has no valid token
+
+
+# ----------------------------------------------------------------------------- backward skips
+# Steel flash-CCE — handoff, Glossary E: the coefficient filter drops gradient-GEMM chunks whose
+# whole coefficient block is below eps.
+def _filter_problem(seed, M=300, d=6, V=200, cap=2.0):
+    rng = _rng(500 + seed)
+    h = rng.standard_normal((M, d))
+    W = rng.standard_normal((V, d)) * 2.0
+    labels = rng.integers(0, V, size=M)
+    labels[5] = -100
+    logp, lse = orc.forward(h, W, labels, cap)
+    g = rng.standard_normal(M) * 1e-2
+    g[labels == -100] = 0.0
+    return h, W, labels, lse, g, cap
+
+
+def test_filter_eps_zero_is_the_exact_backward():
+    h, W, labels, lse, g, cap = _filter_problem(1)
+    dh, dW = orc.backward(h, W, labels, lse, g, cap)
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, 0.0)
+    assert kh == 1.0 and kw == 1.0
+    assert np.allclose(fh, dh, rtol=1e-12, atol=1e-15) and np.allclose(fw, dW, rtol=1e-12, atol=1e-15)
+
+
+def test_filter_huge_eps_drops_everything():
+    h, W, labels, lse, g, cap = _filter_problem(2)
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, 1e9)
+    assert kh == 0.0 and kw == 0.0 and np.all(fh == 0) and np.all(fw == 0)
+
+
+def test_filter_drops_exactly_the_quiet_blocks():
+    # Tokens 256.. (the second 256-token block, ragged: 44 tokens) get a negligible cotangent: every
+    # dh block of theirs is dropped, every other dh row is exact; dW loses exactly their terms.
+    h, W, labels, lse, g, cap = _filter_problem(3)
+    g[256:] *= 1e-9
+    eps = 1e-8
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, eps)
+    dh, _ = orc.backward(h, W, labels, lse, g, cap)
+    g0 = g.copy()
+    g0[256:] = 0.0
+    _, dW0 = orc.backward(h, W, labels, lse, g0, cap)
+    assert np.all(fh[256:] == 0) and np.allclose(fh[:256], dh[:256], rtol=1e-12, atol=1e-15)
+    assert np.allclose(fw, dW0, rtol=1e-9, atol=1e-15)
+    assert kh == pytest.approx(0.5) and 0 < kw < 1     # 2 of 4 token-block rows x 4 vocab slices
+
+
+def test_filter_kept_fraction_is_monotone_in_eps():
+    h, W, labels, lse, g, cap = _filter_problem(4)
+    prev = (1.0, 1.0)
+    for eps in (1e-9, 1e-7, 1e-5, 1e-4, 1e-3):
+        _, _, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, eps)
+        assert kh <= prev[0] and kw <= prev[1]
+        prev = (kh, kw)
+
+
+def test_filter_block_geometry_differs_for_dh_and_dw():
+    # Vocabulary entries 64..127 get very negative logits and no label: their coefficients are
+    # negligible for every token. dh's blocks (256 tokens x 64 entries) over that slice are all
+    # quiet and dropped; dW's blocks (64 tokens x 256 entries) also hold entries 0..63 and are kept.
+    h, W, labels, lse, g, cap = _filter_problem(5, cap=0.0)
+    W[64:128] = 0.0
+    W[64:128, 0] = -1e3 / np.abs(h[:, 0]).min()        # raw <= -1000 for every token
+    h[:, 0] = np.abs(h[:, 0])
+    labels[(labels >= 64) & (labels < 128)] = 3
+    logp, lse = orc.forward(h, W, labels, cap)
+    eps = 1e-12
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, eps)
+    dh, dW = orc.backward(h, W, labels, lse, g, cap)
+    assert kw == 1.0 and kh == pytest.approx(3 / 4)
+    assert np.allclose(fw, dW, rtol=1e-12, atol=1e-15)
+    assert np.allclose(fh, dh, rtol=1e-9, atol=1e-12)  # what is dropped is negligible here too
+    fh2, _, kh2, _ = orc.backward_filtered(h, W, labels, lse, g, cap, eps, k_slice=128)
+    assert kh2 == 1.0                                  # a 128-wide slice is no longer quiet
