@@ -538,3 +538,37 @@ def test_filter_block_geometry_differs_for_dh_and_dw():
     assert np.allclose(fh, dh, rtol=1e-9, atol=1e-12)  # what is dropped is negligible here too
     fh2, _, kh2, _ = orc.backward_filtered(h, W, labels, lse, g, cap, eps, k_slice=128)
     assert kh2 == 1.0                                  # a 128-wide slice is no longer quiet
+
+
+def test_filter_material_drops_follow_each_gemms_blocks():
+    # Cotangent 1 on tokens 0..63, 1e-6 elsewhere; eps = 1e-3 sits between the two scales.
+    # dW's blocks are 64 tokens x 256 entries: only tokens 0..63 survive, so dW is exactly their
+    # contribution. dh's blocks are 256 tokens x 64 entries: the first token block keeps every
+    # slice that token 0..63 make loud (with the quiet tokens' small terms), the ragged second
+    # block (tokens 256..299) is dropped whole.
+    h, W, labels, lse, g, cap = _filter_problem(6)
+    g[:] = 1e-6
+    g[:64] = 1.0
+    g[labels == -100] = 0.0
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, 1e-3)
+    g_loud = np.where(np.arange(len(g)) < 64, g, 0.0)
+    _, dW_loud = orc.backward(h, W, labels, lse, g_loud, cap)
+    assert np.allclose(fw, dW_loud, rtol=1e-12, atol=1e-15)
+    dh, _ = orc.backward(h, W, labels, lse, g, cap)
+    assert np.all(fh[256:] == 0.0)
+    # Rows 64..255 keep their (tiny) terms in the slices that stay: exact there, nonzero.
+    assert np.allclose(fh[:64], dh[:64], rtol=1e-6, atol=1e-12)
+    assert np.any(fh[64:256] != 0.0)
+
+
+def test_filter_decides_on_the_block_maximum():
+    # One loud token (cotangent 1) in a block of quiet ones: its label entry's coefficient (about
+    # 1 - p) keeps that (256-token, 64-entry) block although the block's mean is far below eps.
+    h, W, labels, lse, g, cap = _filter_problem(7)
+    g[:] = 0.0
+    g[0] = 1.0
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, lse, g, cap, 1e-3)
+    dh, dW = orc.backward(h, W, labels, lse, g, cap)
+    assert np.linalg.norm(fh[0] - dh[0]) <= 0.05 * np.linalg.norm(dh[0])
+    assert np.linalg.norm(fw - dW) <= 0.05 * np.linalg.norm(dW)
+    assert 0 < kh < 1
