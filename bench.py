@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
     ap.add_argument("--objective", default="orpo", choices=["orpo", "simpo", "dpo", "grpo"],
                     help="the loss between the head's forward and backward")
+    ap.add_argument("--skip-eps", type=float, default=0.0,
+                    help="backward coefficient filter threshold (0 = exact backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -159,7 +161,8 @@ def main():
             obj["ref_logp"] = pre.logp + obj.pop("ref_noise")
             del pre
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                      want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj)
+                      want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj,
+                      skip_eps=args.skip_eps)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -238,7 +241,7 @@ def main():
         "config": {
             "workload": cfg.name, "M": cfg.M, "valid_tokens": n_valid, "d": cfg.d, "V": cfg.V,
             "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam, "nll_scope": cfg.scope,
-            "objective": args.objective,
+            "objective": args.objective, "skip_eps": args.skip_eps,
             "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
             "parallelism": "single GPU",
         },

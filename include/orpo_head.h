@@ -69,6 +69,12 @@ typedef struct {
   float softcap;        /* > 0: z = softcap * tanh(raw / softcap); <= 0: z = raw                */
   int32_t ignore_index; /* label value of ignored / padding tokens (conventionally -100)        */
   uint32_t flags;       /* ORPO_DW_ACCUMULATE                                                   */
+  float skip_eps;       /* backward coefficient filter: 0 = exact backward; > 0 (bf16 and 4-bit
+                         * heads only) drops from dh every 256-token x 64-entry coefficient block,
+                         * and from dW every 256-entry x 64-token block, whose max |coeff| < skip_eps
+                         * (their GEMM K steps are skipped). An approximation, opt-in; the pages'
+                         * default is 1e-5 ("Steel flash-CCE — handoff", Glossary E "Backward
+                         * approximations"). Ignored by orpo_head_fwd.                          */
 } orpo_head_desc;
 
 /* The head weights: `w` is W[V,d] row-major in w_fmt (for ORPO_Q4G64 the packed uint32 words

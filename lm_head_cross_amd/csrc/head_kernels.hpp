@@ -27,6 +27,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kStatusBadLabel = 1u, kStatusEmptyBranch = 2u, kStatusBadOffsets = 4u;
+constexpr int kMaxKSteps = 8192;   // K steps a dh / dW tile can list under the coefficient filter
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float rcp_(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -390,6 +391,8 @@ struct BwdItem {
   int64_t c0, C_cur;      // token chunk [c0, c0 + C_cur)
   int64_t v0, BV_cur;     // vocabulary block [v0, v0 + BV_cur)
   void* coeff;            // [C, BVb] of E::T, token-major
+  uint8_t* fdh;           // coefficient filter flags for dh: [C/256][BVb/64][4] (null: filter off)
+  uint8_t* fdw;           // ... and for dW: [BVb/256][C/64][2]
   int32_t n_tiles;        // tiles of this item in the launch (coefficient: n_vt * n_tt; GEMM: dh + dW)
   int32_t n_vt, n_tt;     // 256-tiles along vocabulary and tokens
   int32_t n_dh;           // dh tiles (GEMM item); dW tiles are n_tiles - n_dh
@@ -410,13 +413,15 @@ struct BwdArgs {
   float cap;
   int32_t ignore_index;
   int32_t n_jt;           // 256-tiles along d
+  float skip_eps;         // coefficient filter threshold (0: exact backward)
+  int32_t nsl_v, nsl_t;   // 64-wide vocabulary / token slices per coefficient buffer row / column
   BwdItem gm;             // dh / dW tiles (n_tiles = 0: none)
   BwdItem cf;             // coefficient tiles (n_tiles = 0: none)
 };
 
 // Phase 1: recompute a 256 x 256 logit tile (m = vocabulary, n = token) and write its coefficients
 // coeff = g (onehot - softmax) sech^2 (bf16 or fp32) to the item's coefficient buffer.
-template <class E, bool Q4, bool SOFTCAP>
+template <class E, bool Q4, bool SOFTCAP, bool SKIP>
 __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it,
                                            int bid) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
@@ -451,6 +456,7 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
   typedef typename E::T T;
   T* out = (T*)it.coeff;
+  float cmax[2] = {0.f, 0.f};   // max |coeff| of this lane in vocabulary slices 2 wm and 2 wm + 1
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = acc_n(wn, nb, l);
@@ -485,6 +491,7 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
           float c = gt * ((yo == mm ? 1.f : 0.f) - p) * slope;
           if (vbase + mm >= a.V || gt == 0.f) c = 0.f;
           vals[ri] = c;
+          if constexpr (SKIP) cmax[mb >> 1] = fmaxf(cmax[mb >> 1], fabsf(c));
         }
         // 4 consecutive vocabulary entries of token tk.
         const int m0 = acc_m(wm, mb, rg * 4, l);
@@ -498,6 +505,43 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
         }
       }
   }
+  // Coefficient filter: this wave covers 64 tokens (slice wn of the tile) x 128 vocabulary entries
+  // (slices 2 wm, 2 wm + 1); one flag byte per (token block, vocabulary slice, wave) for dh and per
+  // (vocabulary block, token slice, wave) for dW, so every byte has exactly one writer.
+  if constexpr (SKIP) {
+    const bool f0 = __ballot(cmax[0] >= a.skip_eps) != 0, f1 = __ballot(cmax[1] >= a.skip_eps) != 0;
+    if (l == 0) {
+      uint8_t* fh = it.fdh + ((int64_t)tt * a.nsl_v + 4 * vt + 2 * wm) * 4 + wn;
+      fh[0] = f0;
+      fh[4] = f1;
+      it.fdw[((int64_t)vt * a.nsl_t + 4 * tt + wn) * 2 + wm] = f0 || f1;
+    }
+  }
+}
+
+// With the coefficient filter on: the K steps (64-wide slices) whose flag bytes are not all zero,
+// compacted in order into `list`; returns their count. Step s's flags are flags[s * parts + q].
+__device__ __forceinline__ int build_klist(const uint8_t* flags, int nk, int parts, uint16_t* list,
+                                           int* wave_tot) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  int total = 0;
+  for (int base = 0; base < nk; base += kThreads) {
+    const int s = base + tid;
+    bool f = false;
+    if (s < nk)
+      for (int q = 0; q < parts; ++q) f |= flags[(int64_t)s * parts + q] != 0;
+    const uint64_t m = __ballot(f);
+    if (l == 0) wave_tot[w] = __popcll(m);
+    __syncthreads();
+    int off = total;
+    for (int i = 0; i < w; ++i) off += wave_tot[i];
+    int add = 0;
+    for (int i = 0; i < kThreads / 64; ++i) add += wave_tot[i];
+    if (f) list[off + __popcll(m & ((1ull << l) - 1ull))] = (uint16_t)s;
+    total += add;
+    __syncthreads();
+  }
+  return total;
 }
 
 template <class E>
@@ -523,8 +567,9 @@ __device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, 
 }
 
 // Phase 2a: dh[c0 + i][j] (+)= sum_v coeff[i][v] W[v0 + v][j]   (m = token, n = hidden, k = vocabulary)
-template <class E, bool Q4>
-__device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid) {
+template <class E, bool Q4, bool SKIP>
+__device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid,
+                                        uint16_t* klist, int* wave_tot) {
   const int tid = threadIdx.x;
   const int64_t row_bytes = a.d * E::kSize;
   const int64_t cpitch = a.BVb * E::kSize;
@@ -540,8 +585,12 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   typedef typename std::conditional<Q4, Q4N, DmaMN<E>>::type LoaderB;
   LoaderB lb;                                                       // W [v][j], N-major
   if constexpr (Q4) lb.init(a.q4, v_end); else lb.init(a.w, row_bytes, v_end);
+  // Coefficient filter: run only the vocabulary slices some coefficient of this token tile needs.
+  constexpr bool filt = SKIP;
+  const int n_run = filt ? build_klist(it.fdh + (int64_t)ti * a.nsl_v * 4, nk, 4, klist, wave_tot) : nk;
   auto issue = [&](int, int ks, char* sa, char* sb) {
-    const int64_t k0 = (int64_t)ks * E::kBK;
+    const int step = filt ? __builtin_amdgcn_readfirstlane(klist[ks]) : ks;
+    const int64_t k0 = (int64_t)step * E::kBK;
     la.issue(i0, k0 * E::kSize, sa);
     if constexpr (Q4) lb.issue(it.v0 + k0, j0, sb);
     else lb.issue(it.v0 + k0, j0 * E::kSize, sb);
@@ -553,14 +602,16 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, true, false, false>(smem, 1, nk, issue, commit, nop, acc);
+  gemm_run<E, true, false, false>(smem, 1, n_run, issue, commit, nop, acc);
   (void)tid;
-  store_out<E>(a.dh, a.d, it.c0 + i0, t_end, j0, a.d, it.dh_first != 0, acc);
+  if (n_run > 0 || it.dh_first)
+    store_out<E>(a.dh, a.d, it.c0 + i0, t_end, j0, a.d, it.dh_first != 0, acc);
 }
 
 // Phase 2b: dW[v0 + v][j] (+)= sum_i coeff[i][v] h[c0 + i][j]   (m = vocabulary, n = hidden, k = token)
-template <class E>
-__device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid) {
+template <class E, bool SKIP>
+__device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid,
+                                        uint16_t* klist, int* wave_tot) {
   const int64_t row_bytes = a.d * E::kSize;
   const int64_t cpitch = a.BVb * E::kSize;
   const int64_t t_end = min(a.M, it.c0 + it.C_cur);
@@ -572,8 +623,12 @@ __device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, cons
   la.init(it.coeff, cpitch, it.C_cur);
   DmaMN<E> lb;                                                      // h [t][j], N-major
   lb.init(a.h, row_bytes, t_end);
+  // Coefficient filter: run only the token slices some coefficient of this vocabulary tile needs.
+  constexpr bool filt = SKIP;
+  const int n_run = filt ? build_klist(it.fdw + (int64_t)vt * a.nsl_t * 2, nk, 2, klist, wave_tot) : nk;
   auto issue = [&](int, int ks, char* sa, char* sb) {
-    const int64_t k0 = (int64_t)ks * E::kBK;
+    const int step = filt ? __builtin_amdgcn_readfirstlane(klist[ks]) : ks;
+    const int64_t k0 = (int64_t)step * E::kBK;
     la.issue(k0, vl0 * E::kSize, sa);
     lb.issue(it.c0 + k0, j0 * E::kSize, sb);
   };
@@ -584,26 +639,31 @@ __device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, cons
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, false, false, false>(smem, 1, nk, issue, commit, nop, acc);
-  store_out<E>(a.dW, a.d, it.v0 + vl0, min(a.V, it.v0 + it.BV_cur), j0, a.d, it.dw_first != 0, acc);
+  gemm_run<E, false, false, false>(smem, 1, n_run, issue, commit, nop, acc);
+  if (n_run > 0 || it.dw_first)
+    store_out<E>(a.dW, a.d, it.v0 + vl0, min(a.V, it.v0 + it.BV_cur), j0, a.d, it.dw_first != 0, acc);
 }
 
 // One launch of the backward pipeline: [dh tiles of gm | dW tiles of gm | coefficient tiles of cf].
-template <class E, bool Q4, bool SOFTCAP>
+// SKIP: the variant with the coefficient filter (orpo_head_desc.skip_eps > 0); the exact backward
+// compiles without any of its code.
+template <class E, bool Q4, bool SOFTCAP, bool SKIP>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
   ORPO_DECLARE_SMEM(smem);
+  __shared__ uint16_t klist[SKIP ? kMaxKSteps : 1];   // K steps to run under the coefficient filter
+  __shared__ int wave_tot[kThreads / 64];
   int b = blockIdx.x;
   if (b < a.gm.n_dh) {
-    dh_tile<E, Q4>(smem, a, a.gm, b);
+    dh_tile<E, Q4, SKIP>(smem, a, a.gm, b, klist, wave_tot);
     return;
   }
   b -= a.gm.n_dh;
   if (b < a.gm.n_tiles - a.gm.n_dh) {
-    if constexpr (!Q4) dw_tile<E>(smem, a, a.gm, b);
+    if constexpr (!Q4) dw_tile<E, SKIP>(smem, a, a.gm, b, klist, wave_tot);
     return;
   }
   b -= a.gm.n_tiles - a.gm.n_dh;
-  coeff_tile<E, Q4, SOFTCAP>(smem, a, a.cf, b);
+  coeff_tile<E, Q4, SOFTCAP, SKIP>(smem, a, a.cf, b);
 }
 
 }  // namespace orpo

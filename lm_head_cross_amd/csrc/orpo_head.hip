@@ -91,6 +91,8 @@ orpo_status check_desc(const orpo_head_desc* d, Kind* kind) {
   else
     return ORPO_EINVAL;
   if (d->d % 64 != 0) return ORPO_EUNSUPPORTED;
+  if (!(d->skip_eps >= 0.f) || d->skip_eps == __builtin_huge_valf()) return ORPO_EINVAL;
+  if (d->skip_eps > 0.f && k == kF32) return ORPO_EUNSUPPORTED;   // 32-wide K steps, 64-wide blocks
   *kind = k;
   return ORPO_OK;
 }
@@ -119,6 +121,7 @@ FwdPlan plan_fwd(const orpo_head_desc* d) {
 
 struct BwdPlan {
   int64_t C, BVb;
+  size_t fl_bytes;   // skip flags per coefficient buffer (0 without the coefficient filter)
   size_t ws;
 };
 
@@ -128,7 +131,13 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
   p.C = std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), kTile) * kTile, g_chunk);
   const int64_t by_budget = std::max<int64_t>(kTile, int64_t(g_coeff_budget) / (p.C * esize) / kTile * kTile);
   p.BVb = std::min<int64_t>(cdiv(d->V, kTile) * kTile, by_budget);
-  p.ws = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize);
+  // With the coefficient filter: per buffer, dh flags [C/256][BVb/64][4 waves] and dW flags
+  // [BVb/256][C/64][2 waves], one byte each.
+  p.fl_bytes = d->skip_eps > 0.f
+                   ? round_up(size_t(p.C / kTile) * size_t(p.BVb / 64) * 4 +
+                                  size_t(p.BVb / kTile) * size_t(p.C / 64) * 2, 256)
+                   : 0;
+  p.ws = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize) + 2 * p.fl_bytes;
   return p;
 }
 
@@ -146,7 +155,13 @@ orpo_status launch_bwd(const BwdArgs& a, int grid, hipStream_t st) {
                     double(a.d) * (a.gm.n_tiles > 0);
   const int kind = a.gm.n_tiles == 0 ? ORPO_K_COEFF : (a.cf.n_tiles == 0 ? ORPO_K_DHDW : ORPO_K_BWD);
   TraceScope ts(kind, cf + gm, st);
-  hipLaunchKernelGGL((bwd_kernel<E, Q4, SC>), dim3(grid), dim3(kThreads), 0, st, a);
+  if constexpr (E::kSize == 2) {   // the coefficient filter exists for bf16 coefficients only
+    if (a.skip_eps > 0.f) {
+      hipLaunchKernelGGL((bwd_kernel<E, Q4, SC, true>), dim3(grid), dim3(kThreads), 0, st, a);
+      return launched();
+    }
+  }
+  hipLaunchKernelGGL((bwd_kernel<E, Q4, SC, false>), dim3(grid), dim3(kThreads), 0, st, a);
   return launched();
 }
 
@@ -384,10 +399,17 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.cap = desc->softcap;
   a.ignore_index = desc->ignore_index;
   a.n_jt = (int)cdiv(desc->d, kTile);
+  a.skip_eps = desc->skip_eps;
+  a.nsl_v = (int32_t)(p.BVb / 64);
+  a.nsl_t = (int32_t)(p.C / 64);
+  if (a.skip_eps > 0.f && (a.nsl_v > kMaxKSteps || a.nsl_t > kMaxKSteps)) return ORPO_EUNSUPPORTED;
   const bool sc = desc->softcap > 0.f;
   const bool acc_dw = (desc->flags & ORPO_DW_ACCUMULATE) != 0;
   const size_t esize = k == kF32 ? 4 : 2;
-  char* buf[2] = {(char*)ws + kHeader, (char*)ws + kHeader + size_t(p.C) * size_t(p.BVb) * esize};
+  const size_t cbytes = size_t(p.C) * size_t(p.BVb) * esize;
+  char* buf[2] = {(char*)ws + kHeader, (char*)ws + kHeader + cbytes};
+  uint8_t* flg[2] = {(uint8_t*)ws + kHeader + 2 * cbytes, (uint8_t*)ws + kHeader + 2 * cbytes + p.fl_bytes};
+  const size_t fdh_bytes = size_t(p.C / kTile) * size_t(p.BVb / 64) * 4;
   const int64_t n_blocks = cdiv(desc->V, p.BVb);
   const int64_t n_items = cdiv(desc->M, p.C) * n_blocks;
   // Item i = (chunk i / n_blocks, block i % n_blocks); launch i = coefficients of item i + dh/dW of item i-1.
@@ -400,6 +422,8 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
     it.v0 = blk * p.BVb;
     it.BV_cur = std::min(p.BVb, desc->V - it.v0);
     it.coeff = buf[i % 2];
+    it.fdh = p.fl_bytes ? flg[i % 2] : nullptr;
+    it.fdw = p.fl_bytes ? flg[i % 2] + fdh_bytes : nullptr;
     it.n_vt = (int)cdiv(it.BV_cur, kTile);
     it.n_tt = (int)cdiv(it.C_cur, kTile);
     it.dh_first = blk == 0;

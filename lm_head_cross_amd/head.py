@@ -28,7 +28,8 @@ class OrpoError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("d", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("h_fmt", ctypes.c_int32), ("w_fmt", ctypes.c_int32), ("softcap", ctypes.c_float),
-                ("ignore_index", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("ignore_index", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("skip_eps", ctypes.c_float)]
 
 
 class Weight(ctypes.Structure):
@@ -103,9 +104,10 @@ def _need_gpu(*ts):
             raise OrpoError("tensors must be contiguous and on a GPU")
 
 
-def make_desc(M, d, V, h_dtype, w_fmt, softcap, ignore_index=IGNORE_INDEX, flags=0) -> Desc:
+def make_desc(M, d, V, h_dtype, w_fmt, softcap, ignore_index=IGNORE_INDEX, flags=0,
+              skip_eps=0.0) -> Desc:
     h_fmt = ORPO_F32 if h_dtype == torch.float32 else ORPO_BF16
-    return Desc(M, d, V, h_fmt, w_fmt, float(softcap), ignore_index, flags)
+    return Desc(M, d, V, h_fmt, w_fmt, float(softcap), ignore_index, flags, float(skip_eps))
 
 
 def _w_fmt(w, scales):
@@ -174,13 +176,14 @@ def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, retu
 
 
 def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNORE_INDEX,
-             scales=None, biases=None, dW=None, accumulate=False):
-    """dh[M,d] and dW[V,d] (float32; dW None when want_dW is False)."""
+             scales=None, biases=None, dW=None, accumulate=False, skip_eps=0.0):
+    """dh[M,d] and dW[V,d] (float32; dW None when want_dW is False). skip_eps > 0 turns on the
+    coefficient filter (an approximation; see orpo_head_desc.skip_eps)."""
     _need_gpu(h, w, labels, lse, g, scales, biases, dW)
     M, d = h.shape
     V = _vocab(w, scales)
     flags = ORPO_DW_ACCUMULATE if accumulate else 0
-    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, flags)
+    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, flags, skip_eps)
     L = lib()
     ws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc)), h.device)
     dh = torch.empty(M, d, dtype=torch.float32, device=h.device)
@@ -262,7 +265,7 @@ def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip
 class HeadStep:
     def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
                  want_dW=True, ignore_index=IGNORE_INDEX, scope="response", objective="orpo",
-                 obj=None):
+                 obj=None, skip_eps=0.0):
         """One head step: forward -> loss -> backward on preallocated buffers.
 
         objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
@@ -278,7 +281,8 @@ class HeadStep:
         self.S = SCOPES[scope] if objective == "orpo" else (1 if objective == "grpo" else 2)
         self.P = (seg_offsets.shape[0] - 1) // self.S
         dev = h.device
-        self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
+        self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index,
+                              skip_eps=skip_eps)
         L = lib()
         self.fws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(self.desc)), dev)
         self.bws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(self.desc)), dev)

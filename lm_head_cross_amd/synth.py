@@ -47,6 +47,8 @@ class HeadConfig:
     q4: bool = False         # W as 4-bit group-encoded (group 64 along d)
     prompt_lo: int = 0       # prompt span lengths U[prompt_lo, prompt_hi] per pair; prompt_hi = 0:
     prompt_hi: int = 0       # no prompt spans (response-scope NLL)
+    w_std: float = 3.0       # W entries N(0, (w_std / sqrt(d))^2): logit standard deviation ~ w_std
+    p_argmax: float = 0.7    # share of labels that are the row's argmax (the rest uniform)
 
     @property
     def scope(self) -> str:
@@ -72,6 +74,10 @@ CONFIGS = {
                   len_hi=384, softcap=30.0, lam=0.1, q4=True),
     5: HeadConfig(5, "12b-like-bf16-softcap30", M=32768, d=3840, V=262144, pairs=32, len_lo=256,
                   len_hi=768, softcap=30.0, lam=0.2),
+    # The e4b head on peaked, teacher-forced-like logits (logit std 12 under the softcap, 95 % of
+    # labels the argmax): the data the backward's coefficient filter is meant for.
+    7: HeadConfig(7, "e4b-bf16-softcap30-peaked", M=8192, d=2560, V=262144, pairs=16, len_lo=192,
+                  len_hi=320, softcap=30.0, lam=0.1, w_std=12.0, p_argmax=0.95),
     # The e4b head with the full-scope NLL: each pair's chosen sequence also carries its prompt span.
     6: HeadConfig(6, "e4b-bf16-softcap30-fullnll", M=8192, d=2560, V=262144, pairs=16, len_lo=144,
                   len_hi=240, softcap=30.0, lam=0.1, prompt_lo=64, prompt_hi=128),
@@ -186,7 +192,7 @@ def make_inputs(cfg: HeadConfig, seed: int = 0, label_device: str = "cpu") -> He
 
     h64 = r_h.standard_normal((M, d))
     h64 /= np.sqrt(np.mean(h64 * h64, axis=1, keepdims=True))
-    w32 = r_w.standard_normal((V, d), dtype=np.float32) * np.float32(3.0 / math.sqrt(d))
+    w32 = r_w.standard_normal((V, d), dtype=np.float32) * np.float32(cfg.w_std / math.sqrt(d))
     if cfg.dtype == "f32":
         h = torch.from_numpy(h64.astype(np.float32))
         w = torch.from_numpy(w32)
@@ -198,7 +204,7 @@ def make_inputs(cfg: HeadConfig, seed: int = 0, label_device: str = "cpu") -> He
     coin = r_coin.random(M)
     uni = r_uni.integers(0, V, size=M)
     arg = argmax_labels(h, torch.from_numpy(w32) if cfg.q4 else w, label_device)
-    labels = np.where(coin < 0.7, arg, uni).astype(np.int32)
+    labels = np.where(coin < cfg.p_argmax, arg, uni).astype(np.int32)
     labels[int(off[-1]):] = IGNORE_INDEX
 
     wq = scales = biases = None

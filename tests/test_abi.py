@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def _desc(M=512, d=256, V=4096, h=H.ORPO_BF16, w=H.ORPO_BF16, cap=0.0, flags=0):
-    return H.Desc(M, d, V, h, w, cap, -100, flags)
+    return H.Desc(M, d, V, h, w, cap, -100, flags, 0.0)
 
 
 def test_workspace_sizes():

@@ -1,0 +1,120 @@
+"""GPU parity for the backward's coefficient filter (orpo_head_desc.skip_eps > 0): the HIP
+backward against the oracle's filtered backward (the same block definition, in float64), plus the
+exact path's invariance. The filter is an approximation; its distance from the exact backward is
+reported (fidelity) and gated loosely on peaked data."""
+import numpy as np
+import pytest
+import torch
+
+from lm_head_cross_amd import head as H
+from lm_head_cross_amd import synth
+from oracle import orpo_oracle as orc
+from tests.gpu_helpers import TOL_GRAD, dev, oracle_weight, rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _custom(M, d, V, cap, seed, w_std=3.0):
+    rng = np.random.default_rng(seed)
+    h = synth.to_bf16(rng.standard_normal((M, d)))
+    w = synth.to_bf16((rng.standard_normal((V, d)) * (w_std / np.sqrt(d))).astype(np.float32))
+    labels = rng.integers(0, V, size=M).astype(np.int32)
+    labels[M - 3:] = -100
+    labels[10] = -100
+    return h, w, labels
+
+
+def _gpu_bwd(h, w, labels, lse_o, g, cap, eps, scales=None, biases=None, want_dW=True):
+    d = dev()
+    lab = torch.from_numpy(labels).to(d)
+    lse = torch.from_numpy(lse_o.astype(np.float32)).to(d)
+    gg = torch.from_numpy(g.astype(np.float32)).to(d)
+    dh, dW = H.head_bwd(h.to(d), w.to(d), lab, lse, gg, cap, want_dW=want_dW,
+                        scales=None if scales is None else scales.to(d),
+                        biases=None if biases is None else biases.to(d), skip_eps=eps)
+    torch.cuda.synchronize()
+    return dh.cpu().numpy(), (None if dW is None else dW.cpu().numpy())
+
+
+def test_tiny_eps_is_bitwise_the_exact_backward():
+    h, w, labels = _custom(700, 192, 3001, 30.0, seed=1)
+    hh, W = h.float().numpy().astype(np.float64), w.float().numpy().astype(np.float64)
+    _, lse = orc.forward(hh, W, labels, 30.0)
+    g = np.random.default_rng(2).standard_normal(700) * 1e-3
+    g[labels == -100] = 0
+    a = _gpu_bwd(h, w, labels, lse, g, 30.0, 0.0)
+    b = _gpu_bwd(h, w, labels, lse, g, 30.0, 1e-30)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_filter_matches_the_oracles_filtered_backward():
+    # Loud cotangent on tokens 0..63 and 300..363, 1e-6 elsewhere; eps = 1e-3 between the two: the
+    # quiet token block 512..699 is dropped from dh whole, dW keeps only the loud 64-token slices.
+    h, w, labels = _custom(700, 192, 3001, 30.0, seed=3)
+    hh, W = h.float().numpy().astype(np.float64), w.float().numpy().astype(np.float64)
+    _, lse = orc.forward(hh, W, labels, 30.0)
+    g = np.full(700, 1e-6)
+    g[:64] = 1.0
+    g[300:364] = -0.5
+    g[labels == -100] = 0
+    eps = 1e-3
+    dh, dW = _gpu_bwd(h, w, labels, lse, g, 30.0, eps)
+    fh, fw, kh, kw = orc.backward_filtered(hh, W, labels, lse, g, 30.0, eps)
+    e_dh, e_dW = rel(dh, fh), rel(dW, fw)
+    say(f"[filter] kept dh {kh:.3f} dW {kw:.3f}; vs oracle filtered dh={e_dh:.2e} dW={e_dW:.2e}")
+    assert e_dh <= TOL_GRAD and e_dW <= TOL_GRAD
+    assert np.all(dh[512:] == 0.0)                      # the dropped token block
+    ex_dh, _ = orc.backward(hh, W, labels, lse, g, 30.0)
+    assert np.any(ex_dh[512:697] != 0.0)                 # ... which the exact backward fills
+
+
+@pytest.mark.parametrize("chunked", [False, True])
+def test_filter_on_peaked_data(chunked):
+    # Peaked logits (std 12 under the softcap), 95 % argmax labels, the ORPO cotangent, eps 1e-5.
+    cfg = synth.HeadConfig(0, "peaked-small", M=1024, d=256, V=16384, pairs=2, len_lo=200,
+                           len_hi=256, softcap=30.0, lam=0.1, w_std=12.0, p_argmax=0.95)
+    inp = synth.make_inputs(cfg, 0, label_device="cuda")
+    hh, W = inp.h.float().numpy().astype(np.float64), oracle_weight(inp)
+    ora = orc.head_step(hh, W, inp.labels, inp.seg_offsets, cfg.softcap, cfg.lam)
+    eps = 1e-5
+    say(f"[case] filter peaked chunked={chunked}")
+    if chunked:
+        H.set_bwd_tiling(256, 256 * 2048 * 2)          # 4 token chunks x 8 vocabulary blocks
+    try:
+        dh, dW = _gpu_bwd(inp.h, inp.w, inp.labels, ora["lse"], ora["g"], cfg.softcap, eps)
+    finally:
+        H.set_bwd_tiling(0, 0)
+    fh, fw, kh, kw = orc.backward_filtered(hh, W, inp.labels, ora["lse"], ora["g"], cfg.softcap, eps)
+    e_dh, e_dW = rel(dh, fh), rel(dW, fw)
+    f_dh, f_dW = rel(dh, ora["dh"]), rel(dW, ora["dW"])
+    say(f"[filter peaked] kept dh {kh:.3f} dW {kw:.3f}; vs filtered dh={e_dh:.2e} dW={e_dW:.2e}; "
+        f"fidelity vs exact dh={f_dh:.2e} dW={f_dW:.2e}")
+    assert kh < 0.9 and kw < 0.9                        # the filter does drop blocks here
+    assert e_dh <= TOL_GRAD and e_dW <= TOL_GRAD
+    assert f_dh <= 5e-2 and f_dW <= 5e-2
+
+
+def test_filter_with_4bit_weights():
+    cfg = synth.HeadConfig(0, "peaked-q4", M=512, d=256, V=4096, pairs=1, len_lo=200,
+                           len_hi=256, softcap=30.0, lam=0.1, q4=True, w_std=12.0, p_argmax=0.95)
+    inp = synth.make_inputs(cfg, 0, label_device="cuda")
+    hh, W = inp.h.float().numpy().astype(np.float64), oracle_weight(inp)
+    ora = orc.head_step(hh, W, inp.labels, inp.seg_offsets, cfg.softcap, cfg.lam, want_dW=False)
+    eps = 1e-5
+    w = torch.from_numpy(inp.wq.view(np.int32))
+    dh, _ = _gpu_bwd(inp.h, w, inp.labels, ora["lse"], ora["g"], cfg.softcap, eps,
+                     scales=inp.scales, biases=inp.biases, want_dW=False)
+    fh, _, kh, _ = orc.backward_filtered(hh, W, inp.labels, ora["lse"], ora["g"], cfg.softcap, eps)
+    e = rel(dh, fh)
+    say(f"[filter q4] kept dh {kh:.3f} vs filtered dh={e:.2e}")
+    assert e <= TOL_GRAD
+
+
+def test_filter_is_rejected_for_fp32():
+    d = dev()
+    h = torch.zeros(256, 64, device=d)
+    w = torch.zeros(512, 64, device=d)
+    lab = torch.zeros(256, dtype=torch.int32, device=d)
+    z = torch.zeros(256, device=d)
+    with pytest.raises(H.OrpoError):
+        H.head_bwd(h, w, lab, z, z, 0.0, skip_eps=1e-5)
