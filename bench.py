@@ -209,6 +209,20 @@ def main():
                       "tflops": (v[2] / (v[1] / 1e3) / 1e12) if v[1] > 0 and v[2] > 0 else None}
                   for k, v in kinds.items()}
 
+    # Coefficient filter: its distance from the exact backward on this batch (measured once, after
+    # the timed region and after the peak-memory reading).
+    fidelity = None
+    if args.skip_eps > 0:
+        ex = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
+                        want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj)
+        ex.step()
+        torch.cuda.synchronize()
+        rel = lambda a, b: float(torch.linalg.norm(a - b) / torch.linalg.norm(b))
+        fidelity = {"dh_rel": rel(step.dh, ex.dh),
+                    "dW_rel": None if step.dW is None else rel(step.dW, ex.dW),
+                    "against": "the exact backward on the same batch (HIP, skip_eps = 0)"}
+        del ex
+
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -264,6 +278,9 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if args.skip_eps > 0:
+        line["skip_fidelity"] = fidelity
+        line["roofline"]["work"] = "the exact method's FLOP (blocks the filter skips included)"
     print(json.dumps(line), flush=True)
 
 
