@@ -226,6 +226,10 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  *   dW             (device) float [V,d] out (overwritten, or accumulated with ORPO_DW_ACCUMULATE);
  *                  NULL computes dh only. Must be NULL for ORPO_Q4G64 (a quantised head is frozen).
  *   ws             (device) >= orpo_head_bwd_workspace_bytes(desc) bytes
+ *   With desc->skip_eps > 0 (the coefficient filter) the workspace also holds the filter's block
+ *   flags, and ORPO_EUNSUPPORTED is returned for fp32 heads and for backward tilings with more
+ *   than 8192 64-wide slices per coefficient row or column (orpo_set_bwd_tiling). The launches are
+ *   then traced with the exact method's work (skipped blocks included).
  */
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
                           const int32_t* labels, const float* lse, const float* g, float* dh,
