@@ -74,7 +74,8 @@ typedef struct {
                          * and from dW every 256-entry x 64-token block, whose max |coeff| < skip_eps
                          * (their GEMM K steps are skipped). An approximation, opt-in; the pages'
                          * default is 1e-5 ("Steel flash-CCE — handoff", Glossary E "Backward
-                         * approximations"). Ignored by orpo_head_fwd.                          */
+                         * approximations"). With skip_eps > 0 orpo_head_fwd also records per-tile
+                         * logit maxima in its workspace, for orpo_head_bwd's cold-tile skip.    */
 } orpo_head_desc;
 
 /* The head weights: `w` is W[V,d] row-major in w_fmt (for ORPO_Q4G64 the packed uint32 words
@@ -233,7 +234,8 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  */
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
                           const int32_t* labels, const float* lse, const float* g, float* dh,
-                          float* dW, void* ws, size_t ws_bytes, hipStream_t stream);
+                          float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
+                          hipStream_t stream);
 
 /* Backward tiling: the token chunk C (a multiple of 256, default 8192) and the byte budget of one
  * coefficient tile [C, BVb] (default 256 MiB, two are used; BVb is the largest multiple of 256

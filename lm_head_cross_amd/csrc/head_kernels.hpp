@@ -52,6 +52,7 @@ struct FwdArgs {
   const int32_t* labels;  // [M]
   float* logp;            // [M]: receives z[y] here, finished by merge_kernel
   float2* part;           // [nblk, M] (max in log2 units, sum of 2^(u - max))
+  float* tmax;            // [n_tb][n_vtiles][8]: per wave, max raw logit of its part of the tile
   uint32_t* status;
   int64_t M, d, V;
   float cap;
@@ -59,7 +60,9 @@ struct FwdArgs {
   int32_t n_tb, nblk, tiles_per_split, n_vtiles;
 };
 
-template <class E, bool Q4, bool SOFTCAP>
+// TMAX: the variant that also records each wave's largest raw logit per tile (the backward's
+// coefficient filter uses them to skip whole cold coefficient tiles).
+template <class E, bool Q4, bool SOFTCAP, bool TMAX>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   ORPO_DECLARE_SMEM(smem);
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     const int64_t vt0 = (int64_t)(tile0 + tile) * kTile;
     const int64_t vw0 = vt0 + wm * 128;              // first vocabulary row of this wave
     const bool tail = vt0 + kTile > a.V;
+    float rmax = kNegInf;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       // u = z * log2e (or (z - cap) * log2e under a softcap), masked past V on the last tile only
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
               const float x = SOFTCAP ? sc.kz * sc.r_of(raw) : raw * kLog2e - ref;
               const float e = exp2_(x);
               acc_s += keep(mb, r) ? e : 0.f;
+              if constexpr (TMAX) rmax = fmaxf(rmax, keep(mb, r) ? raw : kNegInf);
             }
         }
         return acc_s;
@@ -164,6 +169,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
           a.logp[tok[nb]] = z;
         }
       }
+    }
+    if constexpr (TMAX) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+      if (l == 0) a.tmax[((int64_t)tb * a.n_vtiles + tile0 + tile) * 8 + w] = rmax;
     }
   };
   f32x16 acc[4][2];
@@ -415,6 +425,8 @@ struct BwdArgs {
   int32_t n_jt;           // 256-tiles along d
   float skip_eps;         // coefficient filter threshold (0: exact backward)
   int32_t nsl_v, nsl_t;   // 64-wide vocabulary / token slices per coefficient buffer row / column
+  const float* tmax;      // the forward's per-tile, per-wave raw maxima [M/256][V/256][8] (or null)
+  int32_t n_vtiles;       // 256-tiles along the whole vocabulary
   BwdItem gm;             // dh / dW tiles (n_tiles = 0: none)
   BwdItem cf;             // coefficient tiles (n_tiles = 0: none)
 };
@@ -432,6 +444,56 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   const int64_t tbase = it.c0 + (int64_t)tt * kTile;  // global token of tile column 0
   const int64_t t_end = min(a.M, it.c0 + it.C_cur);
   const int64_t row_bytes = a.d * E::kSize;
+  const Softcap sc(SOFTCAP ? a.cap : 1.f);
+
+  if constexpr (SKIP) {
+    // Cold tile (the forward's block maxima): every coefficient obeys |coeff_tv| <= |g_t| p_tv
+    // <= |g_t| 2^((zmax - lse_t) log2 e) off the label (sech^2 <= 1), with zmax the softcapped
+    // largest raw logit the forward saw in this tile. When that bound is below eps for every
+    // token and no token's label falls in the tile, the filter would drop all of the tile's blocks:
+    // write its flags as zero and skip the recompute (the coefficients are then never read).
+    if (a.tmax) {
+      __shared__ float cold_b[4];
+      __shared__ int cold_y[4];
+      const int64_t tile_idx = ((tbase >> 8) * a.n_vtiles + (vbase >> 8)) * 8;
+      float rmax = kNegInf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rmax = fmaxf(rmax, a.tmax[tile_idx + i]);
+      const float zmax = SOFTCAP ? sc.cap - 2.f * sc.cap * sc.r_of(rmax) : rmax;
+      float b = 0.f;
+      bool ylab = false;
+      if (tid < kTile) {
+        const int64_t tk = tbase + tid;
+        const int y = tk < t_end ? a.labels[tk] : a.ignore_index;
+        const bool yv = tk < t_end && y != a.ignore_index && y >= 0 && (int64_t)y < a.V;
+        const float gt = yv ? a.g[tk] : 0.f;
+        if (gt != 0.f) {
+          b = fabsf(gt) * exp2_((zmax - a.lse[tk]) * kLog2e);
+          ylab = (int64_t)y >= vbase && (int64_t)y < vbase + kTile;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) b = fmaxf(b, __shfl_xor(b, o));
+        const bool anyy = __ballot(ylab) != 0;
+        if (l == 0) {
+          cold_b[w] = b;
+          cold_y[w] = anyy;
+        }
+      }
+      __syncthreads();
+      const float bound = fmaxf(fmaxf(cold_b[0], cold_b[1]), fmaxf(cold_b[2], cold_b[3]));
+      const bool cold = !(cold_y[0] | cold_y[1] | cold_y[2] | cold_y[3]) &&
+                        bound * 1.001f < a.skip_eps;      // margin for exp2's rounding
+      if (cold) {
+        if (l == 0) {
+          uint8_t* fh = it.fdh + ((int64_t)tt * a.nsl_v + 4 * vt + 2 * wm) * 4 + wn;
+          fh[0] = 0;
+          fh[4] = 0;
+          it.fdw[((int64_t)vt * a.nsl_t + 4 * tt + wn) * 2 + wm] = 0;
+        }
+        return;
+      }
+    }
+  }
 
   typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
   LoaderA la;
@@ -453,7 +515,6 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   auto nop = [](int, f32x16(&)[4][2]) {};
   gemm_run<E, true, true, false>(smem, 1, nk, issue, commit, nop, acc);
 
-  const Softcap sc(SOFTCAP ? a.cap : 1.f);
   typedef typename E::T T;
   T* out = (T*)it.coeff;
   float cmax[2] = {0.f, 0.f};   // max |coeff| of this lane in vocabulary slices 2 wm and 2 wm + 1

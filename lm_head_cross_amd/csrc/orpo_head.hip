@@ -105,6 +105,7 @@ orpo_status check_weight(Kind k, const orpo_weight& W) {
 
 struct FwdPlan {
   int n_tb, nblk, tps, n_vtiles;
+  size_t tmax_off;   // byte offset of the per-tile maxima (0: not recorded)
   size_t ws;
 };
 
@@ -116,6 +117,11 @@ FwdPlan plan_fwd(const orpo_head_desc* d) {
   p.tps = (int)cdiv(p.n_vtiles, nblk);
   p.nblk = (int)cdiv(p.n_vtiles, p.tps);
   p.ws = kHeader + round_up(size_t(p.nblk) * size_t(std::max<int64_t>(d->M, 0)) * sizeof(float2), 256);
+  p.tmax_off = 0;
+  if (d->skip_eps > 0.f) {   // per tile and wave, the largest raw logit (the backward's cold-tile test)
+    p.tmax_off = p.ws;
+    p.ws += round_up(size_t(p.n_tb) * size_t(p.n_vtiles) * 8 * sizeof(float), 256);
+  }
   return p;
 }
 
@@ -144,7 +150,13 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
 template <class E, bool Q4, bool SC>
 orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
   TraceScope ts(ORPO_K_FWD, 2.0 * double(a.M) * double(a.V) * double(a.d), st);
-  hipLaunchKernelGGL((fwd_kernel<E, Q4, SC>), dim3(grid), dim3(kThreads), 0, st, a);
+  if constexpr (E::kSize == 2) {
+    if (a.tmax) {
+      hipLaunchKernelGGL((fwd_kernel<E, Q4, SC, true>), dim3(grid), dim3(kThreads), 0, st, a);
+      return launched();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<E, Q4, SC, false>), dim3(grid), dim3(kThreads), 0, st, a);
   return launched();
 }
 
@@ -216,6 +228,7 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.labels = labels;
   a.logp = logp;
   a.part = (float2*)((char*)ws + kHeader);
+  a.tmax = p.tmax_off ? (float*)((char*)ws + p.tmax_off) : nullptr;
   a.status = (uint32_t*)ws;
   a.M = desc->M;
   a.d = desc->d;
@@ -372,7 +385,8 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
 
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
                           const int32_t* labels, const float* lse, const float* g, float* dh,
-                          float* dW, void* ws, size_t ws_bytes, hipStream_t stream) {
+                          float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
+                          hipStream_t stream) {
   Kind k;
   orpo_status st = check_desc(desc, &k);
   if (st != ORPO_OK) return st;
@@ -403,6 +417,9 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.nsl_v = (int32_t)(p.BVb / 64);
   a.nsl_t = (int32_t)(p.C / 64);
   if (a.skip_eps > 0.f && (a.nsl_v > kMaxKSteps || a.nsl_t > kMaxKSteps)) return ORPO_EUNSUPPORTED;
+  a.tmax = (a.skip_eps > 0.f && fwd_ws) ? (const float*)((const char*)fwd_ws + plan_fwd(desc).tmax_off)
+                                        : nullptr;
+  a.n_vtiles = (int32_t)cdiv(desc->V, kTile);
   const bool sc = desc->softcap > 0.f;
   const bool acc_dw = (desc->flags & ORPO_DW_ACCUMULATE) != 0;
   const size_t esize = k == kF32 ? 4 : 2;

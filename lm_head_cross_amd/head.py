@@ -55,7 +55,7 @@ _SIGS = {
                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_double,
                                       ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P]),
     "orpo_head_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, _P, _P,
-                                     ctypes.c_size_t, _P]),
+                                     ctypes.c_size_t, _P, _P]),
     "orpo_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
     "orpo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orpo_last_hip_error": (ctypes.c_int32, []),
@@ -136,12 +136,13 @@ def read_status(ws: torch.Tensor) -> int:
 
 
 def head_fwd(h, w, labels, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None, biases=None,
-             return_ws=False):
-    """logp[M], lse[M] (float32). `w` is W[V,d] (f32/bf16) or the packed q4 words [V,d/8] (int32)."""
+             return_ws=False, skip_eps=0.0):
+    """logp[M], lse[M] (float32). `w` is W[V,d] (f32/bf16) or the packed q4 words [V,d/8] (int32).
+    skip_eps > 0 also records the per-tile logit maxima the backward's cold-tile skip reads."""
     _need_gpu(h, w, labels, scales, biases)
     M, d = h.shape
     V = _vocab(w, scales)
-    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
+    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, skip_eps=skip_eps)
     L = lib()
     ws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(desc)), h.device)
     logp = torch.empty(M, dtype=torch.float32, device=h.device)
@@ -176,9 +177,10 @@ def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, retu
 
 
 def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNORE_INDEX,
-             scales=None, biases=None, dW=None, accumulate=False, skip_eps=0.0):
+             scales=None, biases=None, dW=None, accumulate=False, skip_eps=0.0, fwd_ws=None):
     """dh[M,d] and dW[V,d] (float32; dW None when want_dW is False). skip_eps > 0 turns on the
-    coefficient filter (an approximation; see orpo_head_desc.skip_eps)."""
+    coefficient filter (an approximation; see orpo_head_desc.skip_eps); fwd_ws, the forward's
+    workspace (head_fwd(..., skip_eps=..., return_ws=True)), adds its exact cold-tile skip."""
     _need_gpu(h, w, labels, lse, g, scales, biases, dW)
     M, d = h.shape
     V = _vocab(w, scales)
@@ -194,7 +196,8 @@ def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNOR
     wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
                 None if biases is None else biases.data_ptr())
     _check(L.orpo_head_bwd(ctypes.byref(desc), _ptr(h), wt, _ptr(labels), _ptr(lse), _ptr(g),
-                           _ptr(dh), _ptr(dW), _ptr(ws), ws.numel(), _stream(h.device)), "orpo_head_bwd")
+                           _ptr(dh), _ptr(dW), _ptr(ws), ws.numel(), _ptr(fwd_ws), _stream(h.device)),
+           "orpo_head_bwd")
     return dh, dW
 
 
@@ -332,7 +335,8 @@ class HeadStep:
     def backward(self):
         _check(lib().orpo_head_bwd(ctypes.byref(self.desc), _ptr(self.h), self.wt, _ptr(self.labels),
                                    _ptr(self.lse), _ptr(self.g), _ptr(self.dh), _ptr(self.dW),
-                                   _ptr(self.bws), self.bws.numel(), self._s()), "orpo_head_bwd")
+                                   _ptr(self.bws), self.bws.numel(), _ptr(self.fws), self._s()),
+               "orpo_head_bwd")
 
     def step(self):
         self.forward()

@@ -77,7 +77,7 @@ def test_fwd_rejects_bad_weights_and_workspace():
 def test_bwd_rejects_dW_for_quantised_head():
     L = H.lib()
     q = _desc(w=H.ORPO_Q4G64)
-    st = L.orpo_head_bwd(ctypes.byref(q), 16, H.Weight(16, 16, 16), 16, 16, 16, 16, 16, 4096, 1 << 30, None)
+    st = L.orpo_head_bwd(ctypes.byref(q), 16, H.Weight(16, 16, 16), 16, 16, 16, 16, 16, 4096, 1 << 30, None, None)
     assert st == EUNSUP
 
 

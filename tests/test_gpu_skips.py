@@ -118,3 +118,40 @@ def test_filter_is_rejected_for_fp32():
     z = torch.zeros(256, device=d)
     with pytest.raises(H.OrpoError):
         H.head_bwd(h, w, lab, z, z, 0.0, skip_eps=1e-5)
+
+
+def test_cold_tile_skip_is_exact_for_the_filter_and_skips_tiles():
+    # With the forward's workspace the backward also skips whole cold coefficient tiles; the filter
+    # would drop all of their blocks, so dh and dW equal the filter-only result bit for bit. The
+    # skipped tiles leave their part of the coefficient buffer untouched (a sentinel fill shows it).
+    import ctypes
+    d = dev()
+    # 256 vocabulary tiles, so a 256-token tile's labels leave many of them label-free.
+    cfg = synth.HeadConfig(0, "peaked-cold", M=1024, d=256, V=65536, pairs=2, len_lo=200,
+                           len_hi=256, softcap=30.0, lam=0.1, w_std=12.0, p_argmax=0.95)
+    inp = synth.make_inputs(cfg, 0, label_device="cuda")
+    eps = 1e-4
+    h, w = inp.h.to(d), inp.w.to(d)
+    lab = torch.from_numpy(inp.labels).to(d)
+    off = torch.from_numpy(inp.seg_offsets).to(d)
+    logp, lse, fws = H.head_fwd(h, w, lab, cfg.softcap, return_ws=True, skip_eps=eps)
+    _, g = H.orpo_loss(logp, lab, off, cfg.V, cfg.lam)
+    dh0, dW0 = H.head_bwd(h, w, lab, lse, g, cfg.softcap, skip_eps=eps)             # filter only
+    desc = H.make_desc(cfg.M, cfg.d, cfg.V, h.dtype, H._w_fmt(w, None), cfg.softcap, skip_eps=eps)
+    L = H.lib()
+    nbytes = L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=d)
+    dh = torch.empty_like(dh0)
+    dW = torch.empty_like(dW0)
+    st = L.orpo_head_bwd(ctypes.byref(desc), H._ptr(h), H.Weight(w.data_ptr(), None, None),
+                         H._ptr(lab), H._ptr(lse), H._ptr(g), H._ptr(dh), H._ptr(dW),
+                         H._ptr(ws), nbytes, H._ptr(fws), H._stream(d))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dh, dh0) and torch.equal(dW, dW0)
+    # One item here (C = 1024 tokens, BVb = 65536): buffer 0 holds its [1024, 65536] coefficients.
+    coeff = ws[256:256 + 1024 * 65536 * 2].view(torch.int16).view(1024, 65536)
+    untouched = (coeff == -1).view(4, 256, 256, 256).all(dim=3).all(dim=1)    # [token tile, vocab tile]
+    n_cold = int(untouched.sum().item())
+    say(f"[filter cold tiles] {n_cold} of {untouched.numel()} coefficient tiles skipped")
+    assert n_cold > 0
