@@ -125,3 +125,24 @@ def test_objective_entry_points_reject_bad_arguments():
     assert L.orpo_grpo_loss(10, 1, 16, 16, None, 16, 16, 16, 100, -100, 0.2, 0.1, 16, 16, ws, 4096, None) == EINVAL
     assert L.orpo_grpo_loss(10, 1, 16, 16, 16, 16, 16, 16, 100, -100, -1.0, 0.1, 16, 16, ws, 4096, None) == EINVAL
     assert L.orpo_grpo_loss(10, 1, 16, 16, 16, 16, 16, 16, 100, -100, 0.2, 0.1, 16, 16, ws, 16, None) == ENOWS
+
+
+def test_skip_eps_validation_and_workspaces():
+    L = H.lib()
+    d = _desc(M=8192, d=2560, V=262144)
+    fws0 = L.orpo_head_fwd_workspace_bytes(ctypes.byref(d))
+    bws0 = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
+    d.skip_eps = 1e-5
+    # Forward: + the per-tile, per-wave logit maxima [32 token tiles][1024 vocabulary tiles][8].
+    assert L.orpo_head_fwd_workspace_bytes(ctypes.byref(d)) == fws0 + 32 * 1024 * 8 * 4
+    # Backward: + two sets of filter flags, dh [32][256][4] and dW [64][128][2] bytes.
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == bws0 + 2 * (32 * 256 * 4 + 64 * 128 * 2)
+    for bad in (-1e-5, float("inf"), float("nan")):
+        d.skip_eps = bad
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    f32 = _desc(h=H.ORPO_F32, w=H.ORPO_F32)
+    f32.skip_eps = 1e-5
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(f32)) == 0     # unsupported for fp32
+    st = L.orpo_head_bwd(ctypes.byref(f32), 16, H.Weight(16, None, None), 16, 16, 16, 16, 16, 16,
+                         1 << 30, None, None)
+    assert st == EUNSUP
