@@ -98,13 +98,64 @@ def dpo_epilogue(sw, sr, ref_w, ref_r, beta: float):
             "margin": math.fsum(delta) / P, "delta": delta, "dL_dw": dw, "dL_dr": -dw}
 
 
+# --------------------------------------------------------------------------------------------
+# IPO and hinge (SLiC)
+# --------------------------------------------------------------------------------------------
+# The pages name both as siblings on the shared log-prob engine (Training — design, §8.3
+# "Objective variants and data") and give no formula. Reading: each is the published loss on the
+# log-ratio margin h = (v_w - ref_w) - (v_r - ref_r), with reference values optional (zero gives
+# the reference-free form that SimPO uses). IPO takes SimPO's length-normalised means (the
+# squared loss is scale-sensitive, and length normalisation keeps its target margin meaningful
+# across lengths); hinge takes DPO's per-sequence sums, as SLiC's calibration loss does.
+def ipo_epilogue(lw, lr, ref_w, ref_r, beta: float):
+    """IPO: L_p = (h_p - 1 / (2 beta))^2 with h_p = (lw - ref_w) - (lr - ref_r) on the branch
+    means; loss = mean over pairs (beta > 0). Metrics: accuracy = mean 1[h > 0], margin = mean h.
+    dL/dlw = 2 (h - 1 / (2 beta)) / P, dL/dlr = -dL/dlw."""
+    if not beta > 0:
+        raise OracleError("IPO needs beta > 0")
+    lw, lr, ref_w, ref_r = (np.asarray(x, dtype=np.float64) for x in (lw, lr, ref_w, ref_r))
+    P = lw.shape[0]
+    target = 1.0 / (2.0 * beta)
+    hm = np.zeros(P)
+    lp = np.zeros(P)
+    dw = np.zeros(P)
+    for p in range(P):
+        hm[p] = (lw[p] - ref_w[p]) - (lr[p] - ref_r[p])
+        lp[p] = (hm[p] - target) ** 2
+        dw[p] = 2.0 * (hm[p] - target) / P
+    return {"loss": math.fsum(lp) / P, "accuracy": float(np.mean(hm > 0)),
+            "margin": math.fsum(hm) / P, "h": hm, "dL_dw": dw, "dL_dr": -dw}
+
+
+def hinge_epilogue(sw, sr, ref_w, ref_r, beta: float):
+    """Hinge / SLiC: L_p = max(0, 1 - beta h_p) with h_p = (sw - ref_w) - (sr - ref_r) on the
+    per-sequence sums; loss = mean over pairs. Metrics: accuracy = mean 1[h > 0], margin = mean h.
+    dL/dsw = -beta / P where 1 - beta h > 0, else 0 (the flat side's zero at the kink itself),
+    dL/dsr = -dL/dsw."""
+    sw, sr, ref_w, ref_r = (np.asarray(x, dtype=np.float64) for x in (sw, sr, ref_w, ref_r))
+    P = sw.shape[0]
+    hm = np.zeros(P)
+    lp = np.zeros(P)
+    dw = np.zeros(P)
+    for p in range(P):
+        hm[p] = (sw[p] - ref_w[p]) - (sr[p] - ref_r[p])
+        u = 1.0 - beta * hm[p]
+        lp[p] = u if u > 0 else 0.0
+        dw[p] = -beta / P if u > 0 else 0.0
+    return {"loss": math.fsum(lp) / P, "accuracy": float(np.mean(hm > 0)),
+            "margin": math.fsum(hm) / P, "h": hm, "dL_dw": dw, "dL_dr": -dw}
+
+
+MEAN_KINDS = ("simpo", "ipo")     # length-normalised branch values; the others use sums
+
+
 def pairwise_cotangent(kind: str, ep, n, labels, seg_offsets, ignore_index: int = IGNORE_INDEX):
-    """Per-token g for the pairwise objectives (spans: chosen 2p, rejected 2p+1): a mean (SimPO)
-    spreads dL/dell_b as 1/n_b per token, a sum (DPO) passes it unchanged."""
+    """Per-token g for the pairwise objectives (spans: chosen 2p, rejected 2p+1): a mean (SimPO,
+    IPO) spreads dL/dell_b as 1/n_b per token, a sum (DPO, hinge) passes it unchanged."""
     P = len(ep["dL_dw"])
     dl = np.zeros(2 * P)
     dl[0::2], dl[1::2] = ep["dL_dw"], ep["dL_dr"]
-    scale = 1.0 / np.asarray(n, dtype=np.float64) if kind == "simpo" else None
+    scale = 1.0 / np.asarray(n, dtype=np.float64) if kind in MEAN_KINDS else None
     return span_cotangent(dl, labels, seg_offsets, scale, ignore_index)
 
 

@@ -72,19 +72,33 @@ def _pair_problem(seed, cap):
 def _pairwise_loss(kind, h, W, labels, off, cap, params, ref=None):
     logp, _ = orc.forward(h, W, labels, cap)
     sums, n = ob.span_stats(logp, labels, off)
+    means = sums / n
     if kind == "simpo":
-        means = sums / n
         ep = ob.simpo_epilogue(means[0::2], means[1::2], *params)
+    elif kind == "ipo":
+        ep = ob.ipo_epilogue(means[0::2], means[1::2], ref[0::2], ref[1::2], *params)
+    elif kind == "hinge":
+        ep = ob.hinge_epilogue(sums[0::2], sums[1::2], ref[0::2], ref[1::2], *params)
     else:
         ep = ob.dpo_epilogue(sums[0::2], sums[1::2], ref[0::2], ref[1::2], *params)
     return ep, n
 
 
-@pytest.mark.parametrize("kind,cap", [("simpo", 0.0), ("simpo", 2.0), ("dpo", 0.0), ("dpo", 2.0)])
+_FD_PARAMS = {"simpo": ((2.0, 0.3), None, 4),
+              "dpo": ((0.7,), np.array([-20.0, -18.5, -17.0, -21.0]), 3),
+              # IPO: reference means near the policy's, so each pair's margin is away from the
+              # target 1/(2 beta) and the gradient is not degenerate.
+              "ipo": ((0.8,), np.array([-2.1, -2.6, -2.4, -1.9]), 5),
+              # Hinge: beta and reference sums chosen so one pair is on the sloped side and one on
+              # the flat side, both far from the kink (checked below).
+              "hinge": ((0.25,), np.array([-20.0, -6.0, -14.0, -10.0]), 6)}
+
+
+@pytest.mark.parametrize("kind,cap", [(k, c) for k in ("simpo", "dpo", "ipo", "hinge")
+                                      for c in (0.0, 2.0)])
 def test_pairwise_gradients_match_central_finite_differences(kind, cap):
-    h, W, labels, off = _pair_problem(3 if kind == "dpo" else 4, cap)
-    params = (2.0, 0.3) if kind == "simpo" else (0.7,)
-    ref = np.array([-20.0, -18.5, -17.0, -21.0]) if kind == "dpo" else None
+    params, ref, seed = _FD_PARAMS[kind]
+    h, W, labels, off = _pair_problem(seed, cap)
     logp, lse = orc.forward(h, W, labels, cap)
     ep, n = _pairwise_loss(kind, h, W, labels, off, cap, params, ref)
     g = ob.pairwise_cotangent(kind, ep, n, labels, off)
@@ -102,10 +116,59 @@ def test_pairwise_gradients_match_central_finite_differences(kind, cap):
             out[idx] = (lp - lm) / (2 * eps)
         return out
 
+    if kind == "hinge":
+        u = 1.0 - params[0] * ep["h"]
+        assert np.min(np.abs(u)) > 0.05 and np.any(u > 0) and np.any(u < 0), u
     gh, gw = fd(h, "h"), fd(W, "W")
+    assert np.linalg.norm(gh) > 0
     assert np.linalg.norm(dh - gh) <= 1e-6 * np.linalg.norm(gh)
     assert np.linalg.norm(dW - gw) <= 1e-6 * np.linalg.norm(gw)
     assert np.all(dh[[4, 12, 13]] == 0.0)
+
+
+# ----------------------------------------------------------------------------- IPO, hinge
+def test_ipo_at_target_margin_and_at_zero_margin():
+    # beta = 0.5: target 1/(2 beta) = 1. Margin exactly 1 -> zero loss and zero gradient.
+    ep = ob.ipo_epilogue([-1.0], [-2.0], [0.0], [0.0], 0.5)
+    assert ep["h"][0] == 1.0 and ep["loss"] == 0.0 and ep["dL_dw"][0] == 0.0
+    # Policy equal to the reference: h = 0, L = 1/(4 beta^2), dL/dlw = -1/beta / P.
+    ep = ob.ipo_epilogue([-1.25, -3.0], [-2.0, -0.5], [-1.25, -3.0], [-2.0, -0.5], 0.25)
+    assert np.all(ep["h"] == 0.0) and ep["loss"] == pytest.approx(4.0, rel=1e-15)
+    assert np.allclose(ep["dL_dw"], -4.0 / 2, rtol=1e-15) and ep["accuracy"] == 0.0
+    with pytest.raises(orc.OracleError):
+        ob.ipo_epilogue([-1.0], [-2.0], [0.0], [0.0], 0.0)
+
+
+def test_ipo_closed_form():
+    # h = (-1 + 1.5) - (-3 + 2) = 1.5, beta = 2 -> target 0.25: L = 1.25^2, dL/dlw = 2.5.
+    ep = ob.ipo_epilogue([-1.0], [-3.0], [-1.5], [-2.0], 2.0)
+    assert ep["h"][0] == 1.5 and ep["margin"] == 1.5 and ep["accuracy"] == 1.0
+    assert ep["loss"] == 1.5625 and ep["dL_dw"][0] == 2.5 and ep["dL_dr"][0] == -2.5
+
+
+def test_hinge_flat_and_sloped_sides():
+    # beta h >= 1: no loss, no gradient (the kink itself included).
+    ep = ob.hinge_epilogue([-10.0, -10.0], [-14.0, -12.0], [0.0, 0.0], [0.0, 0.0], 0.5)
+    assert list(ep["h"]) == [4.0, 2.0] and ep["loss"] == 0.0 and np.all(ep["dL_dw"] == 0.0)
+    # beta h < 1: L = 1 - beta h, dL/dsw = -beta / P.
+    ep = ob.hinge_epilogue([-10.0, -30.0], [-15.0, -20.0], [-1.0, 0.0], [-3.0, 0.0], 0.25)
+    assert list(ep["h"]) == [3.0, -10.0]
+    assert ep["loss"] == pytest.approx(((1 - 0.75) + (1 + 2.5)) / 2, rel=1e-15)
+    assert np.all(ep["dL_dw"] == -0.125) and np.all(ep["dL_dr"] == 0.125)
+    assert ep["accuracy"] == 0.5 and ep["margin"] == -3.5
+
+
+def test_pairwise_cotangent_mean_kinds_and_sum_kinds():
+    labels = np.zeros(10, dtype=np.int64)
+    labels[2] = -100
+    off = np.array([0, 4, 10])
+    ep = ob.ipo_epilogue([-3.0], [-4.0], [0.0], [0.0], 1.0)
+    g = ob.pairwise_cotangent("ipo", ep, [3, 6], labels, off)
+    assert g[2] == 0.0 and np.allclose(g[[0, 1, 3]], ep["dL_dw"][0] / 3, rtol=1e-15)
+    assert np.allclose(g[4:], ep["dL_dr"][0] / 6, rtol=1e-15)
+    ep = ob.hinge_epilogue([-3.0], [-4.0], [0.0], [0.0], 0.5)
+    g = ob.pairwise_cotangent("hinge", ep, [3, 6], labels, off)
+    assert g[2] == 0.0 and np.all(g[[0, 1, 3]] == -0.5) and np.all(g[4:] == 0.5)
 
 
 def test_dpo_cotangent_is_per_sequence_sum_and_simpo_per_token_mean():
