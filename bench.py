@@ -31,7 +31,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
-    ap.add_argument("--objective", default="orpo", choices=["orpo", "simpo", "dpo", "grpo"],
+    ap.add_argument("--objective", default="orpo",
+                    choices=["orpo", "simpo", "dpo", "ipo", "hinge", "grpo"],
                     help="the loss between the head's forward and backward")
     ap.add_argument("--skip-eps", type=float, default=0.0,
                     help="backward coefficient filter threshold (0 = exact backward)")
@@ -44,15 +45,18 @@ def _objective_inputs(objective: str, cfg, off: np.ndarray, n_valid_per_span: np
                       seed: int) -> dict:
     """Seeded synthetic inputs of the sibling objectives (parameters and cached reference values);
     timing only. SimPO beta 2, gamma 0.5; DPO beta 0.1 with reference sums near the head's scale;
+    IPO beta 0.5 with reference means near the head's; hinge beta 0.1 with reference sums;
     GRPO clip 0.2, KL weight 0.04, groups of 4 completions; the sampling and reference policies'
     log-probs are filled in by main() from the policy's own forward plus seeded noise."""
     import numpy as np
     rng = np.random.default_rng(9000 + seed)
     if objective == "simpo":
         return {"beta": 2.0, "gamma": 0.5}
-    if objective == "dpo":
+    if objective in ("dpo", "hinge"):
         ref = -7.7 * n_valid_per_span + rng.normal(0.0, 5.0, size=n_valid_per_span.shape)
         return {"beta": 0.1, "ref_sums": ref}
+    if objective == "ipo":
+        return {"beta": 0.5, "ref_sums": -7.7 + rng.normal(0.0, 0.1, size=n_valid_per_span.shape)}
     if objective == "grpo":
         S = len(off) - 1
         rewards = rng.normal(size=S + (-S) % 4)
@@ -99,6 +103,13 @@ def cpu_baseline(inp, rows: int, objective: str):
         elif objective == "dpo":
             ep = ob.dpo_epilogue(sums[0::2], sums[1::2], sums[0::2] - 1.0, sums[1::2], 0.1)
             g = ob.pairwise_cotangent("dpo", ep, n, labels, off)
+        elif objective == "ipo":
+            m = sums / n
+            ep = ob.ipo_epilogue(m[0::2], m[1::2], m[0::2] - 0.1, m[1::2], 0.5)
+            g = ob.pairwise_cotangent("ipo", ep, n, labels, off)
+        elif objective == "hinge":
+            ep = ob.hinge_epilogue(sums[0::2], sums[1::2], sums[0::2] + 1.0, sums[1::2], 0.1)
+            g = ob.pairwise_cotangent("hinge", ep, n, labels, off)
         else:
             ep = ob.grpo_loss(logp, logp - 0.1, logp + 0.1, labels, off, np.array([1.0, -1.0]), 0.2, 0.04)
             g = ep["g"]

@@ -66,7 +66,9 @@ typedef struct {
   int64_t V;            /* vocabulary size, > 0                                                 */
   int32_t h_fmt;        /* ORPO_F32 or ORPO_BF16; row-major [M,d]                               */
   int32_t w_fmt;        /* ORPO_F32 (needs h_fmt F32), ORPO_BF16 or ORPO_Q4G64 (need h_fmt BF16) */
-  float softcap;        /* > 0: z = softcap * tanh(raw / softcap); <= 0: z = raw                */
+  float softcap;        /* > 0: z = softcap * tanh(raw / softcap); <= 0: z = raw. At most 40   */
+                        /* (ORPO_EUNSUPPORTED above: the kernels' fixed softmax reference     */
+                        /* keeps every term a normal float only up to there)                   */
   int32_t ignore_index; /* label value of ignored / padding tokens (conventionally -100)        */
   uint32_t flags;       /* ORPO_DW_ACCUMULATE                                                   */
   float skip_eps;       /* backward coefficient filter: 0 = exact backward; > 0 (bf16 and 4-bit
@@ -165,7 +167,12 @@ orpo_status orpo_loss_full(int64_t M, int32_t n_pairs, const int32_t* seg_offset
  */
 size_t orpo_objective_workspace_bytes(int64_t M, int32_t n_spans);
 
-typedef enum { ORPO_PREF_SIMPO = 1, ORPO_PREF_DPO = 2 } orpo_pref_kind;
+typedef enum {
+  ORPO_PREF_SIMPO = 1,
+  ORPO_PREF_DPO = 2,
+  ORPO_PREF_IPO = 3,
+  ORPO_PREF_HINGE = 4
+} orpo_pref_kind;
 
 /*
  * orpo_pref_loss — pairwise preference losses (chosen span 2p, rejected span 2p+1 of seg_offsets,
@@ -179,12 +186,19 @@ typedef enum { ORPO_PREF_SIMPO = 1, ORPO_PREF_DPO = 2 } orpo_pref_kind;
  *     1[Delta > 0]; margin = mean Delta. gamma is unused. (The post-training design page, "Stage
  *     P1 — DPO": seq_logprob as a per-sequence sum, the DPO loss, only policy terms carry
  *     gradient.)
- *   loss = mean over pairs. g_t = dloss/dlogp_t: dL/dlw / n_w for SimPO (a mean), dL/dsw for DPO (a
- *   sum); 0 for ignored / off-span tokens.
+ *   ORPO_PREF_IPO and ORPO_PREF_HINGE: "Training — design" §8.3 names IPO and hinge/SLiC as
+ *     siblings without formulas; both are read as the published losses on the log-ratio margin
+ *     h = (v_w - ref_w) - (v_r - ref_r), where ref_sums holds reference values of the same kind
+ *     (means for IPO, sums for hinge) and is optional (NULL: reference-free, ref = 0).
+ *     IPO: v = mean logp (as SimPO), L = (h - 1/(2 beta))^2, beta > 0 required.
+ *     HINGE: v = summed logp (as DPO), L = max(0, 1 - beta h), zero gradient at the kink.
+ *     accuracy = mean 1[h > 0]; margin = mean h. gamma is unused.
+ *   loss = mean over pairs. g_t = dloss/dlogp_t: dL/dv / n for the means (SimPO, IPO), dL/dv for
+ *   the sums (DPO, hinge); 0 for ignored / off-span tokens.
  *   out   (device) double [3 + 2*n_pairs]: loss, accuracy, margin, then the chosen values [n_pairs]
  *         (lw or sw), then the rejected ones [n_pairs]
- *   Errors and status bits as for orpo_loss (ORPO_EINVAL also for an unknown kind or a DPO call
- *   without ref_sums).
+ *   Errors and status bits as for orpo_loss (ORPO_EINVAL also for an unknown kind, a DPO call
+ *   without ref_sums, or IPO with beta <= 0).
  */
 orpo_status orpo_pref_loss(int32_t kind, int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
                            const float* logp, const int32_t* labels, int64_t V,

@@ -518,6 +518,10 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   typedef typename E::T T;
   T* out = (T*)it.coeff;
   float cmax[2] = {0.f, 0.f};   // max |coeff| of this lane in vocabulary slices 2 wm and 2 wm + 1
+  const int64_t vw0 = vbase + wm * 128;            // first vocabulary row of this wave
+  // Valid rows of the wave less this lane's row offset 4 (l / 32), as in the forward, so that the
+  // tail tile's mask compares compile-time constants.
+  const int lim = (int)min<int64_t>(max<int64_t>(a.V - vw0, 0), 128) - 4 * (l >> 5);
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = acc_n(wn, nb, l);
@@ -527,44 +531,81 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     const bool yv = tv && y != a.ignore_index && y >= 0 && (int64_t)y < a.V;   // else: ignored
     const float gt = yv ? a.g[tk] : 0.f;
     const float L2 = yv ? a.lse[tk] * kLog2e : 0.f;
-    const int64_t yo = (int64_t)y - vbase;             // label row within this tile
+    // Off the label, coeff = -g p sech^2. Under a softcap, with rr = 1 / (1 + 2^(raw c1)) (so
+    // tanh = 1 - 2 rr, z log2e = cap log2e + kz rr, sech^2 = 4 rr (1 - rr)), that is
+    //   coeff = G (rr - rr^2) 2^(kz rr),   G = -4 g 2^(cap log2e - L2)  (one factor per token);
+    // without one, coeff = -g 2^(raw log2e - L2). Both exponents stay in float range for
+    // softcaps up to 40 (the library's limit). The label's own entry adds g sech^2 (patched below).
+    const float G = SOFTCAP ? -4.f * gt * exp2_(sc.cap * kLog2e - L2) : -gt;
     T* row = out + (tk - it.c0) * a.BVb + (vbase - it.v0);
+    auto body = [&](auto masked_tag) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        float vals[4];
+        for (int rg = 0; rg < 4; ++rg) {
+          float vals[4];
 #pragma unroll
-        for (int ri = 0; ri < 4; ++ri) {
-          const int r = rg * 4 + ri;
-          const int mm = acc_m(wm, mb, r, l);
-          const float raw = acc[mb][nb][r];
-          float zl2, slope;
-          if (SOFTCAP) {
-            const float rr = sc.r_of(raw);
-            zl2 = (sc.cap - 2.f * sc.cap * rr) * kLog2e;
-            slope = 4.f * rr * (1.f - rr);
-          } else {
-            zl2 = raw * kLog2e;
-            slope = 1.f;
+          for (int ri = 0; ri < 4; ++ri) {
+            const int r = rg * 4 + ri;
+            const float raw = acc[mb][nb][r];
+            float c;
+            if (SOFTCAP) {
+              const float rr = sc.r_of(raw);
+              c = G * (__builtin_fmaf(-rr, rr, rr) * exp2_(sc.kz * rr));
+            } else {
+              c = G * exp2_(__builtin_fmaf(raw, kLog2e, -L2));
+            }
+            if (kMasked && !(mb * 32 + 8 * rg + ri < lim)) c = 0.f;
+            vals[ri] = c;
+            if constexpr (SKIP) cmax[mb >> 1] = fmaxf(cmax[mb >> 1], fabsf(c));
           }
-          const float p = exp2_(zl2 - L2);
-          float c = gt * ((yo == mm ? 1.f : 0.f) - p) * slope;
-          if (vbase + mm >= a.V || gt == 0.f) c = 0.f;
-          vals[ri] = c;
-          if constexpr (SKIP) cmax[mb >> 1] = fmaxf(cmax[mb >> 1], fabsf(c));
+          // 4 consecutive vocabulary entries of token tk.
+          const int m0 = acc_m(wm, mb, rg * 4, l);
+          if constexpr (sizeof(T) == 2) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(vals[0], vals[1]);
+            pk[1] = pack_bf16x2(vals[2], vals[3]);
+            *(u32x2*)(row + m0) = pk;
+          } else {
+            *(f32x4*)(row + m0) = f32x4{vals[0], vals[1], vals[2], vals[3]};
+          }
         }
-        // 4 consecutive vocabulary entries of token tk.
-        const int m0 = acc_m(wm, mb, rg * 4, l);
-        if constexpr (sizeof(T) == 2) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(vals[0], vals[1]);
-          pk[1] = pack_bf16x2(vals[2], vals[3]);
-          *(u32x2*)(row + m0) = pk;
+    };
+    if (vbase + kTile > a.V) body(std::true_type{}); else body(std::false_type{});
+    // The label's entry: the one lane holding (v = y, t) rewrites it as g (1 - p) sech^2, after its
+    // earlier store to the same address has completed.
+    const int64_t off = (int64_t)y - vw0;
+    const bool mine = yv && off >= 0 && off < 128 && (((int)off >> 2) & 1) == (l >> 5);
+    if (__builtin_expect(__ballot(mine) != 0, 0)) {
+      if (mine) {
+        const int o = (int)off, mbl = o >> 5, ro = o & 31;
+        const int rl = ((ro >> 3) << 2) | (ro & 3);
+        float raw = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+          for (int rr_ = 0; rr_ < 16; ++rr_)
+            if (mm == mbl && rr_ == rl) raw = acc[mm][nb][rr_];
+        float zl2, slope;
+        if (SOFTCAP) {
+          const float rr = sc.r_of(raw);
+          zl2 = (sc.cap - 2.f * sc.cap * rr) * kLog2e;
+          slope = 4.f * rr * (1.f - rr);
         } else {
-          *(f32x4*)(row + m0) = f32x4{vals[0], vals[1], vals[2], vals[3]};
+          zl2 = raw * kLog2e;
+          slope = 1.f;
+        }
+        const float c = gt * (1.f - exp2_(zl2 - L2)) * slope;
+        if constexpr (SKIP) cmax[mbl >> 1] = fmaxf(cmax[mbl >> 1], fabsf(c));
+        vm_wait();
+        if constexpr (sizeof(T) == 2) {
+          *(uint16_t*)(row + (vw0 - vbase) + o) = (uint16_t)(pack_bf16x2(c, 0.f) & 0xffffu);
+        } else {
+          row[(vw0 - vbase) + o] = c;
         }
       }
+    }
   }
   // Coefficient filter: this wave covers 64 tokens (slice wn of the tile) x 128 vocabulary entries
   // (slices 2 wm, 2 wm + 1); one flag byte per (token block, vocabulary slice, wave) for dh and per

@@ -6,7 +6,10 @@
 
 namespace orpo {
 
-enum : int32_t { kPrefSimpo = 1, kPrefDpo = 2 };
+enum : int32_t { kPrefSimpo = 1, kPrefDpo = 2, kPrefIpo = 3, kPrefHinge = 4 };
+
+// Branch values are length-normalised means for SimPO and IPO, per-sequence sums otherwise.
+__device__ __forceinline__ bool pref_mean(int32_t kind) { return kind == kPrefSimpo || kind == kPrefIpo; }
 
 __device__ __forceinline__ double softplus_d(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 __device__ __forceinline__ double sigmoid_d(double x) {
@@ -60,7 +63,7 @@ __device__ __forceinline__ int span_of(const int32_t* off, int n, int64_t t) {
 }
 
 struct PrefArgs {
-  int32_t kind;           // kPrefSimpo or kPrefDpo
+  int32_t kind;           // kPref*
   int64_t M, V;
   int32_t P;
   const int32_t* off;     // [2P+1]: chosen 2p, rejected 2p+1
@@ -81,8 +84,11 @@ struct PrefArgs {
 // SimPO (Training — design, §8.3 "Objective variants and data"): per pair
 // L = softplus(-beta ((lw - lr) - gamma)) on the length-normalised means. DPO (the post-training
 // design's "Stage P1 — DPO"): Delta = beta [(s_w - ref_w) - (s_r - ref_r)] on per-sequence sums,
-// L = -log sigma(Delta). loss = mean over pairs; g_t = dL/dvalue_s / n_s (SimPO) or dL/dvalue_s
-// (DPO) for a valid token of span s.
+// L = -log sigma(Delta). IPO and hinge/SLiC (named in the same §8.3 without formulas; read as the
+// published losses on the log-ratio margin h = (v_w - ref_w) - (v_r - ref_r), references optional):
+// IPO L = (h - 1/(2 beta))^2 on the means, hinge L = max(0, 1 - beta h) on the sums (zero
+// gradient at the kink). loss = mean over pairs; g_t = dL/dvalue_s / n_s (means) or dL/dvalue_s
+// (sums) for a valid token of span s.
 __global__ __launch_bounds__(1024) void pref_loss_kernel(PrefArgs a) {
   __shared__ int bad;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, ns = 2 * a.P;
@@ -98,27 +104,44 @@ __global__ __launch_bounds__(1024) void pref_loss_kernel(PrefArgs a) {
     span_sum(a.off, s, a.logp, a.labels, a.ignore_index, a.V, &sum, &n);
     if (l == 0) {
       a.cnt[s] = n;
-      a.val[s] = n == 0 ? nan : (a.kind == kPrefSimpo ? sum / (double)n : sum);
+      a.val[s] = n == 0 ? nan : (pref_mean(a.kind) ? sum / (double)n : sum);
       if (n == 0) atomicOr(a.status, kStatusEmptyBranch);
     }
   }
   __syncthreads();
   for (int p = tid; p < a.P; p += 1024) {
     const double vw = a.val[2 * p], vr = a.val[2 * p + 1];
-    double u, margin, acc;
+    double lp, d, margin, acc;
     if (a.kind == kPrefSimpo) {
-      u = a.beta * ((vw - vr) - a.gamma);
+      const double u = a.beta * ((vw - vr) - a.gamma);
+      lp = softplus_d(-u);
+      d = -a.beta * sigmoid_d(-u) / (double)a.P;
       margin = vw - vr;
       acc = vw > vr ? 1.0 : 0.0;
     } else {
-      u = a.beta * ((vw - a.ref[2 * p]) - (vr - a.ref[2 * p + 1]));
-      margin = u;
-      acc = u > 0 ? 1.0 : 0.0;
+      const double rw = a.ref ? a.ref[2 * p] : 0.0, rr = a.ref ? a.ref[2 * p + 1] : 0.0;
+      const double hm = (vw - rw) - (vr - rr);
+      if (a.kind == kPrefDpo) {
+        const double u = a.beta * hm;
+        lp = softplus_d(-u);
+        d = -a.beta * sigmoid_d(-u) / (double)a.P;
+        margin = u;
+      } else if (a.kind == kPrefIpo) {
+        const double e = hm - 1.0 / (2.0 * a.beta);
+        lp = e * e;
+        d = 2.0 * e / (double)a.P;
+        margin = hm;
+      } else {
+        const double u = 1.0 - a.beta * hm;
+        lp = u > 0 ? u : 0.0;
+        d = u > 0 ? -a.beta / (double)a.P : 0.0;
+        margin = hm;
+      }
+      acc = hm > 0 ? 1.0 : 0.0;
     }
-    const double d = -a.beta * sigmoid_d(-u) / (double)a.P;
     a.dv[2 * p] = d;
     a.dv[2 * p + 1] = -d;
-    a.pair[p] = softplus_d(-u);
+    a.pair[p] = lp;
     a.pair[a.P + p] = acc;
     a.pair[2 * a.P + p] = margin;
     a.out[3 + p] = vw;
@@ -141,7 +164,7 @@ __global__ __launch_bounds__(1024) void pref_loss_kernel(PrefArgs a) {
     const int y = a.labels[t];
     if (t >= a.off[0] && t < a.off[ns] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
       const int s = span_of(a.off, ns, t);
-      gv = (float)(a.kind == kPrefSimpo ? a.dv[s] / (double)a.cnt[s] : a.dv[s]);
+      gv = (float)(pref_mean(a.kind) ? a.dv[s] / (double)a.cnt[s] : a.dv[s]);
     }
     a.g[t] = gv;
   }

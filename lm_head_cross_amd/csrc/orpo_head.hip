@@ -72,6 +72,8 @@ struct TraceScope {
   }
 };
 
+constexpr float kMaxSoftcap = 40.f;
+
 // Format combinations this build implements.
 enum Kind { kF32, kBf16, kQ4, kBad };
 
@@ -81,6 +83,9 @@ orpo_status check_desc(const orpo_head_desc* d, Kind* kind) {
   if (d->V > INT32_MAX || d->M > INT32_MAX || d->d > (int64_t(1) << 20)) return ORPO_EUNSUPPORTED;
   if ((d->flags & ~uint32_t(ORPO_DW_ACCUMULATE)) != 0) return ORPO_EINVAL;
   if (!(d->softcap <= 0.f || d->softcap > 0.f)) return ORPO_EINVAL;   // NaN
+  // The softcapped kernels sum 2^((z - softcap) log2 e) with z >= -softcap: every term stays a
+  // normal float while 2 softcap log2 e < 126, and the backward's per-token factor likewise.
+  if (d->softcap > kMaxSoftcap) return ORPO_EUNSUPPORTED;
   Kind k = kBad;
   if (d->h_fmt == ORPO_F32 && d->w_fmt == ORPO_F32) k = kF32;
   else if (d->h_fmt == ORPO_BF16 && d->w_fmt == ORPO_BF16) k = kBf16;
@@ -311,12 +316,13 @@ orpo_status orpo_pref_loss(int32_t kind, int64_t M, int32_t n_pairs, const int32
                            const float* logp, const int32_t* labels, int64_t V,
                            int32_t ignore_index, double beta, double gamma, const double* ref_sums,
                            double* out, float* g, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (kind != ORPO_PREF_SIMPO && kind != ORPO_PREF_DPO) return ORPO_EINVAL;
+  if (kind < ORPO_PREF_SIMPO || kind > ORPO_PREF_HINGE) return ORPO_EINVAL;
   if (M < 0 || M > INT32_MAX || n_pairs < 1 || n_pairs > INT32_MAX / 2 || V <= 0 || V > INT32_MAX)
     return ORPO_EINVAL;
   if (!seg_offsets || !out || (M > 0 && (!logp || !labels || !g))) return ORPO_EINVAL;
   if (kind == ORPO_PREF_DPO && !ref_sums) return ORPO_EINVAL;
   if (!(beta == beta) || !(gamma == gamma)) return ORPO_EINVAL;
+  if (kind == ORPO_PREF_IPO && !(beta > 0.0)) return ORPO_EINVAL;
   if (!ws || ws_bytes < orpo_objective_workspace_bytes(M, 2 * n_pairs) || (uintptr_t)ws % 256)
     return ORPO_ENOWS;
   PrefArgs a;

@@ -226,13 +226,14 @@ def trace_collect() -> dict:
 # ------------------------------------------------------------------------------------------------
 # A preallocated head step: fwd -> loss -> bwd with every buffer and workspace allocated once.
 # ------------------------------------------------------------------------------------------------
-PREF_KINDS = {"simpo": 1, "dpo": 2}
+PREF_KINDS = {"simpo": 1, "dpo": 2, "ipo": 3, "hinge": 4}
 
 
 def pref_loss(kind, logp, labels, seg_offsets, V, beta, gamma=0.0, ref_sums=None,
               ignore_index=IGNORE_INDEX, return_ws=False):
-    """SimPO ("simpo": mean log-probs, margin gamma) or DPO ("dpo": sequence sums against the cached
-    reference sums ref_sums [2P] float64) over chosen/rejected spans seg_offsets [2P+1].
+    """SimPO ("simpo": mean log-probs, margin gamma), DPO ("dpo": sequence sums against the cached
+    reference sums ref_sums [2P] float64), IPO ("ipo": means, optional reference means) or hinge
+    ("hinge": sums, optional reference sums) over chosen/rejected spans seg_offsets [2P+1].
     Returns out (float64 [3 + 2P]: loss, accuracy, margin, chosen values, rejected values), g."""
     _need_gpu(logp, labels, seg_offsets, ref_sums)
     M = logp.shape[0]
@@ -273,7 +274,7 @@ class HeadStep:
 
         objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
         backward, with its parameters and inputs in `obj`: "simpo" {beta, gamma}, "dpo" {beta,
-        ref_sums [2P] float64}, "grpo" {clip_eps, beta, old_logp [M], ref_logp [M], advantages [S]
+        ref_sums [2P] float64}, "ipo" / "hinge" {beta, optional ref_sums}, "grpo" {clip_eps, beta, old_logp [M], ref_logp [M], advantages [S]
         float32, seg_offsets are then [S+1] completions}."""
         _need_gpu(h, w, labels, seg_offsets, scales, biases)
         self.h, self.w, self.labels, self.off = h, w, labels, seg_offsets

@@ -53,6 +53,8 @@ def test_workspace_sizes():
     (dict(M=-1), EINVAL),
     (dict(V=0), EINVAL),
     (dict(flags=8), EINVAL),
+    (dict(cap=float("nan")), EINVAL),
+    (dict(cap=40.5), EUNSUP),                 # beyond the softcap range the kernels support
 ])
 def test_fwd_rejects_bad_descriptors(kw, code):
     L = H.lib()
@@ -114,7 +116,11 @@ def test_objective_entry_points_reject_bad_arguments():
     assert L.orpo_objective_workspace_bytes(100, 0) == 0
     ws = 1 << 20
     # kind, M, P, off, logp, labels, V, ignore, beta, gamma, ref, out, g, ws, bytes, stream
-    assert L.orpo_pref_loss(3, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, 16, 16, 16, ws, 4096, None) == EINVAL
+    for kind in (0, 5):
+        assert L.orpo_pref_loss(kind, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, 16, 16, 16, ws, 4096, None) == EINVAL
+    for beta in (0.0, -0.5):   # IPO's target margin 1/(2 beta) needs beta > 0
+        assert L.orpo_pref_loss(3, 10, 1, 16, 16, 16, 100, -100, beta, 0.0, None, 16, 16, ws, 4096, None) == EINVAL
+    assert L.orpo_pref_loss(4, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, None, 16, 16, ws, 16, None) == ENOWS
     assert L.orpo_pref_loss(2, 10, 1, 16, 16, 16, 100, -100, 0.1, 0.0, None, 16, 16, ws, 4096, None) == EINVAL
     assert L.orpo_pref_loss(1, 10, 0, 16, 16, 16, 100, -100, 0.1, 0.0, None, 16, 16, ws, 4096, None) == EINVAL
     assert L.orpo_pref_loss(1, 10, 1, 16, 16, 16, 100, -100, float("nan"), 0.0, None, 16, 16, ws, 4096, None) == EINVAL

@@ -1,4 +1,4 @@
-"""GPU parity for the sibling objectives (SimPO, DPO, GRPO) that reuse the head's forward and
+"""GPU parity for the sibling objectives (SimPO, DPO, IPO, hinge, GRPO) that reuse the head's forward and
 backward: their float64 epilogues on the GPU's own log-probs against the oracle's, and a whole
 forward -> objective -> backward step against the oracle's. Inputs the objectives need beyond the
 head's (reference sums, the sampling and reference policies' log-probs, advantages) are drawn from
@@ -51,21 +51,43 @@ def _backward_parity(pb, h, w, lab, lse, g_gpu, g_ref, label):
     assert e_dh <= TOL_GRAD and e_dW <= TOL_GRAD
 
 
-@pytest.mark.parametrize("kind", ["simpo", "dpo"])
-def test_pairwise_objective_step(kind):
+def _oracle_pair(kind, sums, n, ref, beta, gamma):
+    """The oracle's epilogue for `kind` on span sums/counts; returns (epilogue, branch values)."""
+    means = sums / n
+    if kind == "simpo":
+        return ob.simpo_epilogue(means[0::2], means[1::2], beta, gamma), means
+    r = np.zeros_like(sums) if ref is None else ref
+    if kind == "ipo":
+        return ob.ipo_epilogue(means[0::2], means[1::2], r[0::2], r[1::2], beta), means
+    if kind == "hinge":
+        return ob.hinge_epilogue(sums[0::2], sums[1::2], r[0::2], r[1::2], beta), sums
+    return ob.dpo_epilogue(sums[0::2], sums[1::2], r[0::2], r[1::2], beta), sums
+
+
+@pytest.mark.parametrize("kind,with_ref", [("simpo", False), ("dpo", True), ("ipo", True),
+                                           ("ipo", False), ("hinge", True), ("hinge", False)])
+def test_pairwise_objective_step(kind, with_ref):
     d = dev()
-    pb = _problem(700, 192, 3001, 30.0, seed=41 if kind == "dpo" else 42, n_spans=6)
-    say(f"[case] {kind} M=700 d=192 V=3001")
+    seed = {"simpo": 42, "dpo": 41, "ipo": 43, "hinge": 44}[kind] + (10 if with_ref else 0)
+    pb = _problem(700, 192, 3001, 30.0, seed=seed, n_spans=6)
+    say(f"[case] {kind} ref={with_ref} M=700 d=192 V=3001")
     h, w, lab, logp, lse = _gpu_logp(pb)
     off_t = torch.from_numpy(pb["off"]).to(d)
     sums_o, n = ob.span_stats(pb["logp"], pb["labels"], pb["off"])
-    if kind == "simpo":
-        beta, gamma, ref = 2.0, 0.3, None
-        ep_o = ob.simpo_epilogue(sums_o[0::2] / n[0::2], sums_o[1::2] / n[1::2], beta, gamma)
-    else:
-        beta, gamma = 0.1, 0.0
-        ref = sums_o + pb["rng"].normal(0.0, 3.0, size=sums_o.shape)     # cached reference sums
-        ep_o = ob.dpo_epilogue(sums_o[0::2], sums_o[1::2], ref[0::2], ref[1::2], beta)
+    beta, gamma = {"simpo": (2.0, 0.3), "dpo": (0.1, 0.0), "ipo": (0.5, 0.0),
+                   "hinge": (0.2, 0.0)}[kind]
+    if kind == "hinge" and not with_ref:
+        beta = 1e-3   # reference-free sums differ by ~1e3 here: a mix of sloped and flat pairs
+    ref = None
+    if with_ref:
+        # Cached reference values of the objective's kind: noise around the oracle's own.
+        scale = {"dpo": 3.0, "hinge": 3.0, "ipo": 0.2}[kind]
+        base = sums_o / n if kind in ob.MEAN_KINDS else sums_o
+        ref = base + pb["rng"].normal(0.0, scale, size=sums_o.shape)
+    ep_o, _ = _oracle_pair(kind, sums_o, n, ref, beta, gamma)
+    if kind == "hinge":   # every pair away from the kink (the two sides' g differ), both sides used
+        u = 1.0 - beta * ep_o["h"]
+        assert np.min(np.abs(u)) > 1e-2 and np.any(u > 0), u
     ref_t = None if ref is None else torch.from_numpy(ref).to(d)
     out, g, ws = H.pref_loss(kind, logp, lab, off_t, pb["V"], beta, gamma, ref_sums=ref_t,
                              return_ws=True)
@@ -73,7 +95,8 @@ def test_pairwise_objective_step(kind):
     assert H.read_status(ws) == 0
     o = out.cpu().numpy()
     g_o = ob.pairwise_cotangent(kind, ep_o, n, pb["labels"], pb["off"])
-    errs = {"loss": abs(o[0] - ep_o["loss"]) / abs(ep_o["loss"]), "g": rel(g.cpu().numpy(), g_o),
+    errs = {"loss": abs(o[0] - ep_o["loss"]) / max(abs(ep_o["loss"]), 1e-12),
+            "g": rel(g.cpu().numpy(), g_o),
             "margin": abs(o[2] - ep_o["margin"]) / max(1.0, abs(ep_o["margin"]))}
     say(f"[objective {kind}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     assert errs["loss"] <= TOL_SCALAR and errs["g"] <= TOL_SCALAR and errs["margin"] <= TOL_SCALAR
@@ -82,12 +105,7 @@ def test_pairwise_objective_step(kind):
     # The float64 epilogue on the GPU's own logp vector, against the oracle's on the same vector.
     lv = logp.cpu().numpy().astype(np.float64)
     sums, n2 = ob.span_stats(lv, pb["labels"], pb["off"])
-    if kind == "simpo":
-        ep = ob.simpo_epilogue(sums[0::2] / n2[0::2], sums[1::2] / n2[1::2], beta, gamma)
-        vals = sums / n2
-    else:
-        ep = ob.dpo_epilogue(sums[0::2], sums[1::2], ref[0::2], ref[1::2], beta)
-        vals = sums
+    ep, vals = _oracle_pair(kind, sums, n2, ref, beta, gamma)
     for i, k in enumerate(("loss", "accuracy", "margin")):
         assert abs(o[i] - ep[k]) <= 1e-12 * max(1.0, abs(ep[k])), k
     assert np.allclose(o[3:6], vals[0::2], rtol=1e-12) and np.allclose(o[6:9], vals[1::2], rtol=1e-12)
