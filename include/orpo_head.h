@@ -252,8 +252,10 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
                           hipStream_t stream);
 
 /* Backward tiling: the token chunk C (a multiple of 256, default 8192) and the byte budget of one
- * coefficient tile [C, BVb] (default 256 MiB, two are used; BVb is the largest multiple of 256
- * that fits, at least 256). 0 restores a default. Process-wide; call it only while no call of this library is in
+ * coefficient tile [C, BVb] (two are used). With a budget, BVb is the largest multiple of 256 that
+ * fits (at least 256). By default (0) the budget is 256 MiB and BVb is further limited to
+ * max(16384, V/8 rounded up to 256) (and never above V), so that a small vocabulary still
+ * pipelines over several blocks. 0 restores a default. Process-wide; call it only while no call of this library is in
  * flight, and size workspaces after it. Returns ORPO_EINVAL for a chunk that is not a multiple of
  * 256 or a negative value. */
 orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes);

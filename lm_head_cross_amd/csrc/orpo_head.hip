@@ -18,11 +18,16 @@ using namespace orpo;
 thread_local int32_t g_last_hip = 0;
 
 constexpr size_t kHeader = 256;                     // status word + padding at the start of a workspace
-constexpr int kTargetWorkgroups = 512;              // forward grid target (2 rounds on 256 CUs)
+constexpr int kTargetWorkgroups = 256;              // forward grid target (one round on 256 CUs)
 constexpr int64_t kChunkDefault = 8192;             // backward token chunk C (multiple of 256)
-constexpr size_t kCoeffDefault = size_t(256) << 20; // bytes of the backward coefficient tile
+// Default coefficient block: the largest that fits 256 MiB per coefficient buffer, but no wider
+// than an eighth of the vocabulary (rounded up to 256) unless that is under 16384 rows, so that a
+// small vocabulary still pipelines over several items (the first launch's coefficients and the
+// last one's dh/dW share the GPU with nothing).
+constexpr int64_t kBvItems = 8, kBvMin = 16384;
+constexpr size_t kCoeffDefault = size_t(256) << 20;
 int64_t g_chunk = kChunkDefault;
-size_t g_coeff_budget = kCoeffDefault;
+size_t g_coeff_budget = 0;                          // 0: the default block rule above
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
@@ -140,8 +145,10 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
   BwdPlan p;
   const int64_t esize = k == kF32 ? 4 : 2;
   p.C = std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), kTile) * kTile, g_chunk);
-  const int64_t by_budget = std::max<int64_t>(kTile, int64_t(g_coeff_budget) / (p.C * esize) / kTile * kTile);
-  p.BVb = std::min<int64_t>(cdiv(d->V, kTile) * kTile, by_budget);
+  const size_t budget = g_coeff_budget ? g_coeff_budget : kCoeffDefault;
+  int64_t bv = std::max<int64_t>(kTile, int64_t(budget) / (p.C * esize) / kTile * kTile);
+  if (!g_coeff_budget) bv = std::min(bv, std::max(kBvMin, cdiv(cdiv(d->V, kBvItems), kTile) * kTile));
+  p.BVb = std::min<int64_t>(cdiv(d->V, kTile) * kTile, bv);
   // With the coefficient filter: per buffer, dh flags [C/256][BVb/64][4 waves] and dW flags
   // [BVb/256][C/64][2 waves], one byte each.
   p.fl_bytes = d->skip_eps > 0.f
@@ -474,7 +481,7 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
 orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes) {
   if (chunk_tokens < 0 || chunk_tokens % kTile != 0) return ORPO_EINVAL;
   g_chunk = chunk_tokens ? chunk_tokens : kChunkDefault;
-  g_coeff_budget = coeff_bytes ? coeff_bytes : kCoeffDefault;
+  g_coeff_budget = coeff_bytes;
   return ORPO_OK;
 }
 

@@ -35,7 +35,7 @@ def test_workspace_sizes():
     d = _desc(M=8192, d=2560, V=262144)
     fws = L.orpo_head_fwd_workspace_bytes(ctypes.byref(d))
     bws = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
-    assert fws == 256 + 16 * 8192 * 8          # 16 vocabulary splits of 64 tiles, float2 each
+    assert fws == 256 + 8 * 8192 * 8           # 8 vocabulary splits of 128 tiles, float2 each
     assert bws == 256 + 2 * 8192 * 16384 * 2   # two 256 MiB bf16 coefficient tiles
     # The backward workspace does not grow with M past one chunk.
     d2 = _desc(M=32768, d=2560, V=262144)
@@ -43,6 +43,15 @@ def test_workspace_sizes():
     assert L.orpo_loss_workspace_bytes(100, 4) == 256 + 512
     assert L.orpo_loss_workspace_bytes(100, 0) == 0
     assert L.orpo_head_fwd_workspace_bytes(ctypes.byref(_desc(d=100))) == 0
+    # Default block rule: the 256 MiB budget, and no wider than max(16384, V/8 rounded up to 256)
+    # nor than V. (M, V) -> BVb:
+    for M, V, bv in ((8192, 73448, 16384), (4096, 73448, 16384), (2048, 150000, 18944),
+                     (8192, 1 << 20, 16384), (2048, 1 << 20, 65536), (8192, 4096, 4096)):
+        dv = _desc(M=M, d=1536, V=V)
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(dv)) == 256 + 2 * M * bv * 2, (M, V)
+    # fp32 coefficients: the budget binds first.
+    df = _desc(M=8192, d=256, V=262144, h=H.ORPO_F32, w=H.ORPO_F32)
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(df)) == 256 + 2 * 8192 * 8192 * 4
 
 
 @pytest.mark.parametrize("kw,code", [

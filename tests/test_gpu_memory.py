@@ -44,6 +44,6 @@ def test_peak_memory_flat_in_M():
         torch.cuda.empty_cache()
     # The backward workspace is constant once M reaches one token chunk (8192).
     assert rows[1][1] == rows[2][1]
-    # The forward partials ([NBLK, M] with NBLK * (M / 256) ~ 512 workgroups) stay ~1 MiB here and
+    # The forward partials ([NBLK, M] with NBLK * (M / 256) ~ 256 workgroups) stay ~1 MiB here and
     # grow at most linearly with M (like lse).
     assert rows[2][2] <= 2 * rows[1][2]

@@ -136,18 +136,24 @@ def test_cold_tile_skip_is_exact_for_the_filter_and_skips_tiles():
     off = torch.from_numpy(inp.seg_offsets).to(d)
     logp, lse, fws = H.head_fwd(h, w, lab, cfg.softcap, return_ws=True, skip_eps=eps)
     _, g = H.orpo_loss(logp, lab, off, cfg.V, cfg.lam)
-    dh0, dW0 = H.head_bwd(h, w, lab, lse, g, cfg.softcap, skip_eps=eps)             # filter only
     desc = H.make_desc(cfg.M, cfg.d, cfg.V, h.dtype, H._w_fmt(w, None), cfg.softcap, skip_eps=eps)
     L = H.lib()
-    nbytes = L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc))
-    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=d)
-    dh = torch.empty_like(dh0)
-    dW = torch.empty_like(dW0)
-    st = L.orpo_head_bwd(ctypes.byref(desc), H._ptr(h), H.Weight(w.data_ptr(), None, None),
-                         H._ptr(lab), H._ptr(lse), H._ptr(g), H._ptr(dh), H._ptr(dW),
-                         H._ptr(ws), nbytes, H._ptr(fws), H._stream(d))
-    assert st == 0
-    torch.cuda.synchronize()
+    # One backward item (the whole [1024, 65536] coefficient block in buffer 0) for both runs, so
+    # that the layout read below holds and both sum dh in the same order.
+    assert L.orpo_set_bwd_tiling(0, 1024 * 65536 * 2) == 0
+    try:
+        dh0, dW0 = H.head_bwd(h, w, lab, lse, g, cfg.softcap, skip_eps=eps)         # filter only
+        nbytes = L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc))
+        ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=d)
+        dh = torch.empty_like(dh0)
+        dW = torch.empty_like(dW0)
+        st = L.orpo_head_bwd(ctypes.byref(desc), H._ptr(h), H.Weight(w.data_ptr(), None, None),
+                             H._ptr(lab), H._ptr(lse), H._ptr(g), H._ptr(dh), H._ptr(dW),
+                             H._ptr(ws), nbytes, H._ptr(fws), H._stream(d))
+        assert st == 0
+        torch.cuda.synchronize()
+    finally:
+        assert L.orpo_set_bwd_tiling(0, 0) == 0
     assert torch.equal(dh, dh0) and torch.equal(dW, dW0)
     # One item here (C = 1024 tokens, BVb = 65536): buffer 0 holds its [1024, 65536] coefficients.
     coeff = ws[256:256 + 1024 * 65536 * 2].view(torch.int16).view(1024, 65536)
