@@ -57,7 +57,8 @@ enum {
 
 /* Option bits of orpo_head_desc.flags. */
 enum {
-  ORPO_DW_ACCUMULATE = 1u << 0      /* orpo_head_bwd adds into dW instead of overwriting it */
+  ORPO_DW_ACCUMULATE = 1u << 0,     /* orpo_head_bwd adds into dW instead of overwriting it */
+  ORPO_DH_BF16 = 1u << 1            /* orpo_head_bwd writes dh as bf16 (bf16 and 4-bit heads)  */
 };
 
 typedef struct {
@@ -70,7 +71,7 @@ typedef struct {
                         /* (ORPO_EUNSUPPORTED above: the kernels' fixed softmax reference     */
                         /* keeps every term a normal float only up to there)                   */
   int32_t ignore_index; /* label value of ignored / padding tokens (conventionally -100)        */
-  uint32_t flags;       /* ORPO_DW_ACCUMULATE                                                   */
+  uint32_t flags;       /* ORPO_DW_ACCUMULATE | ORPO_DH_BF16                                    */
   float skip_eps;       /* backward coefficient filter: 0 = exact backward; > 0 (bf16 and 4-bit
                          * heads only) drops from dh every 256-token x 64-entry coefficient block,
                          * and from dW every 256-entry x 64-token block, whose max |coeff| < skip_eps
@@ -237,7 +238,13 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  *   h, W, labels   as for orpo_head_fwd
  *   lse            (device) float [M] from orpo_head_fwd on the same h, W, labels
  *   g              (device) float [M] dloss/dlogp (e.g. from orpo_loss); ignored tokens must hold 0
- *   dh             (device) float [M,d] out (overwritten)
+ *   dh             (device) float [M,d] out (overwritten); with ORPO_DH_BF16 bf16 [M,d]: the
+ *                  same fp32 sums, rounded to nearest even once (the workspace then also holds an
+ *                  fp32 [C,d] accumulator when V spans several backward blocks; ORPO_EUNSUPPORTED
+ *                  for fp32 heads). The sum over vocabulary blocks stays fp32 either way: the
+ *                  pages found bf16 summation across blocks to be the dominant gradient error
+ *                  ("ORPO training — design", "Memory & speed optimization", the vocab-blocked
+ *                  note).
  *   dW             (device) float [V,d] out (overwritten, or accumulated with ORPO_DW_ACCUMULATE);
  *                  NULL computes dh only. Must be NULL for ORPO_Q4G64 (a quantised head is frozen).
  *   ws             (device) >= orpo_head_bwd_workspace_bytes(desc) bytes
@@ -247,7 +254,7 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  *   then traced with the exact method's work (skipped blocks included).
  */
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
-                          const int32_t* labels, const float* lse, const float* g, float* dh,
+                          const int32_t* labels, const float* lse, const float* g, void* dh,
                           float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
                           hipStream_t stream);
 

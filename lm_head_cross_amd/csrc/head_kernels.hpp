@@ -407,6 +407,7 @@ struct BwdItem {
   int32_t n_vt, n_tt;     // 256-tiles along vocabulary and tokens
   int32_t n_dh;           // dh tiles (GEMM item); dW tiles are n_tiles - n_dh
   int32_t dh_first, dw_first;
+  int32_t dh_last;        // the chunk's last vocabulary block (bf16 dh is written then)
 };
 
 struct BwdArgs {
@@ -416,7 +417,9 @@ struct BwdArgs {
   const int32_t* labels;
   const float* lse;
   const float* g;
-  float* dh;              // [M, d]
+  float* dh;              // [M, d] fp32, or null when dh16 is set
+  uint16_t* dh16;         // [M, d] bf16 output (ORPO_DH_BF16), else null
+  float* dh_acc;          // [C, d] fp32 accumulator of the chunk for bf16 dh over several blocks
   float* dW;              // [V, d] or null
   int64_t M, d, V;
   int64_t BVb;            // row pitch of a coefficient buffer (elements)
@@ -668,6 +671,30 @@ __device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, 
   }
 }
 
+// bf16 output of an fp32 tile: out16 = bf16(acc + prev) (prev: the chunk's fp32 accumulator rows,
+// or nothing on the first block), rounded to nearest even once.
+__device__ __forceinline__ void store_out_bf16(uint16_t* out16, const float* prev, int64_t ld,
+                                               int64_t row0, int64_t prow0, int64_t n_rows,
+                                               int64_t col0, int64_t n_cols,
+                                               const f32x16 (&acc)[4][2]) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int64_t col = col0 + acc_n(wn, nb, l);
+    if (col >= n_cols) continue;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = acc_m(wm, mb, r, l);
+        if (row0 + m < n_rows) {
+          const float v = prev ? prev[(prow0 + m) * ld + col] + acc[mb][nb][r] : acc[mb][nb][r];
+          out16[(row0 + m) * ld + col] = (uint16_t)(pack_bf16x2(v, 0.f) & 0xffffu);
+        }
+      }
+  }
+}
+
 // Phase 2a: dh[c0 + i][j] (+)= sum_v coeff[i][v] W[v0 + v][j]   (m = token, n = hidden, k = vocabulary)
 template <class E, bool Q4, bool SKIP>
 __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid,
@@ -706,8 +733,15 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   auto nop = [](int, f32x16(&)[4][2]) {};
   gemm_run<E, true, false, false>(smem, 1, n_run, issue, commit, nop, acc);
   (void)tid;
-  if (n_run > 0 || it.dh_first)
-    store_out<E>(a.dh, a.d, it.c0 + i0, t_end, j0, a.d, it.dh_first != 0, acc);
+  if (!a.dh16) {
+    if (n_run > 0 || it.dh_first)
+      store_out<E>(a.dh, a.d, it.c0 + i0, t_end, j0, a.d, it.dh_first != 0, acc);
+  } else if (it.dh_last) {   // bf16 dh: sum in fp32 over the chunk's blocks, round once at the end
+    store_out_bf16(a.dh16, it.dh_first ? nullptr : a.dh_acc, a.d, it.c0 + i0, i0, t_end, j0, a.d,
+                   acc);
+  } else if (n_run > 0 || it.dh_first) {
+    store_out<E>(a.dh_acc, a.d, i0, t_end - it.c0, j0, a.d, it.dh_first != 0, acc);
+  }
 }
 
 // Phase 2b: dW[v0 + v][j] (+)= sum_i coeff[i][v] h[c0 + i][j]   (m = vocabulary, n = hidden, k = token)

@@ -86,7 +86,7 @@ orpo_status check_desc(const orpo_head_desc* d, Kind* kind) {
   if (!d) return ORPO_EINVAL;
   if (d->M < 0 || d->d <= 0 || d->V <= 0) return ORPO_EINVAL;
   if (d->V > INT32_MAX || d->M > INT32_MAX || d->d > (int64_t(1) << 20)) return ORPO_EUNSUPPORTED;
-  if ((d->flags & ~uint32_t(ORPO_DW_ACCUMULATE)) != 0) return ORPO_EINVAL;
+  if ((d->flags & ~uint32_t(ORPO_DW_ACCUMULATE | ORPO_DH_BF16)) != 0) return ORPO_EINVAL;
   if (!(d->softcap <= 0.f || d->softcap > 0.f)) return ORPO_EINVAL;   // NaN
   // The softcapped kernels sum 2^((z - softcap) log2 e) with z >= -softcap: every term stays a
   // normal float while 2 softcap log2 e < 126, and the backward's per-token factor likewise.
@@ -137,6 +137,7 @@ FwdPlan plan_fwd(const orpo_head_desc* d) {
 
 struct BwdPlan {
   int64_t C, BVb;
+  size_t dh_acc_bytes;   // fp32 [C, d] chunk accumulator for bf16 dh over several blocks (else 0)
   size_t fl_bytes;   // skip flags per coefficient buffer (0 without the coefficient filter)
   size_t ws;
 };
@@ -155,7 +156,10 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
                    ? round_up(size_t(p.C / kTile) * size_t(p.BVb / 64) * 4 +
                                   size_t(p.BVb / kTile) * size_t(p.C / 64) * 2, 256)
                    : 0;
-  p.ws = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize) + 2 * p.fl_bytes;
+  p.dh_acc_bytes = (d->flags & ORPO_DH_BF16) && cdiv(d->V, p.BVb) > 1
+                       ? round_up(size_t(p.C) * size_t(d->d) * sizeof(float), 256)
+                       : 0;
+  p.ws = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize) + 2 * p.fl_bytes + p.dh_acc_bytes;
   return p;
 }
 
@@ -212,6 +216,7 @@ size_t orpo_head_fwd_workspace_bytes(const orpo_head_desc* desc) {
 size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc) {
   Kind k;
   if (check_desc(desc, &k) != ORPO_OK) return 0;
+  if ((desc->flags & ORPO_DH_BF16) && k == kF32) return 0;   // unsupported
   return plan_bwd(desc, k).ws;
 }
 
@@ -397,7 +402,7 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
 }
 
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
-                          const int32_t* labels, const float* lse, const float* g, float* dh,
+                          const int32_t* labels, const float* lse, const float* g, void* dh,
                           float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
                           hipStream_t stream) {
   Kind k;
@@ -405,6 +410,7 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   if (st != ORPO_OK) return st;
   if ((st = check_weight(k, W)) != ORPO_OK) return st;
   if (k == kQ4 && dW) return ORPO_EUNSUPPORTED;
+  if ((desc->flags & ORPO_DH_BF16) && k == kF32) return ORPO_EUNSUPPORTED;
   const BwdPlan p = plan_bwd(desc, k);
   if (!ws || ws_bytes < p.ws || (uintptr_t)ws % 256) return ORPO_ENOWS;
   if (desc->M == 0) return ORPO_OK;
@@ -417,7 +423,10 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.labels = labels;
   a.lse = lse;
   a.g = g;
-  a.dh = dh;
+  const bool dh_bf16 = (desc->flags & ORPO_DH_BF16) != 0;
+  a.dh = dh_bf16 ? nullptr : (float*)dh;
+  a.dh16 = dh_bf16 ? (uint16_t*)dh : nullptr;
+  a.dh_acc = p.dh_acc_bytes ? (float*)((char*)ws + p.ws - p.dh_acc_bytes) : nullptr;
   a.dW = dW;
   a.M = desc->M;
   a.d = desc->d;
@@ -457,6 +466,7 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
     it.n_vt = (int)cdiv(it.BV_cur, kTile);
     it.n_tt = (int)cdiv(it.C_cur, kTile);
     it.dh_first = blk == 0;
+    it.dh_last = blk == n_blocks - 1;
     it.dw_first = c == 0 && !acc_dw;
     if (gemm) {
       it.n_dh = it.n_tt * a.n_jt;

@@ -14,6 +14,7 @@ import torch
 
 ORPO_F32, ORPO_BF16, ORPO_Q4G64 = 0, 1, 2
 ORPO_DW_ACCUMULATE = 1
+ORPO_DH_BF16 = 2
 STATUS_BITS = {1: "bad label", 2: "empty branch", 4: "bad segment offsets"}
 IGNORE_INDEX = -100
 
@@ -177,18 +178,20 @@ def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, retu
 
 
 def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNORE_INDEX,
-             scales=None, biases=None, dW=None, accumulate=False, skip_eps=0.0, fwd_ws=None):
-    """dh[M,d] and dW[V,d] (float32; dW None when want_dW is False). skip_eps > 0 turns on the
-    coefficient filter (an approximation; see orpo_head_desc.skip_eps); fwd_ws, the forward's
-    workspace (head_fwd(..., skip_eps=..., return_ws=True)), adds its exact cold-tile skip."""
+             scales=None, biases=None, dW=None, accumulate=False, skip_eps=0.0, fwd_ws=None,
+             dh_bf16=False):
+    """dh[M,d] and dW[V,d] (float32; dW None when want_dW is False; dh bfloat16 with dh_bf16, the
+    same fp32 sums rounded once). skip_eps > 0 turns on the coefficient filter (an approximation;
+    see orpo_head_desc.skip_eps); fwd_ws, the forward's workspace (head_fwd(..., skip_eps=...,
+    return_ws=True)), adds its exact cold-tile skip."""
     _need_gpu(h, w, labels, lse, g, scales, biases, dW)
     M, d = h.shape
     V = _vocab(w, scales)
-    flags = ORPO_DW_ACCUMULATE if accumulate else 0
+    flags = (ORPO_DW_ACCUMULATE if accumulate else 0) | (ORPO_DH_BF16 if dh_bf16 else 0)
     desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, flags, skip_eps)
     L = lib()
     ws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc)), h.device)
-    dh = torch.empty(M, d, dtype=torch.float32, device=h.device)
+    dh = torch.empty(M, d, dtype=torch.bfloat16 if dh_bf16 else torch.float32, device=h.device)
     if want_dW and dW is None:
         dW = torch.empty(V, d, dtype=torch.float32, device=h.device)
     if not want_dW:

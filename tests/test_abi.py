@@ -62,6 +62,7 @@ def test_workspace_sizes():
     (dict(M=-1), EINVAL),
     (dict(V=0), EINVAL),
     (dict(flags=8), EINVAL),
+    (dict(flags=4), EINVAL),
     (dict(cap=float("nan")), EINVAL),
     (dict(cap=40.5), EUNSUP),                 # beyond the softcap range the kernels support
 ])
@@ -158,6 +159,24 @@ def test_skip_eps_validation_and_workspaces():
     f32 = _desc(h=H.ORPO_F32, w=H.ORPO_F32)
     f32.skip_eps = 1e-5
     assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(f32)) == 0     # unsupported for fp32
+    st = L.orpo_head_bwd(ctypes.byref(f32), 16, H.Weight(16, None, None), 16, 16, 16, 16, 16, 16,
+                         1 << 30, None, None)
+    assert st == EUNSUP
+
+
+def test_dh_bf16_flag_workspace_and_formats():
+    L = H.lib()
+    d = _desc(M=8192, d=2560, V=262144)
+    base = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
+    d.flags = H.ORPO_DH_BF16
+    # Several vocabulary blocks: + the chunk's fp32 dh accumulator [C, d].
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == base + 8192 * 2560 * 4
+    one = _desc(M=1024, d=256, V=4096)
+    b1 = L.orpo_head_bwd_workspace_bytes(ctypes.byref(one))
+    one.flags = H.ORPO_DH_BF16
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(one)) == b1     # one block: no accumulator
+    f32 = _desc(h=H.ORPO_F32, w=H.ORPO_F32, flags=H.ORPO_DH_BF16)
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(f32)) == 0      # unsupported for fp32
     st = L.orpo_head_bwd(ctypes.byref(f32), 16, H.Weight(16, None, None), 16, 16, 16, 16, 16, 16,
                          1 << 30, None, None)
     assert st == EUNSUP

@@ -182,3 +182,45 @@ def test_status_bits_and_nan_outputs():
     o = out.cpu().numpy()
     assert abs(o[0] - ep["loss"]) <= 1e-12 * abs(ep["loss"]) + 1e-13
     assert rel(g.cpu().numpy(), gref) < 1e-6
+
+
+@pytest.mark.parametrize("case", ["one-block", "chunks-blocks", "q4-chunks-blocks", "filter"])
+def test_dh_bf16_is_the_fp32_dh_rounded_once(case):
+    # ORPO_DH_BF16: the same fp32 sums over vocabulary blocks (kept in an fp32 accumulator across
+    # them), rounded to bf16 once, so it equals the fp32 output rounded to nearest even, bit for
+    # bit; dW is unaffected. Checked on one block, on 3 token chunks x 3 vocabulary blocks, with a
+    # 4-bit head, and under the coefficient filter.
+    q4 = case.startswith("q4")
+    inp = _custom(600, 128, 1500, "bf16", 30.0, 0.1, seed=78, q4=q4)
+    say(f"[case] dh bf16 {case}")
+    d = dev()
+    h = inp.h.to(d)
+    if q4:
+        w = torch.from_numpy(inp.wq.view(np.int32)).to(d)
+        sc, bi = inp.scales.to(d), inp.biases.to(d)
+    else:
+        w, sc, bi = inp.w.to(d), None, None
+    labels = torch.from_numpy(inp.labels).to(d)
+    off = torch.from_numpy(inp.seg_offsets).to(d)
+    eps = 1e-6 if case == "filter" else 0.0
+    logp, lse, fws = H.head_fwd(h, w, labels, 30.0, scales=sc, biases=bi, return_ws=True,
+                                skip_eps=eps)
+    _, g = H.orpo_loss(logp, labels, off, 1500, 0.1)
+    if case != "one-block":
+        H.set_bwd_tiling(256, 256 * 512 * 2)
+    try:
+        kw = dict(want_dW=not q4, scales=sc, biases=bi, skip_eps=eps, fwd_ws=fws if eps else None)
+        dh32, dW32 = H.head_bwd(h, w, labels, lse, g, 30.0, **kw)
+        dh16, dW16 = H.head_bwd(h, w, labels, lse, g, 30.0, dh_bf16=True, **kw)
+        torch.cuda.synchronize()
+    finally:
+        H.set_bwd_tiling(0, 0)
+    assert dh16.dtype == torch.bfloat16
+    assert torch.equal(dh16, dh32.to(torch.bfloat16))
+    if not q4:
+        assert torch.equal(dW16, dW32)
+    if case == "chunks-blocks":   # and against the oracle, to the gradient gate
+        ora = run_oracle(inp)
+        e = rel(dh16.float().cpu().numpy(), ora["dh"])
+        say(f"[dh bf16] rel {e:.2e}")
+        assert e <= TOL_GRAD
