@@ -38,6 +38,10 @@ def parse():
                     help="backward coefficient filter threshold (0 = exact backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--mfma-peak", nargs="?", const="both", default=None,
+                    choices=["both", "zeros", "random"],
+                    help="instead of the head: the bf16 MFMA rate this GPU sustains (microbenchmark), "
+                         "with zero and/or random operands")
     return ap.parse_args()
 
 
@@ -125,12 +129,64 @@ def cpu_baseline(inp, rows: int, objective: str):
     }
 
 
+def mfma_peak(which: str = "both"):
+    """The bf16 MFMA rate the GPU sustains with independent back-to-back 32x32x16 MFMAs on every
+    SIMD (no memory traffic), with zero and with random operands: the achievable ceiling at the
+    clock the chip runs, beside the 2.5 PFLOP/s nominal figure. Prints one JSON line."""
+    import ctypes
+    import torch
+    from lm_head_cross_amd import build as B
+
+    if not os.path.exists(B.PEAK_LIB):
+        raise RuntimeError(f"{B.PEAK_LIB} is missing: run lm_head_cross_amd/build.py first")
+    L = ctypes.CDLL(B.PEAK_LIB)
+    L.mfma_peak_run.restype = ctypes.c_int
+    L.mfma_peak_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    n_wg, iters = 512, 500                # 2 rounds of one workgroup per CU, ~0.5 s at 2 PFLOP/s
+    flop = n_wg * 8 * iters * 8 * 32768.0
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    res = {}
+    kinds = {"zeros": lambda: torch.zeros(128 * 8, dtype=torch.bfloat16, device=dev),
+             "random": lambda: torch.randn(128 * 8, device=dev, generator=g).to(torch.bfloat16)}
+    for name in (["zeros", "random"] if which == "both" else [which]):
+        src = kinds[name]()
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        for _ in range(2):   # warm-up
+            assert L.mfma_peak_run(n_wg, iters, ctypes.c_void_p(src.data_ptr()),
+                                   ctypes.c_void_p(out.data_ptr()), stream) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 5
+        for _ in range(reps):
+            assert L.mfma_peak_run(n_wg, iters, ctypes.c_void_p(src.data_ptr()),
+                                   ctypes.c_void_p(out.data_ptr()), stream) == 0
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        assert bool(torch.isfinite(out).all())
+        res[name] = {"ms_per_launch": round(ms, 3), "tflops": round(flop / ms / 1e9, 1)}
+        print(f"[mfma-peak] {name}: {ms:.3f} ms, {flop / ms / 1e9:.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+    print(json.dumps({"metric": "bf16 MFMA microbenchmark (32x32x16, 8 independent chains per wave, "
+                                "2 waves per SIMD, no memory traffic)", "unit": "TFLOP/s",
+                      "nominal_peak": 2500.0, **res,
+                      "frac_of_nominal": {k: round(v["tflops"] / 2500.0, 4) for k, v in res.items()}}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this head is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
+    if args.mfma_peak:
+        mfma_peak(args.mfma_peak)
+        return
     import numpy as np
     import torch
     from lm_head_cross_amd import head as H

@@ -2,11 +2,17 @@
 
   python -m lm_head_cross_amd.prof_summary stats  KERNEL_STATS.csv  OUT.md  "<command>"
   python -m lm_head_cross_amd.prof_summary traffic FETCH.csv WRITE.csv KERNEL_SUBSTRING OUT.txt "<commands>" [KIND]
+  python -m lm_head_cross_amd.prof_summary mfma   COUNTERS.csv OUT.txt "<command>"
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same counters read for the
 plain 1 GiB device copy that `bench.py --copy-calibration` runs, averages them over the dispatches of
 the named kernel, and records a hash of the kernel sources, so that bench.py reports the figure only
 while the kernels are unchanged.
+
+`mfma` reads a run with the counters SQ_VALU_MFMA_BUSY_CYCLES (summed over the GPU's 1024 SIMDs)
+and GRBM_GUI_ACTIVE (summed over its 8 XCDs) and reports, per kernel and grid size, the clock the
+chip ran at (GRBM_GUI_ACTIVE / 8 over the dispatch's duration) and the MFMA pipe's busy fraction,
+both at that clock and against 2.4 GHz (the clock behind the 2.5 PFLOP/s bf16 figure).
 """
 from __future__ import annotations
 
@@ -19,10 +25,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 1 << 30
 
 
+SIMDS, XCDS, NOMINAL_HZ = 1024, 8, 2.4e9
+MEASUREMENT_AIDS = ("mfma_peak.hip",)   # in csrc/ but not the head's code
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name in MEASUREMENT_AIDS:
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -121,12 +133,37 @@ def read_traffic(path: str):
     return kv.get("kernel"), float(kv["traffic_bytes_per_launch"])
 
 
+def mfma_txt(counters_csv: str, command: str) -> str:
+    per = {}   # (kernel, grid) -> dispatch id -> {counter: value, "ns": duration}
+    for r in _rows(counters_csv):
+        key = (r["Kernel_Name"], int(r["Grid_Size"]))
+        d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = [f"command: {command}", f"source_hash: {source_hash()}", "",
+           "| kernel | grid (threads) | dispatches | avg (us) | clock (GHz) | MFMA busy at that clock | "
+           "MFMA busy vs 2.4 GHz |", "|---|---|---|---|---|---|---|"]
+    for (name, grid), ds in sorted(per.items(), key=lambda kv: -sum(d["ns"] for d in kv[1].values())):
+        ds = [d for d in ds.values() if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d]
+        busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds)
+        if not ds or busy == 0:
+            continue
+        ns = sum(d["ns"] for d in ds)
+        cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / XCDS
+        short = name if len(name) <= 60 else name[:57] + "..."
+        out.append(f"| `{short}` | {grid} | {len(ds)} | {ns / len(ds) / 1e3:.1f} | {cyc / ns:.3f} | "
+                   f"{busy / (cyc * SIMDS):.3f} | {busy / (ns * 1e-9 * NOMINAL_HZ * SIMDS):.3f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv[1] == "stats":
         open(argv[3], "w").write(kernel_stats_md(argv[2], os.path.basename(argv[3]), argv[4]))
     elif argv[1] == "traffic":
         kind = argv[7] if len(argv) > 7 else None
         open(argv[5], "w").write(traffic_txt(argv[2], argv[3], argv[4], argv[6], kind))
+    elif argv[1] == "mfma":
+        open(argv[3], "w").write(mfma_txt(argv[2], argv[4]))
     else:
         raise SystemExit(__doc__)
 
