@@ -224,3 +224,22 @@ def test_dh_bf16_is_the_fp32_dh_rounded_once(case):
         e = rel(dh16.float().cpu().numpy(), ora["dh"])
         say(f"[dh bf16] rel {e:.2e}")
         assert e <= TOL_GRAD
+
+
+def test_softcap_limit_with_saturated_logits():
+    # The supported edge: softcap 40 with every raw logit hugely negative, so every z sits at the
+    # lower end -40 and the forward's fixed-reference terms are e^(z - cap) ~ e^-80 (still normal
+    # floats). All logits then tie: logp = -ln V exactly (up to rounding), lse = -40 + ln V, and
+    # sech^2 underflows so dh and dW vanish. The oracle agrees.
+    inp = _custom(300, 64, 1000, "bf16", 40.0, 0.1, seed=11)
+    inp.h.copy_(torch.ones_like(inp.h))
+    inp.w.copy_(torch.full_like(inp.w, -40.0))          # raw = -2560 for every (token, vocab)
+    say("[case] softcap 40, saturated logits")
+    gpu = run_gpu(inp)
+    valid = inp.labels != -100
+    assert gpu["fwd_status"] == 0
+    assert np.allclose(gpu["logp"][valid], -np.log(1000.0), rtol=0, atol=1e-5)
+    assert np.allclose(gpu["lse"][valid], -40.0 + np.log(1000.0), rtol=0, atol=1e-4)
+    assert np.all(gpu["dh"] == 0) and np.all(gpu["dW"] == 0)
+    ora = run_oracle(inp)
+    assert rel(gpu["logp"], ora["logp"]) < 1e-5
