@@ -140,7 +140,9 @@ def mfma_txt(counters_csv: str, command: str) -> str:
         d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
         d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
-    out = [f"command: {command}", f"source_hash: {source_hash()}", "",
+    out = ["MFMA busy fraction and clock per kernel (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over 1024",
+           "SIMDs; clock = GRBM_GUI_ACTIVE / 8 XCDs over the dispatch's duration).", "",
+           f"command: {command}", f"source_hash: {source_hash()}", "",
            "| kernel | grid (threads) | dispatches | avg (us) | clock (GHz) | MFMA busy at that clock | "
            "MFMA busy vs 2.4 GHz |", "|---|---|---|---|---|---|---|"]
     for (name, grid), ds in sorted(per.items(), key=lambda kv: -sum(d["ns"] for d in kv[1].values())):
