@@ -100,13 +100,42 @@ def _stream(dev: torch.device):
 
 
 def _need_gpu(*ts):
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise OrpoError("tensors must be contiguous and on a GPU")
+        if dev is not None and t.device != dev:
+            raise OrpoError(f"tensors on different devices ({dev} and {t.device})")
+        dev = t.device
+
+
+def _need_dtype(what: str, t, *dtypes):
+    """Raise unless `t` (None allowed) has one of `dtypes`: the kernels read raw memory, so a wrong
+    element type would be reinterpreted, not converted."""
+    if t is not None and t.dtype not in dtypes:
+        names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise OrpoError(f"{what} must be {names}, got {str(t.dtype).replace('torch.', '')}")
+
+
+def _head_dtypes(h, w, labels, scales=None, biases=None):
+    _need_dtype("h", h, torch.bfloat16, torch.float32)
+    _need_dtype("labels", labels, torch.int32)
+    if scales is not None or biases is not None:
+        _need_dtype("w (packed 4-bit words)", w, torch.int32)
+        _need_dtype("scales", scales, torch.bfloat16)
+        _need_dtype("biases", biases, torch.bfloat16)
+        if h.dtype != torch.bfloat16:
+            raise OrpoError("a 4-bit head needs bfloat16 h")
+    else:
+        _need_dtype("w", w, h.dtype)
 
 
 def make_desc(M, d, V, h_dtype, w_fmt, softcap, ignore_index=IGNORE_INDEX, flags=0,
               skip_eps=0.0) -> Desc:
+    if h_dtype not in (torch.float32, torch.bfloat16):
+        raise OrpoError(f"h must be bfloat16 or float32, got {h_dtype}")
     h_fmt = ORPO_F32 if h_dtype == torch.float32 else ORPO_BF16
     return Desc(M, d, V, h_fmt, w_fmt, float(softcap), ignore_index, flags, float(skip_eps))
 
@@ -140,6 +169,7 @@ def head_fwd(h, w, labels, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None, 
              return_ws=False, skip_eps=0.0):
     """logp[M], lse[M] (float32). `w` is W[V,d] (f32/bf16) or the packed q4 words [V,d/8] (int32).
     skip_eps > 0 also records the per-tile logit maxima the backward's cold-tile skip reads."""
+    _head_dtypes(h, w, labels, scales, biases)
     _need_gpu(h, w, labels, scales, biases)
     M, d = h.shape
     V = _vocab(w, scales)
@@ -163,6 +193,9 @@ def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, retu
     """out (float64) and g[M] (float32). scope "response": seg_offsets [2P+1] = (chosen, rejected)
     per pair, out = [loss, nll, or, accuracy, margin, lw[P], lr[P]]; scope "full": seg_offsets
     [3P+1] = (prompt, chosen, rejected) per pair, the NLL over prompt + chosen, out adds pm[P]."""
+    _need_dtype("logp", logp, torch.float32)
+    _need_dtype("labels", labels, torch.int32)
+    _need_dtype("seg_offsets", seg_offsets, torch.int32)
     _need_gpu(logp, labels, seg_offsets)
     S = SCOPES[scope]
     M = logp.shape[0]
@@ -184,7 +217,11 @@ def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNOR
     same fp32 sums rounded once). skip_eps > 0 turns on the coefficient filter (an approximation;
     see orpo_head_desc.skip_eps); fwd_ws, the forward's workspace (head_fwd(..., skip_eps=...,
     return_ws=True)), adds its exact cold-tile skip."""
-    _need_gpu(h, w, labels, lse, g, scales, biases, dW)
+    _head_dtypes(h, w, labels, scales, biases)
+    _need_dtype("lse", lse, torch.float32)
+    _need_dtype("g", g, torch.float32)
+    _need_dtype("dW", dW, torch.float32)
+    _need_gpu(h, w, labels, lse, g, scales, biases, dW, fwd_ws)
     M, d = h.shape
     V = _vocab(w, scales)
     flags = (ORPO_DW_ACCUMULATE if accumulate else 0) | (ORPO_DH_BF16 if dh_bf16 else 0)
@@ -238,6 +275,10 @@ def pref_loss(kind, logp, labels, seg_offsets, V, beta, gamma=0.0, ref_sums=None
     reference sums ref_sums [2P] float64), IPO ("ipo": means, optional reference means) or hinge
     ("hinge": sums, optional reference sums) over chosen/rejected spans seg_offsets [2P+1].
     Returns out (float64 [3 + 2P]: loss, accuracy, margin, chosen values, rejected values), g."""
+    _need_dtype("logp", logp, torch.float32)
+    _need_dtype("labels", labels, torch.int32)
+    _need_dtype("seg_offsets", seg_offsets, torch.int32)
+    _need_dtype("ref_sums", ref_sums, torch.float64)
     _need_gpu(logp, labels, seg_offsets, ref_sums)
     M = logp.shape[0]
     P = (seg_offsets.shape[0] - 1) // 2
@@ -255,6 +296,11 @@ def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip
               ignore_index=IGNORE_INDEX, return_ws=False):
     """GRPO's clipped policy gradient + beta * k3 KL over completions seg_offsets [S+1] with one
     advantage each. Returns out (float64 [4]: loss, pg, kl, clip fraction), g."""
+    for name, t in (("logp", logp), ("old_logp", old_logp), ("ref_logp", ref_logp),
+                    ("advantages", advantages)):
+        _need_dtype(name, t, torch.float32)
+    _need_dtype("labels", labels, torch.int32)
+    _need_dtype("seg_offsets", seg_offsets, torch.int32)
     _need_gpu(logp, old_logp, ref_logp, advantages, labels, seg_offsets)
     M = logp.shape[0]
     S = seg_offsets.shape[0] - 1
@@ -277,9 +323,19 @@ class HeadStep:
 
         objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
         backward, with its parameters and inputs in `obj`: "simpo" {beta, gamma}, "dpo" {beta,
-        ref_sums [2P] float64}, "ipo" / "hinge" {beta, optional ref_sums}, "grpo" {clip_eps, beta, old_logp [M], ref_logp [M], advantages [S]
-        float32, seg_offsets are then [S+1] completions}."""
-        _need_gpu(h, w, labels, seg_offsets, scales, biases)
+        ref_sums [2P] float64}, "ipo" / "hinge" {beta, optional ref_sums}, "grpo" {clip_eps,
+        beta, old_logp [M], ref_logp [M], advantages [S] float32, seg_offsets are then [S+1]
+        completions}."""
+        if objective != "orpo" and objective != "grpo" and objective not in PREF_KINDS:
+            raise OrpoError(f"unknown objective {objective!r}")
+        o = dict(obj or {})
+        _head_dtypes(h, w, labels, scales, biases)
+        _need_dtype("seg_offsets", seg_offsets, torch.int32)
+        _need_dtype("ref_sums", o.get("ref_sums"), torch.float64)
+        for k in ("old_logp", "ref_logp", "advantages"):
+            _need_dtype(k, o.get(k), torch.float32)
+        _need_gpu(h, w, labels, seg_offsets, scales, biases,
+                  *(o.get(k) for k in ("ref_sums", "old_logp", "ref_logp", "advantages")))
         self.h, self.w, self.labels, self.off = h, w, labels, seg_offsets
         self.scales, self.biases = scales, biases
         self.M, self.d = h.shape

@@ -180,3 +180,33 @@ def test_dh_bf16_flag_workspace_and_formats():
     st = L.orpo_head_bwd(ctypes.byref(f32), 16, H.Weight(16, None, None), 16, 16, 16, 16, 16, 16,
                          1 << 30, None, None)
     assert st == EUNSUP
+
+
+def test_binding_rejects_wrong_dtypes_before_any_launch():
+    # The kernels read raw memory: a wrong element type must be refused, not reinterpreted.
+    import torch
+    h = torch.zeros(4, 64, dtype=torch.float16)
+    w = torch.zeros(8, 64, dtype=torch.float16)
+    lab = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(H.OrpoError, match="h must be"):
+        H.head_fwd(h, w, lab.int())
+    with pytest.raises(H.OrpoError, match="labels must be int32"):
+        H.head_fwd(h.bfloat16(), w.bfloat16(), lab)
+    with pytest.raises(H.OrpoError, match="w must be bfloat16"):
+        H.head_fwd(h.bfloat16(), w.float(), lab.int())
+    with pytest.raises(H.OrpoError, match="seg_offsets must be int32"):
+        H.orpo_loss(torch.zeros(4), lab.int(), torch.zeros(3, dtype=torch.int64), 8, 0.1)
+    with pytest.raises(H.OrpoError, match="g must be float32"):
+        H.head_bwd(h.bfloat16(), w.bfloat16(), lab.int(), torch.zeros(4), torch.zeros(4).double())
+    with pytest.raises(H.OrpoError, match="ref_sums must be float64"):
+        H.pref_loss("dpo", torch.zeros(4), lab.int(), torch.zeros(3, dtype=torch.int32), 8, 0.1,
+                    ref_sums=torch.zeros(2))
+    with pytest.raises(H.OrpoError, match="scales must be bfloat16"):
+        H.head_fwd(h.bfloat16(), torch.zeros(8, 8, dtype=torch.int32), lab.int(),
+                   scales=torch.zeros(8, 1), biases=torch.zeros(8, 1, dtype=torch.bfloat16))
+    # Right dtypes on the CPU: refused for placement, still before anything is launched.
+    with pytest.raises(H.OrpoError, match="on a GPU"):
+        H.head_fwd(h.bfloat16(), w.bfloat16(), lab.int())
+    with pytest.raises(H.OrpoError, match="unknown objective"):
+        H.HeadStep(h.bfloat16(), w.bfloat16(), lab.int(), torch.zeros(3, dtype=torch.int32), 8, 0.0,
+                   0.1, objective="kto")
