@@ -106,3 +106,65 @@ def test_full_size_sampled_parity(key):
         msg += f" dW={e_dW:.2e}"
         assert e_dW <= TOL_GRAD
     say(msg)
+
+
+def test_full_size_sibling_objectives_on_gpu_logp():
+    # At the e4b size: every sibling objective's float64 epilogue on the GPU (loss, metrics, branch
+    # values and the per-token g) against the oracle's on the same logp vector. The head kernels
+    # they share are covered above; here it is the objectives' reductions over 8192 tokens.
+    from oracle import objectives as ob
+    cfg = synth.CONFIGS[3]
+    say(f"[fullsize objectives] {cfg.name} M={cfg.M}")
+    inp = synth.make_inputs(cfg, seed=0, label_device="cuda")
+    d = dev()
+    h, w = inp.h.to(d), inp.w.to(d)
+    labels = torch.from_numpy(inp.labels).to(d)
+    off = torch.from_numpy(inp.seg_offsets).to(d)
+    logp_t, _ = H.head_fwd(h, w, labels, cfg.softcap)
+    torch.cuda.synchronize()
+    logp = logp_t.cpu().numpy().astype(np.float64)
+    sums, n = ob.span_stats(logp, inp.labels, inp.seg_offsets)
+    means = sums / n
+    rng = np.random.default_rng(5)
+    P = cfg.pairs
+    for kind, beta, gamma, ref in (("simpo", 2.0, 0.5, None),
+                                   ("dpo", 0.1, 0.0, sums + rng.normal(0, 5.0, 2 * P)),
+                                   ("ipo", 0.5, 0.0, means + rng.normal(0, 0.1, 2 * P)),
+                                   ("hinge", 0.02, 0.0, sums + rng.normal(0, 30.0, 2 * P))):
+        r = np.zeros(2 * P) if ref is None else ref
+        if kind == "simpo":
+            ep, vals = ob.simpo_epilogue(means[0::2], means[1::2], beta, gamma), means
+        elif kind == "dpo":
+            ep, vals = ob.dpo_epilogue(sums[0::2], sums[1::2], r[0::2], r[1::2], beta), sums
+        elif kind == "ipo":
+            ep, vals = ob.ipo_epilogue(means[0::2], means[1::2], r[0::2], r[1::2], beta), means
+        else:
+            ep, vals = ob.hinge_epilogue(sums[0::2], sums[1::2], r[0::2], r[1::2], beta), sums
+            assert np.min(np.abs(1.0 - beta * ep["h"])) > 1e-6       # no pair at the kink
+        ref_t = None if ref is None else torch.from_numpy(ref).to(d)
+        out, g = H.pref_loss(kind, logp_t, labels, off, cfg.V, beta, gamma, ref_sums=ref_t)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        for i, k in enumerate(("loss", "accuracy", "margin")):
+            assert abs(o[i] - ep[k]) <= 1e-12 * max(1.0, abs(ep[k])), (kind, k)
+        assert np.allclose(o[3:3 + P], vals[0::2], rtol=1e-12) and np.allclose(o[3 + P:], vals[1::2], rtol=1e-12)
+        g_o = ob.pairwise_cotangent(kind, ep, n, inp.labels, inp.seg_offsets)
+        e = rel(g.cpu().numpy(), g_o)
+        say(f"[fullsize objectives] {kind}: loss {o[0]:.6g} g rel {e:.1e}")
+        assert e < 1e-6
+    # GRPO over the same spans as completions (old / reference policies: the logp plus noise).
+    old = (logp + rng.normal(0, 0.1, cfg.M)).astype(np.float32)
+    refl = (logp + rng.normal(0, 0.2, cfg.M)).astype(np.float32)
+    S = len(inp.seg_offsets) - 1
+    adv = ob.group_advantages(rng.normal(size=S), 4).astype(np.float32)
+    out, g = H.grpo_loss(logp_t, torch.from_numpy(old).to(d), torch.from_numpy(refl).to(d),
+                         torch.from_numpy(adv).to(d), labels, off, cfg.V, 0.2, 0.04)
+    torch.cuda.synchronize()
+    r = ob.grpo_loss(logp, old, refl, inp.labels, inp.seg_offsets, adv, 0.2, 0.04)
+    o = out.cpu().numpy()
+    for i, k in enumerate(("loss", "pg", "kl")):
+        assert abs(o[i] - r[k]) <= 1e-9 * max(1.0, abs(r[k])), ("grpo", k)
+    assert abs(o[3] - r["clip_frac"]) < 1e-12
+    e = rel(g.cpu().numpy(), r["g"])
+    say(f"[fullsize objectives] grpo: loss {o[0]:.6g} g rel {e:.1e}")
+    assert e < 1e-6
