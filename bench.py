@@ -254,7 +254,9 @@ def main():
     n_valid = inp.n_valid
     tok_s = n_valid / (ms / 1e3)
     peak_flops = PEAK_F32 if cfg.dtype == "f32" else PEAK_BF16
-    work = (6 if cfg.q4 else 8) * cfg.M * cfg.V * cfg.d
+    # Algorithmic work credited: valid tokens only (padding and ignored rows are processed, not
+    # credited), 8 V d FLOP each (fwd 2, bwd 6; 6 V d for the dh-only 4-bit head).
+    work = (6 if cfg.q4 else 8) * n_valid * cfg.V * cfg.d
     mfma_frac = work / (ms / 1e3) / peak_flops
 
     # Dominant kernel: the kind with the most traced time; achieved = its algorithmic FLOPs per
