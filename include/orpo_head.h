@@ -154,7 +154,7 @@ orpo_status orpo_loss(int64_t M, int32_t n_pairs, const int32_t* seg_offsets, co
  *                  token)
  *   Other arguments, the workspace size and the error behaviour as for orpo_loss. A prompt span
  *   without a valid token is allowed (it then weighs nothing and every result equals orpo_loss's on
- *   the two response spans); a response span without one sets ORPO_STATUS_EMPTY_BRANCH.
+ *   the two response spans); a response span without one sets ORPO_DATA_EMPTY_BRANCH.
  */
 orpo_status orpo_loss_full(int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
                            const float* logp, const int32_t* labels, int64_t V,
@@ -221,7 +221,7 @@ orpo_status orpo_pref_loss(int32_t kind, int64_t M, int32_t n_pairs, const int32
  *   the same tokens (inputs; no gradient flows into them).
  *   out   (device) double [4]: loss, pg (mean policy-gradient term), kl (mean k3), clip fraction
  *         (share of valid tokens whose clipped term is the strict minimum)
- *   Errors and status bits as for orpo_loss (an empty completion sets ORPO_STATUS_EMPTY_BRANCH).
+ *   Errors and status bits as for orpo_loss (an empty completion sets ORPO_DATA_EMPTY_BRANCH).
  */
 orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets,
                            const float* logp, const float* old_logp, const float* ref_logp,
@@ -248,6 +248,10 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  *   dW             (device) float [V,d] out (overwritten, or accumulated with ORPO_DW_ACCUMULATE);
  *                  NULL computes dh only. Must be NULL for ORPO_Q4G64 (a quantised head is frozen).
  *   ws             (device) >= orpo_head_bwd_workspace_bytes(desc) bytes
+ *   fwd_ws         (device, optional) the workspace of the orpo_head_fwd call that produced lse,
+ *                  with the same desc; read only with desc->skip_eps > 0, where its per-tile logit
+ *                  maxima let the backward skip whole cold coefficient tiles (exactly the blocks
+ *                  the filter would drop). NULL: the filter alone. Ignored when skip_eps is 0.
  *   With desc->skip_eps > 0 (the coefficient filter) the workspace also holds the filter's block
  *   flags, and ORPO_EUNSUPPORTED is returned for fp32 heads and for backward tilings with more
  *   than 8192 64-wide slices per coefficient row or column (orpo_set_bwd_tiling). The launches are
