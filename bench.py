@@ -27,7 +27,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="workload key in lm_head_cross_amd.synth.CONFIGS")
+    ap.add_argument("--config", default="e4b-bf16-softcap30",
+                    help="workload name (lm_head_cross_amd.synth.WORKLOADS) or its integer key")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
@@ -196,7 +197,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.workload(args.config)
     print(f"[bench] generating {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, seed=args.seed, label_device="cuda")
     h = inp.h.to(dev)

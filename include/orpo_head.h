@@ -37,7 +37,7 @@ extern "C" {
 typedef enum {
   ORPO_OK = 0,
   ORPO_EINVAL = -1,        /* null pointer, negative or inconsistent size, bad option          */
-  ORPO_EUNSUPPORTED = -2,  /* a valid request this build does not implement (see each call)     */
+  ORPO_EUNSUPPORTED = -2,  /* a valid request this library does not implement (see each call)   */
   ORPO_ENOWS = -3,         /* workspace pointer null or smaller than the *_workspace_bytes size */
   ORPO_EHIP = -4           /* a HIP runtime call failed (see orpo_last_hip_error)               */
 } orpo_status;

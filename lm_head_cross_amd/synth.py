@@ -84,6 +84,16 @@ CONFIGS = {
 }
 
 
+WORKLOADS = {cfg.name: cfg for cfg in CONFIGS.values()}   # the same workloads, by name
+
+
+def workload(name_or_key) -> HeadConfig:
+    """A workload by its name (e.g. "e4b-bf16-softcap30") or its integer seed key."""
+    if isinstance(name_or_key, int) or str(name_or_key).isdigit():
+        return CONFIGS[int(name_or_key)]
+    return WORKLOADS[name_or_key]
+
+
 def reduced(cfg: HeadConfig, pairs: int = 1) -> HeadConfig:
     """Same d, V, softcap and distributions with only `pairs` pairs; M = the largest packing."""
     return cfg.replace(pairs=pairs, M=pairs * (2 * cfg.len_hi + cfg.prompt_hi),

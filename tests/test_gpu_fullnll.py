@@ -37,7 +37,7 @@ def _custom_full(M, d, V, cap, lam, seed, pairs=3):
 
 
 def test_e4b_full_nll_one_pair():
-    cfg = synth.reduced(synth.CONFIGS[6], 1)
+    cfg = synth.reduced(synth.workload("e4b-bf16-softcap30-fullnll"), 1)
     say(f"[case] {cfg.name} M={cfg.M}")
     inp = synth.make_inputs(cfg, seed=0, label_device="cuda")
     gpu = run_gpu(inp)

@@ -32,9 +32,11 @@ def _sample_rows(inp, n_per_branch=2, seed=0):
     return np.unique(np.array(rows, dtype=np.int64))
 
 
-@pytest.mark.parametrize("key", [2, 3, 4, 5, 6])
-def test_full_size_sampled_parity(key):
-    cfg = synth.CONFIGS[key]
+@pytest.mark.parametrize("name", ["minicpm-like-bf16", "e4b-bf16-softcap30",
+                                  "q4g64-minicpm-shape-softcap30", "12b-like-bf16-softcap30",
+                                  "e4b-bf16-softcap30-fullnll"])
+def test_full_size_sampled_parity(name):
+    cfg = synth.workload(name)
     say(f"[fullsize] {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}")
     inp = synth.make_inputs(cfg, seed=0, label_device="cuda")
     d = dev()
@@ -113,7 +115,7 @@ def test_full_size_sibling_objectives_on_gpu_logp():
     # values and the per-token g) against the oracle's on the same logp vector. The head kernels
     # they share are covered above; here it is the objectives' reductions over 8192 tokens.
     from oracle import objectives as ob
-    cfg = synth.CONFIGS[3]
+    cfg = synth.workload("e4b-bf16-softcap30")
     say(f"[fullsize objectives] {cfg.name} M={cfg.M}")
     inp = synth.make_inputs(cfg, seed=0, label_device="cuda")
     d = dev()

@@ -28,7 +28,7 @@ def _snap(step):
 
 
 def test_head_step_replays_as_a_hip_graph():
-    cfg = synth.reduced(synth.CONFIGS[3], 2).replace(V=20000, name="e4b-like-graph")
+    cfg = synth.reduced(synth.workload("e4b-bf16-softcap30"), 2).replace(V=20000, name="e4b-like-graph")
     say(f"[case] graph replay {cfg.name} M={cfg.M} V={cfg.V}")
     step = _step(cfg, 0)
     step.step()
@@ -55,7 +55,7 @@ def test_head_step_replays_as_a_hip_graph():
 
 
 def test_two_steps_on_two_streams_match_sequential():
-    cfg = synth.reduced(synth.CONFIGS[2], 2).replace(name="minicpm-like-streams")
+    cfg = synth.reduced(synth.workload("minicpm-like-bf16"), 2).replace(name="minicpm-like-streams")
     say(f"[case] two streams {cfg.name} M={cfg.M} V={cfg.V}")
     a, b = _step(cfg, 1), _step(cfg, 2)
     a.step()

@@ -24,25 +24,25 @@ def _check_config(cfg, seed=0):
 
 
 def test_tiny_f32_full():
-    errs = _check_config(synth.CONFIGS[1])
+    errs = _check_config(synth.workload("tiny-f32"))
     # fp32 operands: far inside the gates.
     assert errs["logp"] < 1e-5 and errs["dh"] < 1e-4 and errs["dW"] < 1e-4
 
 
 def test_minicpm_shape_one_pair():
-    _check_config(synth.reduced(synth.CONFIGS[2], 1))
+    _check_config(synth.reduced(synth.workload("minicpm-like-bf16"), 1))
 
 
 def test_e4b_shape_one_pair():
-    _check_config(synth.reduced(synth.CONFIGS[3], 1))
+    _check_config(synth.reduced(synth.workload("e4b-bf16-softcap30"), 1))
 
 
 def test_q4_head_one_pair():
-    _check_config(synth.reduced(synth.CONFIGS[4], 1))
+    _check_config(synth.reduced(synth.workload("q4g64-minicpm-shape-softcap30"), 1))
 
 
 def test_12b_shape_short_pair():
-    cfg = synth.CONFIGS[5].replace(pairs=1, M=512, len_lo=200, len_hi=256, name="12b-like-short")
+    cfg = synth.workload("12b-like-bf16-softcap30").replace(pairs=1, M=512, len_lo=200, len_hi=256, name="12b-like-short")
     _check_config(cfg)
 
 
@@ -124,7 +124,7 @@ def test_zero_weights_closed_form():
 
 
 def test_deterministic_bitwise():
-    inp = synth.make_inputs(synth.reduced(synth.CONFIGS[2], 1), seed=4, label_device="cuda")
+    inp = synth.make_inputs(synth.reduced(synth.workload("minicpm-like-bf16"), 1), seed=4, label_device="cuda")
     a = run_gpu(inp)
     b = run_gpu(inp)
     for k in ("logp", "lse", "g", "dh", "dW"):

@@ -7,8 +7,8 @@ from oracle import orpo_oracle as orc
 
 
 def test_tiny_config_layout_and_determinism():
-    a = synth.make_inputs(synth.CONFIGS[1], seed=0)
-    b = synth.make_inputs(synth.CONFIGS[1], seed=0)
+    a = synth.make_inputs(synth.workload("tiny-f32"), seed=0)
+    b = synth.make_inputs(synth.workload("tiny-f32"), seed=0)
     assert list(a.seg_offsets) == [0, 128, 256]
     assert a.h.dtype == torch.float32 and a.w.dtype == torch.float32
     assert torch.equal(a.h, b.h) and torch.equal(a.w, b.w) and np.array_equal(a.labels, b.labels)
@@ -18,7 +18,7 @@ def test_tiny_config_layout_and_determinism():
 
 
 def test_packing_padding_and_peaked_labels():
-    cfg = synth.reduced(synth.CONFIGS[2], pairs=2).replace(V=2048, d=128)
+    cfg = synth.reduced(synth.workload("minicpm-like-bf16"), pairs=2).replace(V=2048, d=128)
     x = synth.make_inputs(cfg, seed=1)
     off = x.seg_offsets
     assert off[0] == 0 and np.all(np.diff(off) >= 1) and off[-1] <= cfg.M
@@ -54,7 +54,7 @@ def test_prompt_spans_layout():
     # The full-NLL workload: per pair (prompt, chosen, rejected), prompt lengths in their range (up to
     # the packing scale), responses in theirs, all within M; the response-scope draws are unchanged
     # by the prompt option (same seed, same response lengths before any packing scale).
-    cfg = synth.reduced(synth.CONFIGS[6], 3).replace(d=256, V=4096)   # layout only: small head
+    cfg = synth.reduced(synth.workload("e4b-bf16-softcap30-fullnll"), 3).replace(d=256, V=4096)   # layout only: small head
     inp = synth.make_inputs(cfg, seed=2)
     assert cfg.scope == "full" and cfg.spans_per_pair == 3
     off = inp.seg_offsets
