@@ -318,14 +318,14 @@ def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip
 class HeadStep:
     def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
                  want_dW=True, ignore_index=IGNORE_INDEX, scope="response", objective="orpo",
-                 obj=None, skip_eps=0.0):
+                 obj=None, skip_eps=0.0, dh_bf16=False):
         """One head step: forward -> loss -> backward on preallocated buffers.
 
         objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
         backward, with its parameters and inputs in `obj`: "simpo" {beta, gamma}, "dpo" {beta,
         ref_sums [2P] float64}, "ipo" / "hinge" {beta, optional ref_sums}, "grpo" {clip_eps,
         beta, old_logp [M], ref_logp [M], advantages [S] float32, seg_offsets are then [S+1]
-        completions}."""
+        completions}. dh_bf16: dh as bfloat16 (the fp32 sums rounded once)."""
         if objective != "orpo" and objective != "grpo" and objective not in PREF_KINDS:
             raise OrpoError(f"unknown objective {objective!r}")
         o = dict(obj or {})
@@ -345,7 +345,7 @@ class HeadStep:
         self.P = (seg_offsets.shape[0] - 1) // self.S
         dev = h.device
         self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index,
-                              skip_eps=skip_eps)
+                              flags=ORPO_DH_BF16 if dh_bf16 else 0, skip_eps=skip_eps)
         L = lib()
         self.fws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(self.desc)), dev)
         self.bws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(self.desc)), dev)
@@ -356,7 +356,8 @@ class HeadStep:
         n_out = {"orpo": 5 + (3 if self.S == 3 else 2) * self.P, "grpo": 4}.get(objective, 3 + 2 * self.P)
         self.out = torch.empty(n_out, dtype=torch.float64, device=dev)
         self.g = torch.empty(self.M, dtype=torch.float32, device=dev)
-        self.dh = torch.empty(self.M, self.d, dtype=torch.float32, device=dev)
+        self.dh = torch.empty(self.M, self.d, dtype=torch.bfloat16 if dh_bf16 else torch.float32,
+                              device=dev)
         self.dW = torch.empty(V, self.d, dtype=torch.float32, device=dev) if want_dW else None
         self.wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
                          None if biases is None else biases.data_ptr())
