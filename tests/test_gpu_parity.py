@@ -243,3 +243,17 @@ def test_softcap_limit_with_saturated_logits():
     assert np.all(gpu["dh"] == 0) and np.all(gpu["dW"] == 0)
     ora = run_oracle(inp)
     assert rel(gpu["logp"], ora["logp"]) < 1e-5
+
+
+def test_head_step_dh_bf16_matches_rounded_fp32():
+    inp = _custom(600, 128, 1500, "bf16", 30.0, 0.1, seed=79)
+    say("[case] HeadStep dh bf16")
+    d = dev()
+    args = (inp.h.to(d), inp.w.to(d), torch.from_numpy(inp.labels).to(d),
+            torch.from_numpy(inp.seg_offsets).to(d), 1500, 30.0, 0.1)
+    s32, s16 = H.HeadStep(*args), H.HeadStep(*args, dh_bf16=True)
+    s32.step()
+    s16.step()
+    torch.cuda.synchronize()
+    assert s16.dh.dtype == torch.bfloat16
+    assert torch.equal(s16.dh, s32.dh.to(torch.bfloat16)) and torch.equal(s16.dW, s32.dW)
