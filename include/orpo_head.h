@@ -253,9 +253,11 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  *                  maxima let the backward skip whole cold coefficient tiles (exactly the blocks
  *                  the filter would drop). NULL: the filter alone. Ignored when skip_eps is 0.
  *   With desc->skip_eps > 0 (the coefficient filter) the workspace also holds the filter's block
- *   flags, and ORPO_EUNSUPPORTED is returned for fp32 heads and for backward tilings with more
- *   than 8192 64-wide slices per coefficient row or column (orpo_set_bwd_tiling). The launches are
- *   then traced with the exact method's work (skipped blocks included).
+ *   flags, and ORPO_EUNSUPPORTED is returned (and 0 by orpo_head_bwd_workspace_bytes) for fp32
+ *   heads and for a vocabulary block or token chunk of more than 8192 64-wide slices, i.e. above
+ *   524288 entries or tokens (reachable only through orpo_set_bwd_tiling: the default 256 MiB
+ *   budget keeps bf16 blocks within it). The launches are then traced with the exact method's work
+ *   (skipped blocks included).
  */
 orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
                           const int32_t* labels, const float* lse, const float* g, void* dh,
@@ -268,7 +270,8 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
  * max(16384, V/8 rounded up to 256) (and never above V), so that a small vocabulary still
  * pipelines over several blocks. 0 restores a default. Process-wide; call it only while no call of this library is in
  * flight, and size workspaces after it. Returns ORPO_EINVAL for a chunk that is not a multiple of
- * 256 or a negative value. */
+ * 256, a negative value, a chunk above 2^31 tokens or a budget above 2^40 bytes (these bounds keep
+ * every workspace size far from wrapping a size_t). */
 orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes);
 
 /* Kernel tracing (a profiling aid). While enabled, every kernel this library launches is bracketed
@@ -296,8 +299,9 @@ orpo_status orpo_trace_reset(void);                    /* forget the records, ke
  * *status_out (host). Returns ORPO_EHIP if the wait or copy fails. */
 orpo_status orpo_read_status(const void* ws, uint32_t* status_out, hipStream_t stream);
 
-/* Text for a status code (static storage). */
-const char* orpo_status_string(orpo_status s);
+/* Text for a status code (static storage). Takes any int32 value (an orpo_status is passed as
+ * one); codes outside orpo_status give "unknown status". */
+const char* orpo_status_string(int32_t status);
 
 /* The last HIP error code seen by this library on the calling thread (hipSuccess if none). */
 int32_t orpo_last_hip_error(void);

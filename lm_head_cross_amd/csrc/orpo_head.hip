@@ -163,6 +163,11 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
   return p;
 }
 
+// Under the coefficient filter a dh / dW tile lists its K steps (64 entries or tokens each) in LDS.
+bool bwd_plan_supported(const orpo_head_desc* d, const BwdPlan& p) {
+  return !(d->skip_eps > 0.f) || (p.BVb / 64 <= kMaxKSteps && p.C / 64 <= kMaxKSteps);
+}
+
 template <class E, bool Q4, bool SC>
 orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
   TraceScope ts(ORPO_K_FWD, 2.0 * double(a.M) * double(a.V) * double(a.d), st);
@@ -217,7 +222,8 @@ size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc) {
   Kind k;
   if (check_desc(desc, &k) != ORPO_OK) return 0;
   if ((desc->flags & ORPO_DH_BF16) && k == kF32) return 0;   // unsupported
-  return plan_bwd(desc, k).ws;
+  const BwdPlan p = plan_bwd(desc, k);
+  return bwd_plan_supported(desc, p) ? p.ws : 0;
 }
 
 size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs) {
@@ -412,6 +418,7 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   if (k == kQ4 && dW) return ORPO_EUNSUPPORTED;
   if ((desc->flags & ORPO_DH_BF16) && k == kF32) return ORPO_EUNSUPPORTED;
   const BwdPlan p = plan_bwd(desc, k);
+  if (!bwd_plan_supported(desc, p)) return ORPO_EUNSUPPORTED;
   if (!ws || ws_bytes < p.ws || (uintptr_t)ws % 256) return ORPO_ENOWS;
   if (desc->M == 0) return ORPO_OK;
   if (!h || !labels || !lse || !g || !dh) return ORPO_EINVAL;
@@ -438,7 +445,6 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.skip_eps = desc->skip_eps;
   a.nsl_v = (int32_t)(p.BVb / 64);
   a.nsl_t = (int32_t)(p.C / 64);
-  if (a.skip_eps > 0.f && (a.nsl_v > kMaxKSteps || a.nsl_t > kMaxKSteps)) return ORPO_EUNSUPPORTED;
   a.tmax = (a.skip_eps > 0.f && fwd_ws) ? (const float*)((const char*)fwd_ws + plan_fwd(desc).tmax_off)
                                         : nullptr;
   a.n_vtiles = (int32_t)cdiv(desc->V, kTile);
@@ -490,6 +496,8 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
 
 orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes) {
   if (chunk_tokens < 0 || chunk_tokens % kTile != 0) return ORPO_EINVAL;
+  // Bounds that keep every workspace size below 2^54 bytes, so no size product can wrap.
+  if (chunk_tokens > (int64_t(1) << 31) || coeff_bytes > (size_t(1) << 40)) return ORPO_EINVAL;
   g_chunk = chunk_tokens ? chunk_tokens : kChunkDefault;
   g_coeff_budget = coeff_bytes;
   return ORPO_OK;
@@ -546,8 +554,8 @@ orpo_status orpo_read_status(const void* ws, uint32_t* status_out, hipStream_t s
   return ORPO_OK;
 }
 
-const char* orpo_status_string(orpo_status s) {
-  switch (s) {
+const char* orpo_status_string(int32_t status) {
+  switch (status) {
     case ORPO_OK: return "ok";
     case ORPO_EINVAL: return "invalid argument";
     case ORPO_EUNSUPPORTED: return "unsupported shape or format";

@@ -114,6 +114,45 @@ def test_bwd_tiling_knob_validates_and_resizes():
     assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 2 * 4096 * 4096 * 2
 
 
+def test_filter_k_step_limit_reported_by_workspace_size_and_entry_point():
+    L = H.lib()
+    ws = (ctypes.c_char * 512)()
+    base = ctypes.addressof(ws) + (-ctypes.addressof(ws)) % 256
+    big = H.Desc(256, 256, 1 << 20, H.ORPO_BF16, H.ORPO_BF16, 30.0, -100, 0, 1e-5)
+    exact = H.Desc(256, 256, 1 << 20, H.ORPO_BF16, H.ORPO_BF16, 30.0, -100, 0, 0.0)
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) > 0
+    try:
+        assert L.orpo_set_bwd_tiling(256, 256 * 524288 * 2) == 0           # 8192 slices of 64: the limit
+        fl = 524288 // 64 * 4 + 524288 // 256 * 4 * 2                       # dh and dW block flags
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == 256 + 2 * 256 * 524288 * 2 + 2 * fl
+        assert L.orpo_set_bwd_tiling(256, 256 * (524288 + 256) * 2) == 0   # one slice more
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == 0
+        w = H.Weight(16, None, None)
+        st = L.orpo_head_bwd(ctypes.byref(big), 16, w, 16, 16, 16, 16, None, base, 256, None, None)
+        assert st == EUNSUP                                                # before the workspace check
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(exact)) > 0   # no limit without the filter
+    finally:
+        assert L.orpo_set_bwd_tiling(0, 0) == 0
+
+
+def test_bwd_tiling_bounds_keep_workspace_sizes_from_wrapping():
+    L = H.lib()
+    assert L.orpo_set_bwd_tiling((1 << 31) + 256, 0) == EINVAL
+    assert L.orpo_set_bwd_tiling(0, (1 << 40) + 1) == EINVAL
+    big = _desc(M=(1 << 31) - 1, d=1 << 20, V=(1 << 31) - 1, flags=2)   # bf16 dh: the fp32 chunk accumulator
+    try:
+        assert L.orpo_set_bwd_tiling(1 << 31, 1 << 40) == 0
+        # C = 2^31 tokens, so the 2^40-byte budget leaves one 256-entry block: 2 tiles of 2^31 x 256 bf16.
+        expect = 256 + 2 * (1 << 31) * 256 * 2 + (1 << 31) * (1 << 20) * 4
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == expect
+        assert L.orpo_set_bwd_tiling(256, 1 << 40) == 0
+        # C = 256: the budget allows 2^31 entries, capped at V rounded up to 256 (one block, no accumulator).
+        expect = 256 + 2 * 256 * (1 << 31) * 2
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == expect
+    finally:
+        assert L.orpo_set_bwd_tiling(0, 0) == 0
+
+
 def test_status_strings():
     L = H.lib()
     assert L.orpo_status_string(0) == b"ok"
