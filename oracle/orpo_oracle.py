@@ -334,7 +334,7 @@ def token_cotangent_full(dL_dmean, n, labels, seg_offsets, ignore_index: int = I
 # Backward: coeff, dh, dW
 # --------------------------------------------------------------------------------------------
 def backward(h, W, labels, lse, g, cap: float = 0.0, ignore_index: int = IGNORE_INDEX,
-             want_dW: bool = True, rows: int = 64):
+             want_dW: bool = True, rows: int = 64, logit_operands=None):
     """dh = coeff . W and dW = coeff^T . h with coeff_tv = g_t (1[v = y_t] - p_tv) sech^2(raw_tv/cap).
 
     Training — design (older revision), "Implementation spec — fused linear-CE log-prob head",
@@ -342,6 +342,10 @@ def backward(h, W, labels, lse, g, cap: float = 0.0, ignore_index: int = IGNORE_
     cotangent g (onehot - softmax), times sech^2 under a softcap; Steel flash-CCE — handoff,
     Glossary D "softmax-onehot coeff". dW is the same chain rule for the weight operand of
     raw = h . W^T. Returns (dh [M, d], dW [V, d] or None) in float64.
+
+    logit_operands = (h_l, W_l): the logits (and so p, the softcap slope and lse's consistency)
+    come from raw = h_l . W_l^T while the gradient products keep h and W; the low-precision head
+    passes its dequantised FP8 operands here (see oracle/fp8.py for that reading).
     """
     h = np.asarray(h, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
@@ -350,11 +354,18 @@ def backward(h, W, labels, lse, g, cap: float = 0.0, ignore_index: int = IGNORE_
     g = np.asarray(g, dtype=np.float64)
     M, V = h.shape[0], W.shape[0]
     valid = _check_labels(labels, V, ignore_index)
+    if logit_operands is None:
+        h_l, W_l = h, W
+    else:
+        h_l = np.asarray(logit_operands[0], dtype=np.float64)
+        W_l = np.asarray(logit_operands[1], dtype=np.float64)
+        if h_l.shape != h.shape or W_l.shape != W.shape:
+            raise OracleError("logit operands must have the shapes of h and W")
     dh = np.zeros_like(h)
     dW = np.zeros_like(W) if want_dW else None
     for r0 in range(0, M, rows):
         r1 = min(M, r0 + rows)
-        raw = h[r0:r1] @ W.T
+        raw = h_l[r0:r1] @ W_l.T
         p = np.exp(softcap(raw, cap) - lse[r0:r1, None])
         onehot = np.zeros_like(raw)
         for i in range(r1 - r0):
