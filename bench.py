@@ -19,6 +19,7 @@ import time
 
 PEAK_BF16 = 2.5e15       # MI355X dense bf16 MFMA, FLOP/s
 PEAK_F32 = 157.3e12      # MI355X fp32 (vector and MFMA)
+PEAK_FP8 = 5.0e15        # MI355X dense fp8 MFMA, FLOP/s
 HBM_PEAK = 8.0e12        # bytes/s
 
 
@@ -37,6 +38,9 @@ def parse():
                     help="the loss between the head's forward and backward")
     ap.add_argument("--skip-eps", type=float, default=0.0,
                     help="backward coefficient filter threshold (0 = exact backward)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the FP8 head (row-wise E4M3 logit operands; an approximation, reported "
+                         "with its distance from the exact head)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--mfma-peak", nargs="?", const="both", default=None,
@@ -228,9 +232,12 @@ def main():
             obj["old_logp"] = pre.logp + obj.pop("old_noise")
             obj["ref_logp"] = pre.logp + obj.pop("ref_noise")
             del pre
+    if args.fp8 and (cfg.q4 or cfg.dtype != "bf16"):
+        print("--fp8 approximates a bf16 head: pick a bf16 workload", file=sys.stderr)
+        sys.exit(2)
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
                       want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj,
-                      skip_eps=args.skip_eps)
+                      skip_eps=args.skip_eps, fp8=args.fp8)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -258,6 +265,10 @@ def main():
     # Algorithmic work credited: valid tokens only (padding and ignored rows are processed, not
     # credited), 8 V d FLOP each (fwd 2, bwd 6; 6 V d for the dh-only 4-bit head).
     work = (6 if cfg.q4 else 8) * n_valid * cfg.V * cfg.d
+    if args.fp8:
+        # The logit GEMMs (forward 2 V d, recompute 2 V d) run at the fp8 rate, dh and dW (4 V d) at
+        # the bf16 rate: the step's peak is the harmonic mix.
+        peak_flops = 8.0 / (4.0 / PEAK_FP8 + 4.0 / PEAK_BF16)
     mfma_frac = work / (ms / 1e3) / peak_flops
 
     # Dominant kernel: the kind with the most traced time; achieved = its algorithmic FLOPs per
@@ -268,11 +279,15 @@ def main():
     n_l, tot_ms, fl = kinds[dom]
     avg_ms = tot_ms / n_l
     achieved = (fl / n_l) / (avg_ms / 1e3)
+    dom_peak = peak_flops
+    if args.fp8:   # the dominant kernel's own mix: fp8 logits, bf16 gradient products
+        dom_peak = {"fwd": PEAK_FP8, "coeff": PEAK_FP8, "dhdw": PEAK_BF16,
+                    "bwd": 6.0 / (2.0 / PEAK_FP8 + 4.0 / PEAK_BF16)}.get(dom, PEAK_BF16)
     traffic = None
     tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                          f"{cfg.name}_traffic.txt")
     t = prof_summary.read_traffic(tfile)
-    if t is not None and t[0] == dom:
+    if t is not None and t[0] == dom and not args.fp8 and args.skip_eps == 0:
         traffic = round(t[1])
     per_kernel = {k: {"launches_per_step": v[0] / args.steps, "avg_ms": v[1] / max(v[0], 1),
                       "ms_per_step": v[1] / args.steps,
@@ -291,6 +306,21 @@ def main():
         fidelity = {"dh_rel": rel(step.dh, ex.dh),
                     "dW_rel": None if step.dW is None else rel(step.dW, ex.dW),
                     "against": "the exact backward on the same batch (HIP, skip_eps = 0)"}
+        del ex
+
+    # The FP8 head: its distance from the exact head on this batch.
+    fp8_fid = None
+    if args.fp8:
+        ex = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, want_dW=True,
+                        scope=cfg.scope, objective=args.objective, obj=obj)
+        ex.step()
+        torch.cuda.synchronize()
+        rel = lambda a, b: float(torch.linalg.norm(a.float() - b.float()) / torch.linalg.norm(b.float()))
+        m = labels != synth.IGNORE_INDEX
+        fp8_fid = {"logp_rel": rel(step.logp[m], ex.logp[m]), "lse_rel": rel(step.lse, ex.lse),
+                   "loss_rel": abs(float(step.out[0]) - float(ex.out[0])) / abs(float(ex.out[0])),
+                   "dh_rel": rel(step.dh, ex.dh), "dW_rel": rel(step.dW, ex.dW),
+                   "against": "the exact bf16 head on the same batch (HIP)"}
         del ex
 
     if args.copy_calibration:
@@ -320,12 +350,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "dtype": "f32" if cfg.dtype == "f32" else ("fp8e4m3 logits, bf16 gradients" if args.fp8 else "bf16"),
         "data": "synthetic",
         "config": {
             "workload": cfg.name, "M": cfg.M, "valid_tokens": n_valid, "d": cfg.d, "V": cfg.V,
             "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam, "nll_scope": cfg.scope,
-            "objective": args.objective, "skip_eps": args.skip_eps,
+            "objective": args.objective, "skip_eps": args.skip_eps, "fp8": args.fp8,
             "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
             "parallelism": "single GPU",
         },
@@ -340,14 +370,18 @@ def main():
             "kernel": dom,
             "bound": "mfma",
             "achieved": round(achieved / 1e12, 1),
-            "peak": round(peak_flops / 1e12, 1),
+            "peak": round(dom_peak / 1e12, 1),
             "unit": "TFLOP/s",
-            "frac": round(achieved / peak_flops, 4),
+            "frac": round(achieved / dom_peak, 4),
             "traffic": traffic,
             "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         },
         "cpu_baseline": cpu,
     }
+    if args.fp8:
+        line["fp8_fidelity"] = fp8_fid
+        line["peak_note"] = ("fp8 logit GEMMs at 5.0 PFLOP/s, bf16 gradient GEMMs at 2.5: the step's "
+                             "peak is their harmonic mix")
     if args.skip_eps > 0:
         line["skip_fidelity"] = fidelity
         line["roofline"]["work"] = "the exact method's FLOP (blocks the filter skips included)"

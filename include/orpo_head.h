@@ -264,6 +264,64 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
                           float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
                           hipStream_t stream);
 
+/* ---- The FP8 head: low-precision logit operands (opt-in approximation) ----------------------
+ * The pages plan a lower-precision head ("ORPO training — design", §8.1 deferred work, the "W4A16
+ * head GEMM" item): half-width operands for the head's logit GEMM with fp32 accumulation, the
+ * forward first, the backward's gradient GEMMs left at the higher precision until a range probe
+ * clears them (their surviving coefficients are tiny tails), the exact mode kept as the parity
+ * mode. On gfx950 the next format below bf16 is the 8-bit float of its 32x32x64 MFMA, so here:
+ *   - h and W are quantised per row to FP8 E4M3 with one power-of-two scale per row
+ *     (orpo_quantize_fp8; the MFMA applies the scales itself, so the products are exact);
+ *   - orpo_head_fwd_fp8 takes logp and lse over raw = dequant(hq) . dequant(Wq)^T;
+ *   - orpo_head_bwd_fp8 recomputes those logits for the coefficients and forms dh = coeff . W and
+ *     dW = coeff^T . h with the unquantised bf16 h and W, as orpo_head_bwd does.
+ * Results differ from the exact head by the quantisation (per element at most 2^-4 relative); they
+ * match a float64 evaluation of the same definition on the same codes up to fp32 accumulation. */
+typedef struct {
+  const uint8_t* hq;     /* (device) [M, d] E4M3 codes of h, row-major                               */
+  const uint8_t* h_exp;  /* (device) [M] E8M0 row exponents: row t of h is hq[t] * 2^(h_exp[t] - 127) */
+  const uint8_t* wq;     /* (device) [V, d] E4M3 codes of W                                            */
+  const uint8_t* w_exp;  /* (device) [V] E8M0 row exponents of W                                       */
+} orpo_fp8_operands;
+
+/*
+ * orpo_quantize_fp8 — bf16 rows to E4M3 codes and power-of-two row scales.
+ *   x    (device) bf16 [rows, cols] row-major, finite, 16-byte aligned; cols a multiple of 8
+ *   q    (device) uint8 [rows, cols] out, 8-byte aligned: the E4M3 code nearest to x * 2^-e, ties to
+ *        the even code, a negative value that rounds to zero keeping its sign (code 0x80). E4M3:
+ *        1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, largest value 448; the NaN code
+ *        S.1111.111 is never produced
+ *   exps (device) uint8 [rows] out: e + 127, with 2^e the smallest power of two (e >= -127) for
+ *        which max|x| <= 448 * 2^e (e = 0 for an all-zero row)
+ * Returns ORPO_EINVAL for negative rows, cols not a positive multiple of 8, null or misaligned
+ * pointers (rows > 0). One launch on `stream`, no workspace.
+ */
+orpo_status orpo_quantize_fp8(const void* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* exps,
+                              hipStream_t stream);
+
+/*
+ * orpo_head_fwd_fp8 — orpo_head_fwd with the logits taken from FP8 operands.
+ *   desc   the bf16 head being approximated: h_fmt = w_fmt = ORPO_BF16 and d a multiple of 128
+ *          (else ORPO_EUNSUPPORTED); M, V, softcap, ignore_index, skip_eps as for orpo_head_fwd
+ *   q      the quantised h and W (orpo_quantize_fp8); NULL or a NULL member (M > 0): ORPO_EINVAL
+ *   labels, logp, lse, ws, ws_bytes, stream as for orpo_head_fwd (ws: orpo_head_fwd_workspace_bytes)
+ */
+orpo_status orpo_head_fwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operands* q,
+                              const int32_t* labels, float* logp, float* lse, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * orpo_head_bwd_fp8 — orpo_head_bwd for the FP8 head: lse from orpo_head_fwd_fp8 on the same
+ * operands, the coefficients g (onehot - softmax) sech^2 from the recomputed FP8 logits, and
+ * dh = coeff . W, dW = coeff^T . h with the bf16 h and W given here. Arguments as for
+ * orpo_head_bwd (ws: orpo_head_bwd_workspace_bytes, ORPO_DH_BF16 and ORPO_DW_ACCUMULATE honoured),
+ * plus q as for orpo_head_fwd_fp8; fwd_ws (optional) is that forward's workspace.
+ */
+orpo_status orpo_head_bwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operands* q,
+                              const void* h, orpo_weight W, const int32_t* labels,
+                              const float* lse, const float* g, void* dh, float* dW, void* ws,
+                              size_t ws_bytes, const void* fwd_ws, hipStream_t stream);
+
 /* Backward tiling: the token chunk C (a multiple of 256, default 8192) and the byte budget of one
  * coefficient tile [C, BVb] (two are used). With a budget, BVb is the largest multiple of 256 that
  * fits (at least 256). By default (0) the budget is 256 MiB and BVb is further limited to
@@ -289,7 +347,8 @@ typedef enum {
   ORPO_K_COEFF = 3,  /* backward launch with coefficient tiles only (first of a pass)    */
   ORPO_K_DHDW = 4,   /* backward launch with dh / dW tiles only (last of a pass)         */
   ORPO_K_BWD = 5,    /* backward launch with both (all the others)                       */
-  ORPO_K_COUNT = 6
+  ORPO_K_QUANT = 6,  /* FP8 row quantisation (orpo_quantize_fp8)                          */
+  ORPO_K_COUNT = 7
 } orpo_kernel_kind;
 orpo_status orpo_trace_enable(int32_t max_launches);   /* 0 disables and releases the events */
 orpo_status orpo_trace_collect(int32_t kind, int64_t* launches, double* total_ms, double* flops);

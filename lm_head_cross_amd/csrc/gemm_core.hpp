@@ -2,11 +2,13 @@
 //
 // One workgroup of 512 threads (8 wave64s) computes a 256 x 256 fp32 tile C[m][n] = sum_k
 // A[m][k] B[k][n] with the 32x32 MFMA (bf16: v_mfma_f32_32x32x16_bf16; fp32: 4 x
-// v_mfma_f32_32x32x2f32 per 8-wide k group). Waves sit in a 2 (m) x 4 (n) grid; each owns a
-// 128 x 64 sub-tile = 4 x 2 MFMA blocks = 128 accumulator registers per lane.
+// v_mfma_f32_32x32x2f32 per 8-wide k group; FP8 E4M3 with power-of-two row scales:
+// v_mfma_scale_f32_32x32x64_f8f6f4, the scales applied by the instruction itself). Waves sit in a
+// 2 (m) x 4 (n) grid; each owns a 128 x 64 sub-tile = 4 x 2 MFMA blocks = 128 accumulator
+// registers per lane.
 //
-// Operands are staged through LDS, 128 bytes of K per row per stage (64 bf16 / 32 fp32), in two
-// stages. Dense operands go global -> LDS directly (buffer_load_dwordx4 ... lds): each wave
+// Operands are staged through LDS, 128 bytes of K per row per stage (64 bf16 / 32 fp32 / 128 fp8),
+// in two stages. Dense operands go global -> LDS directly (buffer_load_dwordx4 ... lds): each wave
 // instruction fills 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16), and the buffer
 // descriptor's range check returns zeros past the operand's last valid row, so tails need no VALU
 // work and loads need no staging registers. 4-bit weights take a register path that dequantises on
@@ -39,6 +41,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -47,7 +51,6 @@ constexpr int kTile = 256;                  // tile extent in m and n
 constexpr int kKBytes = 128;                // bytes of K per stage per row
 constexpr int kStageBytes = 32768;          // LDS bytes of one operand stage
 constexpr int kLdsBytes = 4 * kStageBytes;  // A and B, two stages each
-constexpr int kKGroups = 4;                 // MFMA k groups per stage (bf16: 4 x 16, fp32: 4 x 8)
 constexpr uint32_t kBufferFlags = 0x00020000u;   // raw buffer descriptor word 3 (32-bit data format)
 
 // LDS swizzles (16-byte chunk index XOR a function of the row). K-major: row r's chunk c sits at
@@ -66,16 +69,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, in
 }
 
 // ------------------------------------------------------------------------------------------
-// Element policies: K per stage, fragment reads and the MFMA step. A fragment is 16 bytes per
-// lane: for the 32-row block starting at row0, lane l holds row row0 + l % 32 and k slots
-// kg*KG + (l / 32) * KG/2 + [0, KG/2) with KG = 16 (bf16) or 8 (fp32). Any consistent k-slot
-// assignment gives the same sum, as long as A and B use the same one.
+// Element policies: K per stage, K groups per stage, fragment reads and the MFMA step. A fragment
+// holds, for the 32-row block starting at row0, row row0 + l % 32 in lane l and a fixed set of k
+// slots of K group kg: 16 bytes per lane for bf16 (kg*16 + (l / 32) * 8 + [0, 8)) and fp32
+// (kg*8 + (l / 32) * 4 + [0, 4)), 32 bytes for fp8 (kg*64 + (l / 32) * 32 + [0, 32)). Any
+// consistent k-slot assignment gives the same sum, as long as A and B use the same one.
+// Scales: the per-row scale operands of the MFMA (an empty type where the format has none).
 // ------------------------------------------------------------------------------------------
+struct NoScales {};
+
 struct EBf16 {
   typedef __bf16 T;
   typedef bf16x8 Frag;
+  typedef NoScales Scales;
   static constexpr int kSize = 2;
   static constexpr int kBK = 64;           // K elements per stage
+  static constexpr int kGroups = 4;        // MFMA K groups per stage
+  static constexpr int kReadsK = 1;        // LDS reads per K-major fragment
+  static constexpr int kSets = 2;          // fragment register sets (2: next group read ahead)
   static constexpr int kMnRows = 64;       // rows of an MN-major stage
   static constexpr int kMnChunks = 32;     // 16-byte chunks per MN-major row
 
@@ -96,7 +107,8 @@ struct EBf16 {
     i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(Frag, v);
   }
-  static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b) {
+  template <int MB, int NB>
+  static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b, const Scales&) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
 };
@@ -104,8 +116,12 @@ struct EBf16 {
 struct EF32 {
   typedef float T;
   typedef f32x4 Frag;
+  typedef NoScales Scales;
   static constexpr int kSize = 4;
   static constexpr int kBK = 32;
+  static constexpr int kGroups = 4;
+  static constexpr int kReadsK = 1;
+  static constexpr int kSets = 2;
   static constexpr int kMnRows = 32;
   static constexpr int kMnChunks = 64;
 
@@ -124,11 +140,44 @@ struct EF32 {
     f[3] = *(const float*)(p + 3 * kMnChunks * 16);
     return f;
   }
-  static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b) {
+  template <int MB, int NB>
+  static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b, const Scales&) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
+  }
+};
+
+// FP8 E4M3 operands (K-major only: the logit GEMMs) with one power-of-two scale per row, given as
+// E8M0 exponent bytes. Scales.a holds the exponents of the lane's row in the wave's four 32-row
+// A blocks (byte mb), Scales.b those of its two B blocks (byte nb); the MFMA's byte selects pick
+// them, so C accumulates 2^(ea + eb) sum_k a_k b_k with exact products in fp32.
+struct EFp8 {
+  typedef uint8_t T;
+  typedef i32x8 Frag;
+  struct Scales {
+    int32_t a, b;
+  };
+  static constexpr int kSize = 1;
+  static constexpr int kBK = 128;
+  static constexpr int kGroups = 2;
+  static constexpr int kReadsK = 2;
+  // One register set: 32-byte fragments in two sets (96 VGPRs) and the 128 accumulators would
+  // not fit in a wave's 256 registers. A group's reads follow its MFMAs; the SIMD's other wave
+  // covers their latency.
+  static constexpr int kSets = 1;
+
+  static __device__ __forceinline__ Frag frag_k(const char* s, int row0, int kg, int l) {
+    const int r = row0 + (l & 31), c = kg * 4 + (l >> 5) * 2;
+    const i32x4 lo = *(const i32x4*)(s + r * kKBytes + ((c ^ swz_k(r)) << 4));
+    const i32x4 hi = *(const i32x4*)(s + r * kKBytes + (((c + 1) ^ swz_k(r)) << 4));
+    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  template <int MB, int NB>
+  static __device__ __forceinline__ void mma(f32x16& c, const Frag& a, const Frag& b, const Scales& sc) {
+    // Format selectors 0 / 0: both operands FP8 E4M3.
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, MB, sc.a, NB, sc.b);
   }
 };
 
@@ -294,35 +343,42 @@ struct Q4N {
 // ------------------------------------------------------------------------------------------
 // Compute one LDS stage into the wave's 4 x 2 accumulator blocks.
 // ------------------------------------------------------------------------------------------
+template <class E, bool K>
+__device__ __forceinline__ typename E::Frag frag(const char* s, int row0, int kg, int l) {
+  if constexpr (K) return E::frag_k(s, row0, kg, l);
+  else return E::frag_mn(s, row0, kg, l);
+}
+
 template <class E, bool AK, bool BK>
 __device__ __forceinline__ void load_frags(const char* sa, const char* sb, int kg, int wm, int wn,
                                            int l, typename E::Frag (&a)[4],
                                            typename E::Frag (&b)[2]) {
   // In the order the MFMAs consume them: b0, a0, b1, then a1..a3.
-  b[0] = BK ? E::frag_k(sb, wn * 64, kg, l) : E::frag_mn(sb, wn * 64, kg, l);
-  a[0] = AK ? E::frag_k(sa, wm * 128, kg, l) : E::frag_mn(sa, wm * 128, kg, l);
-  b[1] = BK ? E::frag_k(sb, wn * 64 + 32, kg, l) : E::frag_mn(sb, wn * 64 + 32, kg, l);
+  b[0] = frag<E, BK>(sb, wn * 64, kg, l);
+  a[0] = frag<E, AK>(sa, wm * 128, kg, l);
+  b[1] = frag<E, BK>(sb, wn * 64 + 32, kg, l);
 #pragma unroll
-  for (int mb = 1; mb < 4; ++mb)
-    a[mb] = AK ? E::frag_k(sa, wm * 128 + mb * 32, kg, l) : E::frag_mn(sa, wm * 128 + mb * 32, kg, l);
+  for (int mb = 1; mb < 4; ++mb) a[mb] = frag<E, AK>(sa, wm * 128 + mb * 32, kg, l);
 }
 
 // Instruction counts of one K group, for the scheduling pattern below: LDS reads per fragment
-// (one ds_read_b128 for K-major; two transposing reads (bf16) or four dword reads (fp32) for
-// MN-major) and MFMA instructions per fragment pair.
+// (ds_read_b128s for K-major: one, or two for fp8; two transposing reads (bf16) or four dword
+// reads (fp32) for MN-major) and MFMA instructions per fragment pair.
 template <class E, bool K>
-constexpr int reads_per_frag() { return K ? 1 : (E::kSize == 2 ? 2 : 4); }
+constexpr int reads_per_frag() { return K ? E::kReadsK : (E::kSize == 2 ? 2 : 4); }
 template <class E>
 constexpr int mfma_per_mma() { return E::kSize == 2 ? 1 : 4; }
 
-// The MFMAs of one K group: the wave's 4 x 2 blocks of 32 x 32.
-template <class E>
+// The MFMAs of one K group: the wave's 4 x 2 blocks of 32 x 32, in the order (0,0), (0,1), (1,0),
+// ... (block indices are template arguments: the fp8 MFMA takes its scale byte selects as
+// constants).
+template <class E, int MB = 0, int NB = 0>
 __device__ __forceinline__ void mma_group(f32x16 (&acc)[4][2], const typename E::Frag (&a)[4],
-                                          const typename E::Frag (&b)[2]) {
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) E::mma(acc[mb][nb], a[mb], b[nb]);
+                                          const typename E::Frag (&b)[2],
+                                          const typename E::Scales& sc) {
+  E::template mma<MB, NB>(acc[MB][NB], a[MB], b[NB], sc);
+  if constexpr (NB + 1 < 2) mma_group<E, MB, NB + 1>(acc, a, b, sc);
+  else if constexpr (MB + 1 < 4) mma_group<E, MB + 1, 0>(acc, a, b, sc);
 }
 
 // Pins the order of the LDS reads and MFMAs of kGroups K groups, each group's MFMAs interleaved
@@ -344,6 +400,14 @@ __device__ __forceinline__ void sched_groups() {
       if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   }
+}
+
+// An empty asm that reads and "writes" the accumulators: the MFMAs before it stay before it.
+__device__ __forceinline__ void hold_acc(f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][2]) {
@@ -371,45 +435,73 @@ struct Smem {
   __shared__ __attribute__((aligned(1024))) char name##_b1[kStageBytes]; \
   const Smem name = {name##_a0, name##_a1, name##_b0, name##_b1}
 
-// Fragments of two K groups: group kg lives in set kg & 1.
+// Fragments of E::kSets K groups: group kg lives in set kg % kSets.
 template <class E>
 struct FragSets {
-  typename E::Frag a[2][4], b[2][2];
+  typename E::Frag a[E::kSets][4], b[E::kSets][2];
 };
 
 // One K step s, reading stage (ca, cb); stage (na, nb) holds step s + 1. The workgroup barrier
 // sits before the last K group rather than at the end of the step: by then every wave holds that
 // group's fragments in registers, so its MFMAs run while the next stage's first fragments are read,
 // and the MFMA pipe does not idle on an LDS round trip after each barrier.
-//   region 1: MFMAs of groups 0..2, each with the next group's reads;
+//   region 1: MFMAs of groups 0..G-2, each with the next group's reads (G = E::kGroups);
 //   barrier:  this stage is no longer read by anyone, stage s + 1 is in LDS (own loads waited
 //             first, register-staged loads committed first); the loads of step s + 2 then go into
 //             this stage;
-//   region 2: MFMAs of group 3 with the reads of step s + 1's group 0 (issued unconditionally; on
+//   region 2: MFMAs of group G-1 with the reads of step s + 1's group 0 (issued unconditionally; on
 //             the last step they read a stale stage and are never used), then the epilogue if the
 //             step ends a tile.
-template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi>
+// Row scales (fp8): the last step of each tile fetches the next tile's scales (`scales(tile)`)
+// just before its wait for the step's loads, so they cost no wait of their own; they replace the
+// current ones after the tile's epilogue.
+template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi, class Scl>
 __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __restrict__ ca,
                                           char* __restrict__ cb, char* __restrict__ na,
                                           char* __restrict__ nb, Issue& issue, Commit& commit,
-                                          Epi& epi, FragSets<E>& f, f32x16 (&acc)[4][2], int wm,
-                                          int wn, int l) {
+                                          Epi& epi, Scl& scales, typename E::Scales& sc,
+                                          typename E::Scales& sc_next, FragSets<E>& f,
+                                          f32x16 (&acc)[4][2], int wm, int wn, int l) {
+  constexpr int kG = E::kGroups;
+  if constexpr (E::kSets == 2) {
 #pragma unroll
-  for (int kg = 0; kg < kKGroups - 1; ++kg) {
-    load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
-    mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1]);
+    for (int kg = 0; kg < kG - 1; ++kg) {
+      load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
+      mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
+    }
+    sched_groups<E, AK, BK, kG - 1>();
+  } else {
+    // One register set: the reads that refill it may not move above the MFMAs that read it (that
+    // would need a second set), nor those MFMAs below the workgroup barrier (an empty asm takes
+    // the accumulators here).
+#pragma unroll
+    for (int kg = 0; kg < kG - 1; ++kg) {
+      mma_group<E>(acc, f.a[0], f.b[0], sc);
+      hold_acc(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[0], f.b[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  sched_groups<E, AK, BK, kKGroups - 1>();
   if (s + 1 < total) commit(na, nb);
+  if ((s + 1) % nk == 0 && s + 1 < total) sc_next = scales(s / nk + 1);
   vm_wait();
   __syncthreads();
   if (s + 2 < total) issue((s + 2) / nk, (s + 2) % nk, ca, cb);
-  load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
-  mma_group<E>(acc, f.a[(kKGroups - 1) & 1], f.b[(kKGroups - 1) & 1]);
-  sched_groups<E, AK, BK, 1>();
+  if constexpr (E::kSets == 2) {
+    load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+    mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
+    sched_groups<E, AK, BK, 1>();
+  } else {
+    mma_group<E>(acc, f.a[0], f.b[0], sc);
+    hold_acc(acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+  }
   if ((s + 1) % nk == 0) {
     epi(s / nk, acc);
     if (kClear) zero_acc(acc);
+    sc = sc_next;
   }
 }
 
@@ -417,25 +509,30 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
 // barrier before the last group measured slower): the next step's loads are issued first, then the
 // MFMAs of the four groups with each group's reads one group ahead (left to the compiler's
 // schedule), then the step's epilogue, wait and barrier.
-template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi>
+template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi, class Scl>
 __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, char* __restrict__ ca,
                                               char* __restrict__ cb, char* __restrict__ na,
                                               char* __restrict__ nb, Issue& issue, Commit& commit,
-                                              Epi& epi, f32x16 (&acc)[4][2], int wm, int wn,
-                                              int l) {
+                                              Epi& epi, Scl& scales, typename E::Scales& sc,
+                                              typename E::Scales& sc_next, f32x16 (&acc)[4][2],
+                                              int wm, int wn, int l) {
+  constexpr int kG = E::kGroups;
   if (s + 1 < total) issue((s + 1) / nk, (s + 1) % nk, na, nb);
+  static_assert(E::kSets == 2, "transposing stages read the next group ahead");
   FragSets<E> f;
   load_frags<E, AK, BK>(ca, cb, 0, wm, wn, l, f.a[0], f.b[0]);
 #pragma unroll
-  for (int kg = 0; kg < kKGroups; ++kg) {
-    if (kg + 1 < kKGroups)
+  for (int kg = 0; kg < kG; ++kg) {
+    if (kg + 1 < kG)
       load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
-    mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1]);
+    mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
   }
   if (s + 1 < total) commit(na, nb);
+  if ((s + 1) % nk == 0 && s + 1 < total) sc_next = scales(s / nk + 1);
   if ((s + 1) % nk == 0) {
     epi(s / nk, acc);
     if (kClear) zero_acc(acc);
+    sc = sc_next;
   }
   vm_wait();
   __syncthreads();
@@ -446,16 +543,20 @@ __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, char* __
 //   issue(tile, ks, stageA, stageB): start the loads of step (tile, ks) into the given stages;
 //   commit(stageA, stageB): finish register-staged loads into LDS (no-op for direct loads);
 //   epi(tile, acc): runs after the tile's last K step (it must not touch LDS), then the
-//   accumulators are cleared unless kClear is false (single-tile callers read acc after the loop).
+//   accumulators are cleared unless kClear is false (single-tile callers read acc after the loop);
+//   scales(tile): the MFMA row scales of a tile (fp8; gemm_run passes none for other formats).
 // Two stages: step s + 1's loads are in flight during step s's MFMAs. The loop is unrolled by two
 // so that every step reads and fills statically known stages.
-template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi>
-__device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Issue&& issue,
-                                         Commit&& commit, Epi&& epi, f32x16 (&acc)[4][2]) {
+template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi,
+          class Scl>
+__device__ __forceinline__ void gemm_run_scaled(const Smem& sm, int n_tiles, int nk, Issue&& issue,
+                                                Commit&& commit, Epi&& epi, Scl&& scales,
+                                                f32x16 (&acc)[4][2]) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
   const int total = n_tiles * nk;
   if (total <= 0) return;
+  typename E::Scales sc = scales(0), sc_next = sc;
   issue(0, 0, sm.a0, sm.b0);
   commit(sm.a0, sm.b0);
   vm_wait();
@@ -464,10 +565,10 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
     // Transposing reads: barrier at the end of each step.
     for (int it = 0; it < total; it += 2) {
       gemm_step_end<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit,
-                                       epi, acc, wm, wn, l);
+                                       epi, scales, sc, sc_next, acc, wm, wn, l);
       if (it + 1 < total)
         gemm_step_end<E, AK, BK, kClear>(it + 1, total, nk, sm.a1, sm.b1, sm.a0, sm.b0, issue,
-                                         commit, epi, acc, wm, wn, l);
+                                         commit, epi, scales, sc, sc_next, acc, wm, wn, l);
     }
     return;
   }
@@ -475,12 +576,19 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
   FragSets<E> f;
   load_frags<E, AK, BK>(sm.a0, sm.b0, 0, wm, wn, l, f.a[0], f.b[0]);
   for (int it = 0; it < total; it += 2) {
-    gemm_step<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit, epi, f,
-                                 acc, wm, wn, l);
+    gemm_step<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit, epi,
+                                 scales, sc, sc_next, f, acc, wm, wn, l);
     if (it + 1 < total)
       gemm_step<E, AK, BK, kClear>(it + 1, total, nk, sm.a1, sm.b1, sm.a0, sm.b0, issue, commit,
-                                   epi, f, acc, wm, wn, l);
+                                   epi, scales, sc, sc_next, f, acc, wm, wn, l);
   }
+}
+
+template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi>
+__device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Issue&& issue,
+                                         Commit&& commit, Epi&& epi, f32x16 (&acc)[4][2]) {
+  gemm_run_scaled<E, AK, BK, kClear>(sm, n_tiles, nk, issue, commit, epi,
+                                     [](int) { return typename E::Scales{}; }, acc);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with

@@ -1,5 +1,7 @@
 // head_kernels.hpp — the flash-CCE ORPO head kernels for gfx950.
 //
+//   quant_fp8_kernel: bf16 rows -> FP8 E4M3 codes with one power-of-two (E8M0) scale per row, for
+//                   the low-precision logit operands.
 //   fwd_kernel    : raw = W . h^T tile by tile (MFMA), softcap, online softmax per token over the
 //                   workgroup's vocabulary split, label-logit capture -> per-split (max, sum) partials.
 //   merge_kernel  : partials of all splits -> lse, logp = z[y] - lse.
@@ -43,12 +45,97 @@ struct Softcap {
 };
 
 // ------------------------------------------------------------------------------------------
+// FP8 E4M3 row quantisation (the low-precision logit operands; "ORPO training — design", §8.1, the
+// lower-precision head GEMM item: half-width operands for the logit GEMM, fp32 accumulation). Each
+// row gets the smallest power-of-two scale 2^e with max|x| <= 448 2^e (e >= -127; e = 0 for a zero
+// row), stored as the E8M0 byte e + 127, and every element the E4M3 code nearest to x 2^-e, ties to
+// the even code, the sign kept on zero. Codes: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+// bits; S.1111.111 is NaN and never produced (|x 2^-e| <= 448 = S.1111.110).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int fp8_row_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  const float m = __builtin_frexpf(amax, &k);     // amax = m 2^k, m in [0.5, 1); 448 = 0.875 2^9
+  return max(m <= 0.875f ? k - 9 : k - 8, -127);
+}
+
+__device__ __forceinline__ uint32_t e4m3_code(float y) {   // |y| <= 448
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a < 0x1p-6f) {
+    c = (uint32_t)__builtin_rintf(a * 0x1p9f);     // subnormal grid n 2^-9; n = 8 is code 8 = 2^-6
+  } else {
+    int k;
+    const float m = __builtin_frexpf(a, &k);       // a = (2m) 2^(k-1): exponent field k - 1 + 7
+    c = (uint32_t)((k + 6) << 3) + (uint32_t)__builtin_rintf((2.f * m - 1.f) * 8.f);   // carry ok
+  }
+  return c | ((__float_as_uint(y) >> 31) << 7);
+}
+
+// One wave per row: pass 1 the row maximum, pass 2 the codes (8 per lane and iteration). cols is a
+// multiple of 8; x rows 16-byte and q rows 8-byte aligned.
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* x, int64_t rows, int64_t cols,
+                                                        uint8_t* q, uint8_t* exps) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (r >= rows) return;
+  const uint16_t* xr = x + r * cols;
+  float amax = 0.f;
+  for (int64_t c = (int64_t)l * 8; c < cols; c += 512) {
+    const u32x4 v = *(const u32x4*)(xr + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[i] & 0xFFFFu)));
+      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[i] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const int e = fp8_row_exponent(amax);
+  for (int64_t c = (int64_t)l * 8; c < cols; c += 512) {
+    const u32x4 v = *(const u32x4*)(xr + c);
+    u32x2 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = e4m3_code(__builtin_ldexpf(bf16_bits_to_f32(v[i] & 0xFFFFu), -e));
+      const uint32_t hi = e4m3_code(__builtin_ldexpf(bf16_bits_to_f32(v[i] >> 16), -e));
+      const uint32_t pair = lo | (hi << 8);
+      if (i & 1) out[i >> 1] |= pair << 16;
+      else out[i >> 1] = pair;
+    }
+    *(u32x2*)(q + r * cols + c) = out;
+  }
+  if (l == 0) exps[r] = (uint8_t)(e + 127);
+}
+
+// E8M0 exponent bytes of rows r0 + lane_row + 32 i (i < N) packed little-endian, the MFMA's
+// per-block scale word (r0 uniform, rows >= 1); rows past `rows` get 127 (2^0: their operand
+// data is zero) and read row rows - 1 instead, so every load stays in bounds. 32-bit lane
+// offsets keep the live state small.
+template <int N>
+__device__ __forceinline__ int32_t pack_row_exps(const uint8_t* e, int64_t r0, int lane_row,
+                                                 int64_t rows) {
+  const uint8_t* base = e + r0;
+  const int left = (int)min<int64_t>(rows - r0, 1 << 30);
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int rr = lane_row + 32 * i;
+    const uint32_t b = base[rr < left ? rr : left - 1];
+    v |= (rr < left ? b : 127u) << (8 * i);
+  }
+  return (int32_t)v;
+}
+
+// ------------------------------------------------------------------------------------------
 // Forward
 // ------------------------------------------------------------------------------------------
 struct FwdArgs {
-  const void* h;          // [M, d]
-  const void* w;          // [V, d] dense, or Q4Weight below
+  const void* h;          // [M, d] (FP8 codes for EFp8)
+  const void* w;          // [V, d] dense (FP8 codes for EFp8), or Q4Weight below
   Q4Weight q4;
+  const uint8_t* h_exp;   // EFp8: E8M0 row exponents of h [M] and W [V]
+  const uint8_t* w_exp;
   const int32_t* labels;  // [M]
   float* logp;            // [M]: receives z[y] here, finished by merge_kernel
   float2* part;           // [nblk, M] (max in log2 units, sum of 2^(u - max))
@@ -176,9 +263,19 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
       if (l == 0) a.tmax[((int64_t)tb * a.n_vtiles + tile0 + tile) * 8 + w] = rmax;
     }
   };
+  constexpr bool kF8 = std::is_same<E, EFp8>::value;
+  const int32_t sc_b = kF8 ? pack_row_exps<2>(a.h_exp, t0 + wn * 64, l & 31, a.M) : 0;   // fixed
+  auto scales = [&, sc_b](int tile) {
+    typename E::Scales sc{};
+    if constexpr (kF8) {
+      sc.a = pack_row_exps<4>(a.w_exp, (int64_t)(tile0 + tile) * kTile + wm * 128, l & 31, a.V);
+      sc.b = sc_b;
+    }
+    return sc;
+  };
   f32x16 acc[4][2];
   zero_acc(acc);
-  gemm_run<E, true, true>(smem, n_tiles, nk, issue, commit, epi, acc);
+  gemm_run_scaled<E, true, true>(smem, n_tiles, nk, issue, commit, epi, scales, acc);
 
   // Combine the lane pair (l, l ^ 32), then the two m-waves, and write this split's partials.
 #pragma unroll
@@ -414,6 +511,10 @@ struct BwdArgs {
   const void* h;
   const void* w;
   Q4Weight q4;
+  const void* hq;         // FP8 logit operands (coefficient recompute of the FP8 head), else null
+  const void* wq;
+  const uint8_t* h_exp;
+  const uint8_t* w_exp;
   const int32_t* labels;
   const float* lse;
   const float* g;
@@ -435,10 +536,14 @@ struct BwdArgs {
 };
 
 // Phase 1: recompute a 256 x 256 logit tile (m = vocabulary, n = token) and write its coefficients
-// coeff = g (onehot - softmax) sech^2 (bf16 or fp32) to the item's coefficient buffer.
-template <class E, bool Q4, bool SOFTCAP, bool SKIP>
+// coeff = g (onehot - softmax) sech^2 (bf16 or fp32) to the item's coefficient buffer. EL is the
+// logit operands' format: E, or EFp8 for the FP8 head (its forward's operands, so that the
+// recomputed logits are the ones its lse was taken over).
+template <class E, bool Q4, bool SOFTCAP, bool SKIP, class EL>
 __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it,
                                            int bid) {
+  constexpr bool kF8 = std::is_same<EL, EFp8>::value;
+  static_assert(!(kF8 && Q4), "FP8 logit operands come from a bf16 head");
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
   // Plain round-robin order: consecutive tiles step along the vocabulary, so an XCD's ~32
   // concurrent tiles form a ~(8 vocabulary x 4 token) group sharing 12 operand slices.
@@ -446,7 +551,7 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   const int64_t vbase = it.v0 + (int64_t)vt * kTile;  // global vocabulary row of tile row 0
   const int64_t tbase = it.c0 + (int64_t)tt * kTile;  // global token of tile column 0
   const int64_t t_end = min(a.M, it.c0 + it.C_cur);
-  const int64_t row_bytes = a.d * E::kSize;
+  const int64_t row_bytes = a.d * EL::kSize;
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
 
   if constexpr (SKIP) {
@@ -501,9 +606,9 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
   LoaderA la;
   DmaK lb;
-  if constexpr (Q4) la.init(a.q4); else la.init(a.w, row_bytes, a.V);
-  lb.init(a.h, row_bytes, t_end);
-  const int nk = (int)(a.d / E::kBK);
+  if constexpr (Q4) la.init(a.q4); else la.init(kF8 ? a.wq : a.w, row_bytes, a.V);
+  lb.init(kF8 ? a.hq : a.h, row_bytes, t_end);
+  const int nk = (int)(a.d / EL::kBK);
   auto issue = [&](int, int ks, char* sa, char* sb) {
     if constexpr (Q4) la.issue(vbase, (int64_t)ks * E::kBK, sa);
     else la.issue(vbase, (int64_t)ks * kKBytes, sa);
@@ -513,10 +618,18 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     la.commit(sa);
     lb.commit(sb);
   };
+  auto scales = [&](int) {
+    typename EL::Scales s{};
+    if constexpr (kF8) {
+      s.a = pack_row_exps<4>(a.w_exp, vbase + wm * 128, l & 31, a.V);
+      s.b = pack_row_exps<2>(a.h_exp, tbase + wn * 64, l & 31, t_end);
+    }
+    return s;
+  };
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, true, true, false>(smem, 1, nk, issue, commit, nop, acc);
+  gemm_run_scaled<EL, true, true, false>(smem, 1, nk, issue, commit, nop, scales, acc);
 
   typedef typename E::T T;
   T* out = (T*)it.coeff;
@@ -782,8 +895,9 @@ __device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, cons
 
 // One launch of the backward pipeline: [dh tiles of gm | dW tiles of gm | coefficient tiles of cf].
 // SKIP: the variant with the coefficient filter (orpo_head_desc.skip_eps > 0); the exact backward
-// compiles without any of its code.
-template <class E, bool Q4, bool SOFTCAP, bool SKIP>
+// compiles without any of its code. F8: the coefficient tiles recompute the logits from the FP8
+// operands (the dh / dW tiles are unchanged).
+template <class E, bool Q4, bool SOFTCAP, bool SKIP, bool F8 = false>
 __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
   ORPO_DECLARE_SMEM(smem);
   __shared__ uint16_t klist[SKIP ? kMaxKSteps : 1];   // K steps to run under the coefficient filter
@@ -799,7 +913,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kernel(BwdArgs a) {
     return;
   }
   b -= a.gm.n_tiles - a.gm.n_dh;
-  coeff_tile<E, Q4, SOFTCAP, SKIP>(smem, a, a.cf, b);
+  coeff_tile<E, Q4, SOFTCAP, SKIP, typename std::conditional<F8, EFp8, E>::type>(smem, a, a.cf, b);
 }
 
 }  // namespace orpo

@@ -171,7 +171,7 @@ bool bwd_plan_supported(const orpo_head_desc* d, const BwdPlan& p) {
 template <class E, bool Q4, bool SC>
 orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
   TraceScope ts(ORPO_K_FWD, 2.0 * double(a.M) * double(a.V) * double(a.d), st);
-  if constexpr (E::kSize == 2) {
+  if constexpr (E::kSize <= 2) {   // bf16, 4-bit and fp8 heads (the coefficient filter's formats)
     if (a.tmax) {
       hipLaunchKernelGGL((fwd_kernel<E, Q4, SC, true>), dim3(grid), dim3(kThreads), 0, st, a);
       return launched();
@@ -181,7 +181,7 @@ orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
   return launched();
 }
 
-template <class E, bool Q4, bool SC>
+template <class E, bool Q4, bool SC, bool F8 = false>
 orpo_status launch_bwd(const BwdArgs& a, int grid, hipStream_t st) {
   const double cf = 2.0 * double(a.cf.C_cur) * double(a.cf.BV_cur) * double(a.d) * (a.cf.n_tiles > 0);
   const double gm = (a.gm.n_tiles > a.gm.n_dh ? 4.0 : 2.0) * double(a.gm.C_cur) * double(a.gm.BV_cur) *
@@ -190,12 +190,21 @@ orpo_status launch_bwd(const BwdArgs& a, int grid, hipStream_t st) {
   TraceScope ts(kind, cf + gm, st);
   if constexpr (E::kSize == 2) {   // the coefficient filter exists for bf16 coefficients only
     if (a.skip_eps > 0.f) {
-      hipLaunchKernelGGL((bwd_kernel<E, Q4, SC, true>), dim3(grid), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((bwd_kernel<E, Q4, SC, true, F8>), dim3(grid), dim3(kThreads), 0, st, a);
       return launched();
     }
   }
-  hipLaunchKernelGGL((bwd_kernel<E, Q4, SC, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_kernel<E, Q4, SC, false, F8>), dim3(grid), dim3(kThreads), 0, st, a);
   return launched();
+}
+
+// FP8 logit operands: a bf16 head, d a multiple of 128 (one 128-byte stage of K per step), and
+// all four arrays given.
+orpo_status check_fp8(const orpo_head_desc* d, Kind k, const orpo_fp8_operands* q) {
+  if (!q) return ORPO_EINVAL;
+  if (k != kBf16 || d->d % 128 != 0) return ORPO_EUNSUPPORTED;
+  if (d->M > 0 && (!q->hq || !q->h_exp || !q->wq || !q->w_exp)) return ORPO_EINVAL;
+  return ORPO_OK;
 }
 
 Q4Weight q4_of(const orpo_head_desc* d, const orpo_weight& W) {
@@ -232,22 +241,26 @@ size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs) {
   return kHeader + round_up(size_t(n_pairs) * 15 * 8, 256);
 }
 
-orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
-                          const int32_t* labels, float* logp, float* lse, void* ws,
-                          size_t ws_bytes, hipStream_t stream) {
-  Kind k;
-  orpo_status st = check_desc(desc, &k);
-  if (st != ORPO_OK) return st;
-  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// The forward of either head: `q8` null runs the exact head on h and W, else the FP8 logit
+// operands (desc and the checks as in the entry points).
+orpo_status fwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const orpo_weight& W,
+                     const orpo_fp8_operands* q8, const int32_t* labels, float* logp, float* lse,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
   const FwdPlan p = plan_fwd(desc);
   if (!ws || ws_bytes < p.ws || (uintptr_t)ws % 256) return ORPO_ENOWS;
   if (desc->M == 0) return ORPO_OK;
-  if (!h || !labels || !logp || !lse) return ORPO_EINVAL;
+  if ((!q8 && !h) || !labels || !logp || !lse) return ORPO_EINVAL;
 
-  FwdArgs a;
-  a.h = h;
-  a.w = W.w;
+  FwdArgs a{};
+  a.h = q8 ? (const void*)q8->hq : h;
+  a.w = q8 ? (const void*)q8->wq : W.w;
   a.q4 = q4_of(desc, W);
+  a.h_exp = q8 ? q8->h_exp : nullptr;
+  a.w_exp = q8 ? q8->w_exp : nullptr;
   a.labels = labels;
   a.logp = logp;
   a.part = (float2*)((char*)ws + kHeader);
@@ -264,7 +277,9 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
   a.n_vtiles = p.n_vtiles;
   const int grid = p.n_tb * p.nblk;
   const bool sc = desc->softcap > 0.f;
-  if (k == kF32) st = sc ? launch_fwd<EF32, false, true>(a, grid, stream) : launch_fwd<EF32, false, false>(a, grid, stream);
+  orpo_status st;
+  if (q8) st = sc ? launch_fwd<EFp8, false, true>(a, grid, stream) : launch_fwd<EFp8, false, false>(a, grid, stream);
+  else if (k == kF32) st = sc ? launch_fwd<EF32, false, true>(a, grid, stream) : launch_fwd<EF32, false, false>(a, grid, stream);
   else if (k == kBf16) st = sc ? launch_fwd<EBf16, false, true>(a, grid, stream) : launch_fwd<EBf16, false, false>(a, grid, stream);
   else st = sc ? launch_fwd<EBf16, true, true>(a, grid, stream) : launch_fwd<EBf16, true, false>(a, grid, stream);
   if (st != ORPO_OK) return st;
@@ -272,6 +287,41 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)cdiv(desc->M, 256)), dim3(256), 0, stream,
                      (const float2*)a.part, p.nblk, desc->M, labels, desc->V, desc->ignore_index,
                      logp, lse, a.status);
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                          const int32_t* labels, float* logp, float* lse, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+  return fwd_impl(desc, k, h, W, nullptr, labels, logp, lse, ws, ws_bytes, stream);
+}
+
+orpo_status orpo_head_fwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operands* q,
+                              const int32_t* labels, float* logp, float* lse, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_fp8(desc, k, q)) != ORPO_OK) return st;
+  return fwd_impl(desc, k, nullptr, orpo_weight{}, q, labels, logp, lse, ws, ws_bytes, stream);
+}
+
+orpo_status orpo_quantize_fp8(const void* x, int64_t rows, int64_t cols, uint8_t* q,
+                              uint8_t* exps, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0 || rows > 4 * int64_t(INT32_MAX)) return ORPO_EINVAL;
+  if (rows == 0) return ORPO_OK;
+  if (!x || !q || !exps || (uintptr_t)x % 16 || (uintptr_t)q % 8) return ORPO_EINVAL;
+  TraceScope ts(ORPO_K_QUANT, 0.0, stream);
+  hipLaunchKernelGGL(quant_fp8_kernel, dim3((unsigned)cdiv(rows, 4)), dim3(256), 0, stream,
+                     (const uint16_t*)x, rows, cols, q, exps);
   return launched();
 }
 
@@ -407,14 +457,16 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
   return launched();
 }
 
-orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
-                          const int32_t* labels, const float* lse, const float* g, void* dh,
-                          float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
-                          hipStream_t stream) {
-  Kind k;
-  orpo_status st = check_desc(desc, &k);
-  if (st != ORPO_OK) return st;
-  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// The backward of either head (q8: the FP8 head's logit operands for the coefficient recompute).
+orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const orpo_weight& W,
+                     const orpo_fp8_operands* q8, const int32_t* labels, const float* lse,
+                     const float* g, void* dh, float* dW, void* ws, size_t ws_bytes,
+                     const void* fwd_ws, hipStream_t stream) {
+  orpo_status st;
   if (k == kQ4 && dW) return ORPO_EUNSUPPORTED;
   if ((desc->flags & ORPO_DH_BF16) && k == kF32) return ORPO_EUNSUPPORTED;
   const BwdPlan p = plan_bwd(desc, k);
@@ -423,10 +475,16 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
   if (desc->M == 0) return ORPO_OK;
   if (!h || !labels || !lse || !g || !dh) return ORPO_EINVAL;
 
-  BwdArgs a;
+  BwdArgs a{};
   a.h = h;
   a.w = W.w;
   a.q4 = q4_of(desc, W);
+  if (q8) {
+    a.hq = q8->hq;
+    a.wq = q8->wq;
+    a.h_exp = q8->h_exp;
+    a.w_exp = q8->w_exp;
+  }
   a.labels = labels;
   a.lse = lse;
   a.g = g;
@@ -486,12 +544,40 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
     a.cf = make_item(i, false);
     a.gm = make_item(i - 1, true);
     const int grid = a.cf.n_tiles + a.gm.n_tiles;
-    if (k == kF32) st = sc ? launch_bwd<EF32, false, true>(a, grid, stream) : launch_bwd<EF32, false, false>(a, grid, stream);
+    if (q8) st = sc ? launch_bwd<EBf16, false, true, true>(a, grid, stream) : launch_bwd<EBf16, false, false, true>(a, grid, stream);
+    else if (k == kF32) st = sc ? launch_bwd<EF32, false, true>(a, grid, stream) : launch_bwd<EF32, false, false>(a, grid, stream);
     else if (k == kBf16) st = sc ? launch_bwd<EBf16, false, true>(a, grid, stream) : launch_bwd<EBf16, false, false>(a, grid, stream);
     else st = sc ? launch_bwd<EBf16, true, true>(a, grid, stream) : launch_bwd<EBf16, true, false>(a, grid, stream);
     if (st != ORPO_OK) return st;
   }
   return ORPO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                          const int32_t* labels, const float* lse, const float* g, void* dh,
+                          float* dW, void* ws, size_t ws_bytes, const void* fwd_ws,
+                          hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+  return bwd_impl(desc, k, h, W, nullptr, labels, lse, g, dh, dW, ws, ws_bytes, fwd_ws, stream);
+}
+
+orpo_status orpo_head_bwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operands* q,
+                              const void* h, orpo_weight W, const int32_t* labels,
+                              const float* lse, const float* g, void* dh, float* dW, void* ws,
+                              size_t ws_bytes, const void* fwd_ws, hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+  if ((st = check_fp8(desc, k, q)) != ORPO_OK) return st;
+  return bwd_impl(desc, k, h, W, q, labels, lse, g, dh, dW, ws, ws_bytes, fwd_ws, stream);
 }
 
 orpo_status orpo_set_bwd_tiling(int64_t chunk_tokens, size_t coeff_bytes) {

@@ -37,6 +37,11 @@ class Weight(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
 
 
+class Fp8Operands(ctypes.Structure):
+    _fields_ = [("hq", ctypes.c_void_p), ("h_exp", ctypes.c_void_p), ("wq", ctypes.c_void_p),
+                ("w_exp", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _SIGS = {
     "orpo_head_fwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Desc)]),
@@ -57,6 +62,11 @@ _SIGS = {
                                       ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P]),
     "orpo_head_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P, _P]),
+    "orpo_quantize_fp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
+    "orpo_head_fwd_fp8": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Fp8Operands), _P, _P,
+                                         _P, _P, ctypes.c_size_t, _P]),
+    "orpo_head_bwd_fp8": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Fp8Operands), _P,
+                                         Weight, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "orpo_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
     "orpo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orpo_last_hip_error": (ctypes.c_int32, []),
@@ -66,7 +76,7 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "orpo_trace_reset": (ctypes.c_int, []),
 }
-KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw", 5: "bwd"}
+KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw", 5: "bwd", 6: "quant"}
 _lib = None
 
 
@@ -242,6 +252,84 @@ def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNOR
 
 
 # ------------------------------------------------------------------------------------------------
+# The FP8 head: row-wise E4M3 logit operands (an opt-in approximation of the bf16 head)
+# ------------------------------------------------------------------------------------------------
+def quantize_fp8(x, q=None, exps=None):
+    """E4M3 codes [R, C] (uint8) and E8M0 row exponents [R] (uint8) of a bf16 matrix x [R, C]."""
+    _need_dtype("x", x, torch.bfloat16)
+    _need_dtype("q", q, torch.uint8)
+    _need_dtype("exps", exps, torch.uint8)
+    _need_gpu(x, q, exps)
+    R, C = x.shape
+    if q is None:
+        q = torch.empty(R, C, dtype=torch.uint8, device=x.device)
+    if exps is None:
+        exps = torch.empty(R, dtype=torch.uint8, device=x.device)
+    if q.shape != x.shape or exps.shape != (R,):
+        raise OrpoError("q must have the shape of x and exps one entry per row")
+    _check(lib().orpo_quantize_fp8(_ptr(x), R, C, _ptr(q), _ptr(exps), _stream(x.device)),
+           "orpo_quantize_fp8")
+    return q, exps
+
+
+def _fp8_operands(hq, h_exp, wq, w_exp):
+    for name, t in (("hq", hq), ("h_exp", h_exp), ("wq", wq), ("w_exp", w_exp)):
+        _need_dtype(name, t, torch.uint8)
+    _need_gpu(hq, h_exp, wq, w_exp)
+    if hq.shape[0] != h_exp.shape[0] or wq.shape[0] != w_exp.shape[0] or hq.shape[1] != wq.shape[1]:
+        raise OrpoError("FP8 operand shapes disagree")
+    return Fp8Operands(hq.data_ptr(), h_exp.data_ptr(), wq.data_ptr(), w_exp.data_ptr())
+
+
+def head_fwd_fp8(hq, h_exp, wq, w_exp, labels, softcap=0.0, ignore_index=IGNORE_INDEX,
+                 return_ws=False, skip_eps=0.0):
+    """logp[M], lse[M] of the FP8 head: logits from the quantised operands (quantize_fp8)."""
+    _need_dtype("labels", labels, torch.int32)
+    q8 = _fp8_operands(hq, h_exp, wq, w_exp)
+    _need_gpu(hq, labels)
+    M, d = hq.shape
+    V = wq.shape[0]
+    desc = make_desc(M, d, V, torch.bfloat16, ORPO_BF16, softcap, ignore_index, skip_eps=skip_eps)
+    L = lib()
+    ws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(desc)), hq.device)
+    logp = torch.empty(M, dtype=torch.float32, device=hq.device)
+    lse = torch.empty(M, dtype=torch.float32, device=hq.device)
+    _check(L.orpo_head_fwd_fp8(ctypes.byref(desc), ctypes.byref(q8), _ptr(labels), _ptr(logp),
+                               _ptr(lse), _ptr(ws), ws.numel(), _stream(hq.device)), "orpo_head_fwd_fp8")
+    return (logp, lse, ws) if return_ws else (logp, lse)
+
+
+def head_bwd_fp8(hq, h_exp, wq, w_exp, h, w, labels, lse, g, softcap=0.0, want_dW=True,
+                 ignore_index=IGNORE_INDEX, dW=None, accumulate=False, skip_eps=0.0, fwd_ws=None,
+                 dh_bf16=False):
+    """dh, dW of the FP8 head: coefficients from the quantised logits, products with bf16 h, W."""
+    _head_dtypes(h, w, labels)
+    _need_dtype("h", h, torch.bfloat16)
+    _need_dtype("lse", lse, torch.float32)
+    _need_dtype("g", g, torch.float32)
+    _need_dtype("dW", dW, torch.float32)
+    q8 = _fp8_operands(hq, h_exp, wq, w_exp)
+    _need_gpu(hq, h, w, labels, lse, g, dW, fwd_ws)
+    M, d = h.shape
+    V = w.shape[0]
+    if hq.shape != (M, d) or wq.shape != (V, d):
+        raise OrpoError("FP8 operands must have the shapes of h and w")
+    flags = (ORPO_DW_ACCUMULATE if accumulate else 0) | (ORPO_DH_BF16 if dh_bf16 else 0)
+    desc = make_desc(M, d, V, h.dtype, ORPO_BF16, softcap, ignore_index, flags, skip_eps)
+    L = lib()
+    ws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc)), h.device)
+    dh = torch.empty(M, d, dtype=torch.bfloat16 if dh_bf16 else torch.float32, device=h.device)
+    if want_dW and dW is None:
+        dW = torch.empty(V, d, dtype=torch.float32, device=h.device)
+    if not want_dW:
+        dW = None
+    _check(L.orpo_head_bwd_fp8(ctypes.byref(desc), ctypes.byref(q8), _ptr(h), Weight(w.data_ptr()),
+                               _ptr(labels), _ptr(lse), _ptr(g), _ptr(dh), _ptr(dW), _ptr(ws),
+                               ws.numel(), _ptr(fwd_ws), _stream(h.device)), "orpo_head_bwd_fp8")
+    return dh, dW
+
+
+# ------------------------------------------------------------------------------------------------
 # Tracing (HIP event pairs recorded by the library around each of its launches)
 # ------------------------------------------------------------------------------------------------
 def trace_enable(max_launches: int):
@@ -318,14 +406,16 @@ def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip
 class HeadStep:
     def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
                  want_dW=True, ignore_index=IGNORE_INDEX, scope="response", objective="orpo",
-                 obj=None, skip_eps=0.0, dh_bf16=False):
+                 obj=None, skip_eps=0.0, dh_bf16=False, fp8=False):
         """One head step: forward -> loss -> backward on preallocated buffers.
 
         objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
         backward, with its parameters and inputs in `obj`: "simpo" {beta, gamma}, "dpo" {beta,
         ref_sums [2P] float64}, "ipo" / "hinge" {beta, optional ref_sums}, "grpo" {clip_eps,
         beta, old_logp [M], ref_logp [M], advantages [S] float32, seg_offsets are then [S+1]
-        completions}. dh_bf16: dh as bfloat16 (the fp32 sums rounded once)."""
+        completions}. dh_bf16: dh as bfloat16 (the fp32 sums rounded once). fp8: the FP8 head (an
+        approximation): each step quantises h and W to row-wise E4M3 (part of the step) and takes
+        the logits from them; the gradient products keep the bf16 h and W."""
         if objective != "orpo" and objective != "grpo" and objective not in PREF_KINDS:
             raise OrpoError(f"unknown objective {objective!r}")
         o = dict(obj or {})
@@ -361,12 +451,33 @@ class HeadStep:
         self.dW = torch.empty(V, self.d, dtype=torch.float32, device=dev) if want_dW else None
         self.wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
                          None if biases is None else biases.data_ptr())
+        self.fp8 = bool(fp8)
+        if self.fp8:
+            if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or scales is not None:
+                raise OrpoError("the FP8 head approximates a bf16 head")
+            self.hq = torch.empty(self.M, self.d, dtype=torch.uint8, device=dev)
+            self.h_exp = torch.empty(self.M, dtype=torch.uint8, device=dev)
+            self.wq = torch.empty(V, self.d, dtype=torch.uint8, device=dev)
+            self.w_exp = torch.empty(V, dtype=torch.uint8, device=dev)
+            self.q8 = Fp8Operands(self.hq.data_ptr(), self.h_exp.data_ptr(), self.wq.data_ptr(),
+                                  self.w_exp.data_ptr())
         self.stream = None
 
     def _s(self):
         return _stream(self.h.device)
 
     def forward(self):
+        if self.fp8:
+            L = lib()
+            _check(L.orpo_quantize_fp8(_ptr(self.h), self.M, self.d, _ptr(self.hq), _ptr(self.h_exp),
+                                       self._s()), "orpo_quantize_fp8")
+            _check(L.orpo_quantize_fp8(_ptr(self.w), self.V, self.d, _ptr(self.wq), _ptr(self.w_exp),
+                                       self._s()), "orpo_quantize_fp8")
+            _check(L.orpo_head_fwd_fp8(ctypes.byref(self.desc), ctypes.byref(self.q8),
+                                       _ptr(self.labels), _ptr(self.logp), _ptr(self.lse),
+                                       _ptr(self.fws), self.fws.numel(), self._s()),
+                   "orpo_head_fwd_fp8")
+            return
         _check(lib().orpo_head_fwd(ctypes.byref(self.desc), _ptr(self.h), self.wt, _ptr(self.labels),
                                    _ptr(self.logp), _ptr(self.lse), _ptr(self.fws), self.fws.numel(),
                                    self._s()), "orpo_head_fwd")
@@ -394,6 +505,13 @@ class HeadStep:
                   self.lws.numel(), self._s()), "orpo_loss")
 
     def backward(self):
+        if self.fp8:
+            _check(lib().orpo_head_bwd_fp8(ctypes.byref(self.desc), ctypes.byref(self.q8),
+                                           _ptr(self.h), self.wt, _ptr(self.labels), _ptr(self.lse),
+                                           _ptr(self.g), _ptr(self.dh), _ptr(self.dW),
+                                           _ptr(self.bws), self.bws.numel(), _ptr(self.fws),
+                                           self._s()), "orpo_head_bwd_fp8")
+            return
         _check(lib().orpo_head_bwd(ctypes.byref(self.desc), _ptr(self.h), self.wt, _ptr(self.labels),
                                    _ptr(self.lse), _ptr(self.g), _ptr(self.dh), _ptr(self.dW),
                                    _ptr(self.bws), self.bws.numel(), _ptr(self.fws), self._s()),
@@ -405,4 +523,7 @@ class HeadStep:
         self.backward()
 
     def workspace_bytes(self) -> int:
-        return self.fws.numel() + self.bws.numel() + self.lws.numel()
+        n = self.fws.numel() + self.bws.numel() + self.lws.numel()
+        if self.fp8:
+            n += self.hq.numel() + self.h_exp.numel() + self.wq.numel() + self.w_exp.numel()
+        return n

@@ -84,17 +84,21 @@ def row_exponent(amax: float) -> int:
     return max(e, MIN_EXP)
 
 
-def quantize_rows(x) -> tuple[np.ndarray, np.ndarray]:
-    """Row-wise E4M3 codes [R, C] (uint8) and E8M0 row exponents [R] (uint8, exponent + 127)."""
-    x = np.asarray(x, dtype=np.float64)
+def quantize_rows(x, block: int = 1024) -> tuple[np.ndarray, np.ndarray]:
+    """Row-wise E4M3 codes [R, C] (uint8) and E8M0 row exponents [R] (uint8, exponent + 127).
+    Rows are independent; `block` rows are encoded per call only to bound the memory used."""
+    x = np.asarray(x)
     if x.ndim != 2:
         raise ValueError("quantize_rows takes a matrix")
-    codes = np.zeros(x.shape, dtype=np.uint8)
-    exps = np.zeros(x.shape[0], dtype=np.uint8)
-    for r in range(x.shape[0]):
-        e = row_exponent(np.max(np.abs(x[r])) if x.shape[1] else 0.0)
-        codes[r] = e4m3_encode(np.ldexp(x[r], -e))
-        exps[r] = e + E8M0_BIAS
+    R, C = x.shape
+    codes = np.zeros((R, C), dtype=np.uint8)
+    exps = np.zeros(R, dtype=np.uint8)
+    for r0 in range(0, R, block):
+        xb = np.asarray(x[r0:r0 + block], dtype=np.float64)
+        amax = np.abs(xb).max(axis=1) if C else np.zeros(len(xb))
+        e = np.array([row_exponent(a) for a in amax], dtype=np.int64)
+        codes[r0:r0 + block] = e4m3_encode(np.ldexp(xb, -e[:, None]))
+        exps[r0:r0 + block] = (e + E8M0_BIAS).astype(np.uint8)
     return codes, exps
 
 

@@ -249,3 +249,37 @@ def test_binding_rejects_wrong_dtypes_before_any_launch():
     with pytest.raises(H.OrpoError, match="unknown objective"):
         H.HeadStep(h.bfloat16(), w.bfloat16(), lab.int(), torch.zeros(3, dtype=torch.int32), 8, 0.0,
                    0.1, objective="kto")
+
+
+def test_fp8_entry_points_validate_before_any_launch():
+    L = H.lib()
+    ws = (ctypes.c_char * 1024)()
+    base = ctypes.addressof(ws) + (-ctypes.addressof(ws)) % 256
+    q8 = H.Fp8Operands(4096, 4096, 4096, 4096)
+    d = _desc(M=512, d=256, V=4096, cap=30.0)
+    fws = L.orpo_head_fwd_workspace_bytes(ctypes.byref(d))
+    assert fws > 256
+    # Valid request, one byte of workspace short: ENOWS (nothing launched).
+    assert L.orpo_head_fwd_fp8(ctypes.byref(d), ctypes.byref(q8), 16, 16, 16, base, fws - 1, None) == ENOWS
+    assert L.orpo_head_fwd_fp8(ctypes.byref(d), None, 16, 16, 16, base, 1 << 30, None) == EINVAL
+    assert L.orpo_head_fwd_fp8(ctypes.byref(d), ctypes.byref(H.Fp8Operands(4096, None, 4096, 4096)),
+                               16, 16, 16, base, 1 << 30, None) == EINVAL
+    d64 = _desc(M=512, d=192, V=4096)                       # d not a multiple of 128
+    assert L.orpo_head_fwd_fp8(ctypes.byref(d64), ctypes.byref(q8), 16, 16, 16, base, 1 << 30, None) == EUNSUP
+    f32 = _desc(h=H.ORPO_F32, w=H.ORPO_F32)                 # the FP8 head approximates a bf16 head
+    assert L.orpo_head_fwd_fp8(ctypes.byref(f32), ctypes.byref(q8), 16, 16, 16, base, 1 << 30, None) == EUNSUP
+    bws = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
+    w = H.Weight(16, None, None)
+    assert L.orpo_head_bwd_fp8(ctypes.byref(d), ctypes.byref(q8), 16, w, 16, 16, 16, 16, 16, base,
+                               bws - 1, None, None) == ENOWS
+    assert L.orpo_head_bwd_fp8(ctypes.byref(d64), ctypes.byref(q8), 16, w, 16, 16, 16, 16, 16, base,
+                               1 << 30, None, None) == EUNSUP
+    assert L.orpo_head_bwd_fp8(ctypes.byref(d), None, 16, w, 16, 16, 16, 16, 16, base, 1 << 30,
+                               None, None) == EINVAL
+    # Quantisation: shape and alignment checks.
+    assert L.orpo_quantize_fp8(4096, 4, 12, 4096, 4096, None) == EINVAL      # cols % 8
+    assert L.orpo_quantize_fp8(4096, -1, 64, 4096, 4096, None) == EINVAL
+    assert L.orpo_quantize_fp8(4104, 4, 64, 4096, 4096, None) == EINVAL      # x not 16-byte aligned
+    assert L.orpo_quantize_fp8(4096, 4, 64, 4100, 4096, None) == EINVAL      # q not 8-byte aligned
+    assert L.orpo_quantize_fp8(None, 4, 64, 4096, 4096, None) == EINVAL
+    assert L.orpo_quantize_fp8(None, 0, 64, None, None, None) == 0           # nothing to do
