@@ -87,6 +87,7 @@ struct EBf16 {
   static constexpr int kGroups = 4;        // MFMA K groups per stage
   static constexpr int kReadsK = 1;        // LDS reads per K-major fragment
   static constexpr int kSets = 2;          // fragment register sets (2: next group read ahead)
+  static constexpr int kSwzK = 7;          // K-major swizzle mask (swz_k)
   static constexpr int kMnRows = 64;       // rows of an MN-major stage
   static constexpr int kMnChunks = 32;     // 16-byte chunks per MN-major row
 
@@ -122,6 +123,7 @@ struct EF32 {
   static constexpr int kGroups = 4;
   static constexpr int kReadsK = 1;
   static constexpr int kSets = 2;
+  static constexpr int kSwzK = 7;
   static constexpr int kMnRows = 32;
   static constexpr int kMnChunks = 64;
 
@@ -167,11 +169,15 @@ struct EFp8 {
   // not fit in a wave's 256 registers. A group's reads follow its MFMAs; the SIMD's other wave
   // covers their latency.
   static constexpr int kSets = 1;
+  // Swizzle r & 6: an even XOR keeps a fragment's two chunks (c even, c + 1) adjacent, so both
+  // reads share one address register (offsets 0 and 16); the 8 rows of a read phase still cover
+  // 8 distinct (row parity, chunk) bank groups.
+  static constexpr int kSwzK = 6;
 
   static __device__ __forceinline__ Frag frag_k(const char* s, int row0, int kg, int l) {
-    const int r = row0 + (l & 31), c = kg * 4 + (l >> 5) * 2;
-    const i32x4 lo = *(const i32x4*)(s + r * kKBytes + ((c ^ swz_k(r)) << 4));
-    const i32x4 hi = *(const i32x4*)(s + r * kKBytes + (((c + 1) ^ swz_k(r)) << 4));
+    const int r = row0 + (l & 31), c = (kg * 4 + (l >> 5) * 2) ^ (r & kSwzK);
+    const i32x4 lo = *(const i32x4*)(s + r * kKBytes + (c << 4));
+    const i32x4 hi = *(const i32x4*)(s + r * kKBytes + (c << 4) + 16);
     return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   template <int MB, int NB>
@@ -192,8 +198,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint
 // instructions i = 0..3 filling LDS bytes [(4w + i) KiB, +1 KiB), lane l the chunk 64 (4w + i) + l.
 // ------------------------------------------------------------------------------------------
 
-// K-major operand: rows [row0, row0 + 256) of a row-major matrix, bytes [kb, kb + 128) of each row.
-struct DmaK {
+// K-major operand: rows [row0, row0 + 256) of a row-major matrix, bytes [kb, kb + 128) of each row,
+// chunk c of row r stored at chunk c ^ (r & kSwzMask).
+template <int kSwzMask>
+struct DmaKS {
   const char* base;
   int64_t ld, n_rows;
   uint32_t voff[4];
@@ -205,7 +213,7 @@ struct DmaK {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = (4 * w + i) * 64 + l;
-      const int r = j >> 3, c = (j & 7) ^ swz_k(j >> 3);
+      const int r = j >> 3, c = (j & 7) ^ ((j >> 3) & kSwzMask);
       voff[i] = (uint32_t)(r * ld_bytes + c * 16);
     }
   }
@@ -217,6 +225,7 @@ struct DmaK {
   }
   __device__ __forceinline__ void commit(char*) const {}
 };
+typedef DmaKS<7> DmaK;   // swz_k
 
 // MN-major operand: rows [k0, k0 + kMnRows) of a row-major matrix, bytes [cb, cb + kMnChunks*16).
 template <class E>
@@ -402,6 +411,15 @@ __device__ __forceinline__ void sched_groups() {
   }
 }
 
+// Row scales fetched before a step's wait are taken here, right after it: the compiler then counts
+// their loads as done at this point and does not place its own wait for them after the next
+// step's direct loads are issued (which would make the fragment reads wait for those loads).
+__device__ __forceinline__ void hold_scales(NoScales&) {}
+template <class S>
+__device__ __forceinline__ void hold_scales(S& sc) {
+  asm volatile("" : "+v"(sc.a), "+v"(sc.b));
+}
+
 // An empty asm that reads and "writes" the accumulators: the MFMAs before it stay before it.
 __device__ __forceinline__ void hold_acc(f32x16 (&acc)[4][2]) {
 #pragma unroll
@@ -441,6 +459,54 @@ struct FragSets {
   typename E::Frag a[E::kSets][4], b[E::kSets][2];
 };
 
+// One K group with streamed fragments (policies with one fragment set), in two parts. The group's
+// B pair and first A block are in f on entry. group_head reads A blocks 1..3 of group kg of stage
+// sa, each under the two MFMAs of the block before, and returns block 3; group_tail reads the next
+// group's B pair and first A block (group nkg of stage (nsa, nsb)) under the last two MFMAs. At
+// most six fragments are live at once and each read has two MFMAs to land. The stage's workgroup
+// barrier goes between the last group's head and tail: every read of the stage is then done, and
+// the last two MFMAs overlap the next stage's first reads.
+template <class E, bool AK, bool BK>
+__device__ __forceinline__ typename E::Frag group_head(f32x16 (&acc)[4][2], const FragSets<E>& f,
+                                                       const char* __restrict__ sa, int kg,
+                                                       const typename E::Scales& sc, int wm, int l) {
+  constexpr int kR = reads_per_frag<E, AK>();
+  const typename E::Frag a1 = frag<E, AK>(sa, wm * 128 + 32, kg, l);
+  E::template mma<0, 0>(acc[0][0], f.a[0][0], f.b[0][0], sc);
+  E::template mma<0, 1>(acc[0][1], f.a[0][0], f.b[0][1], sc);
+  const typename E::Frag a2 = frag<E, AK>(sa, wm * 128 + 64, kg, l);
+  E::template mma<1, 0>(acc[1][0], a1, f.b[0][0], sc);
+  E::template mma<1, 1>(acc[1][1], a1, f.b[0][1], sc);
+  const typename E::Frag a3 = frag<E, AK>(sa, wm * 128 + 96, kg, l);
+  E::template mma<2, 0>(acc[2][0], a2, f.b[0][0], sc);
+  E::template mma<2, 1>(acc[2][1], a2, f.b[0][1], sc);
+  __builtin_amdgcn_sched_group_barrier(0x100, kR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  return a3;
+}
+
+template <class E, bool AK, bool BK>
+__device__ __forceinline__ void group_tail(f32x16 (&acc)[4][2], FragSets<E>& f,
+                                           const typename E::Frag& a3, const char* __restrict__ nsa,
+                                           const char* __restrict__ nsb, int nkg,
+                                           const typename E::Scales& sc, int wm, int wn, int l) {
+  constexpr int kR = reads_per_frag<E, AK>(), kRb = reads_per_frag<E, BK>();
+  const typename E::Frag nb0 = frag<E, BK>(nsb, wn * 64, nkg, l);
+  const typename E::Frag na0 = frag<E, AK>(nsa, wm * 128, nkg, l);
+  const typename E::Frag nb1 = frag<E, BK>(nsb, wn * 64 + 32, nkg, l);
+  E::template mma<3, 0>(acc[3][0], a3, f.b[0][0], sc);
+  E::template mma<3, 1>(acc[3][1], a3, f.b[0][1], sc);
+  f.a[0][0] = na0;
+  f.b[0][0] = nb0;
+  f.b[0][1] = nb1;
+  __builtin_amdgcn_sched_group_barrier(0x100, kR + 2 * kRb, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
 // One K step s, reading stage (ca, cb); stage (na, nb) holds step s + 1. The workgroup barrier
 // sits before the last K group rather than at the end of the step: by then every wave holds that
 // group's fragments in registers, so its MFMAs run while the next stage's first fragments are read,
@@ -463,6 +529,7 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
                                           typename E::Scales& sc_next, FragSets<E>& f,
                                           f32x16 (&acc)[4][2], int wm, int wn, int l) {
   constexpr int kG = E::kGroups;
+  typename E::Frag a_last;   // streamed path: the last group's A block 3, across the barrier
   if constexpr (E::kSets == 2) {
 #pragma unroll
     for (int kg = 0; kg < kG - 1; ++kg) {
@@ -471,21 +538,22 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
     }
     sched_groups<E, AK, BK, kG - 1>();
   } else {
-    // One register set: the reads that refill it may not move above the MFMAs that read it (that
-    // would need a second set), nor those MFMAs below the workgroup barrier (an empty asm takes
-    // the accumulators here).
+    // Streamed fragments: whole groups, then the last group's head; its tail follows the barrier.
+    // The MFMAs may not move below the barrier (an empty asm takes the accumulators here), where
+    // they would hold more fragments live.
 #pragma unroll
     for (int kg = 0; kg < kG - 1; ++kg) {
-      mma_group<E>(acc, f.a[0], f.b[0], sc);
-      hold_acc(acc);
-      __builtin_amdgcn_sched_barrier(0);
-      load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[0], f.b[0]);
+      const typename E::Frag a3 = group_head<E, AK, BK>(acc, f, ca, kg, sc, wm, l);
+      group_tail<E, AK, BK>(acc, f, a3, ca, cb, kg + 1, sc, wm, wn, l);
     }
+    a_last = group_head<E, AK, BK>(acc, f, ca, kG - 1, sc, wm, l);
+    hold_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (s + 1 < total) commit(na, nb);
   if ((s + 1) % nk == 0 && s + 1 < total) sc_next = scales(s / nk + 1);
   vm_wait();
+  hold_scales(sc_next);
   __syncthreads();
   if (s + 2 < total) issue((s + 2) / nk, (s + 2) % nk, ca, cb);
   if constexpr (E::kSets == 2) {
@@ -493,10 +561,7 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
     mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
     sched_groups<E, AK, BK, 1>();
   } else {
-    mma_group<E>(acc, f.a[0], f.b[0], sc);
-    hold_acc(acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+    group_tail<E, AK, BK>(acc, f, a_last, na, nb, 0, sc, wm, wn, l);
   }
   if ((s + 1) % nk == 0) {
     epi(s / nk, acc);

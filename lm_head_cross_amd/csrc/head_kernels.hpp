@@ -174,9 +174,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   }
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
 
-  typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K, DmaKS<E::kSwzK>>::type LoaderA;
   LoaderA la;
-  DmaK lb;
+  DmaKS<E::kSwzK> lb;
   if constexpr (Q4) la.init(a.q4); else la.init(a.w, row_bytes, a.V);
   lb.init(a.h, row_bytes, a.M);
   const int nk = (int)(a.d / E::kBK);
@@ -603,9 +603,9 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     }
   }
 
-  typedef typename std::conditional<Q4, Q4K, DmaK>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K, DmaKS<EL::kSwzK>>::type LoaderA;
   LoaderA la;
-  DmaK lb;
+  DmaKS<EL::kSwzK> lb;
   if constexpr (Q4) la.init(a.q4); else la.init(kF8 ? a.wq : a.w, row_bytes, a.V);
   lb.init(kF8 ? a.hq : a.h, row_bytes, t_end);
   const int nk = (int)(a.d / EL::kBK);
