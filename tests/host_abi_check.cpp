@@ -9,6 +9,7 @@
 //   - an entry point refuses with EINVAL / EUNSUPPORTED where the size query says 0, and asks for
 //     more workspace (ENOWS) otherwise,
 //   - no size arithmetic overflows (UBSan) and no host memory is touched out of bounds (ASan).
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -72,6 +73,22 @@ void check_head(const orpo_head_desc& d) {
     else if (with_dw && d.w_fmt == ORPO_Q4G64) EXPECT(st == ORPO_EUNSUPPORTED);   // frozen head
     else EXPECT(st == ORPO_ENOWS);
   }
+  // The FP8 head: the same sizes; refused unless the head is bf16 with d a multiple of 128.
+  const orpo_fp8_operands q8 = {(const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p,
+                                (const uint8_t*)p};
+  const bool fp8_ok = d.h_fmt == ORPO_BF16 && d.w_fmt == ORPO_BF16 && d.d % 128 == 0;
+  st = orpo_head_fwd_fp8(&d, &q8, (const int32_t*)p, (float*)p, (float*)p, fake(kWs),
+                         fw ? fw - 1 : std::numeric_limits<size_t>::max(), nullptr);
+  if (fw == 0) EXPECT(refused(st));
+  else EXPECT(st == (fp8_ok ? ORPO_ENOWS : ORPO_EUNSUPPORTED));
+  EXPECT(orpo_head_fwd_fp8(&d, nullptr, (const int32_t*)p, (float*)p, (float*)p, fake(kWs),
+                           std::numeric_limits<size_t>::max(), nullptr) != ORPO_OK);
+  st = orpo_head_bwd_fp8(&d, &q8, p, w, (const int32_t*)p, (const float*)p, (const float*)p, p,
+                         (float*)p, fake(kWs), bw ? bw - 1 : std::numeric_limits<size_t>::max(),
+                         nullptr, nullptr);
+  if (bw == 0) EXPECT(refused(st));
+  else if (!fp8_ok) EXPECT(st == ORPO_EUNSUPPORTED);
+  else EXPECT(st == ORPO_ENOWS);
   // A misaligned workspace of any size is refused as ENOWS once the descriptor is valid.
   st = orpo_head_fwd(&d, p, w, (const int32_t*)p, (float*)p, (float*)p, fake(kWs + 64),
                      std::numeric_limits<size_t>::max(), nullptr);
@@ -195,6 +212,23 @@ void sweep_losses() {
         }
 }
 
+void sweep_quantize() {
+  const int64_t I64 = std::numeric_limits<int64_t>::max();
+  for (int64_t rows : {int64_t(-1), int64_t(0), int64_t(1), int64_t(1) << 33, I64})
+    for (int64_t cols : {int64_t(-8), int64_t(0), int64_t(4), int64_t(8), int64_t(2560), I64})
+      for (uintptr_t xo : {uintptr_t(0), uintptr_t(8)})
+        for (uintptr_t qo : {uintptr_t(0), uintptr_t(4)}) {
+          const bool shape_ok = rows >= 0 && cols > 0 && cols % 8 == 0 && rows <= 4 * int64_t(INT32_MAX);
+          if (shape_ok && rows > 0 && !xo && !qo) continue;   // valid: it would launch
+          const orpo_status st = orpo_quantize_fp8(fake(kPtr + xo), rows, cols,
+                                                   (uint8_t*)fake(kPtr + qo), (uint8_t*)fake(kPtr),
+                                                   nullptr);
+          if (!shape_ok) EXPECT(st == ORPO_EINVAL);
+          else if (rows == 0) EXPECT(st == ORPO_OK);
+          else EXPECT(st == ORPO_EINVAL);                    // misaligned x or q
+        }
+}
+
 void check_misc() {
   for (int64_t s : {int64_t(std::numeric_limits<int32_t>::min()), int64_t(-5), int64_t(-4),
                     int64_t(-1), int64_t(0), int64_t(1), int64_t(std::numeric_limits<int32_t>::max())})
@@ -222,6 +256,7 @@ int main() {
   sweep_head();
   sweep_tiling();
   sweep_losses();
+  sweep_quantize();
   check_misc();
   std::printf("%s: %ld checks, %ld failures\n", g_fails ? "FAILED" : "ok", g_checks, g_fails);
   return g_fails ? 1 : 0;
