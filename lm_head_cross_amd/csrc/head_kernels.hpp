@@ -762,11 +762,45 @@ __device__ __forceinline__ int build_klist(const uint8_t* flags, int nk, int par
   return total;
 }
 
+// Row offset of accumulator element r within its 32 x 32 block (acc_m(wm, mb, r, l) - acc_m(wm, mb, 0, l)).
+__device__ __forceinline__ int acc_dr(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// dh / dW tile store: out (+)= acc in fp32 (first: overwrite). A whole tile (the usual case) goes
+// through a buffer descriptor over its 256 rows: each 32 x 32 block is one per-lane offset plus a
+// uniform row offset per element, and its 16 previous values are all read before any is added, so
+// a lane waits for memory 8 times per tile. Element by element (the tail path) each read is its
+// own round trip.
 template <class E>
 __device__ __forceinline__ void store_out(float* out, int64_t ld, int64_t row0, int64_t n_rows,
                                           int64_t col0, int64_t n_cols, bool first,
                                           const f32x16 (&acc)[4][2]) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
+  if (row0 + kTile <= n_rows && col0 + kTile <= n_cols) {
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc((const char*)(out + row0 * ld + col0), (int64_t)kTile * ld * 4);
+    const int ldb = (int)(ld * 4);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int vo = acc_m(wm, mb, 0, l) * ldb + acc_n(wn, nb, l) * 4;
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = acc[mb][nb][r];
+        if (!first) {
+          float prev[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            prev[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, vo, acc_dr(r) * ldb, 0));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = prev[r] + v[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), rs, vo, acc_dr(r) * ldb, 0);
+      }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int64_t col = col0 + acc_n(wn, nb, l);
@@ -791,6 +825,36 @@ __device__ __forceinline__ void store_out_bf16(uint16_t* out16, const float* pre
                                                int64_t col0, int64_t n_cols,
                                                const f32x16 (&acc)[4][2]) {
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
+  if (row0 + kTile <= n_rows && col0 + kTile <= n_cols) {   // whole tile: as store_out
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(prev ? (const char*)(prev + prow0 * ld + col0) : nullptr, prev ? (int64_t)kTile * ld * 4 : 0);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc((const char*)(out16 + row0 * ld + col0), (int64_t)kTile * ld * 2);
+    const int ldb = (int)(ld * 4);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int m0 = acc_m(wm, mb, 0, l), n = acc_n(wn, nb, l);
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = acc[mb][nb][r];
+        if (prev) {
+          float pv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            pv[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, m0 * ldb + n * 4,
+                                                                                  acc_dr(r) * ldb, 0));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = pv[r] + v[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(pack_bf16x2(v[r], 0.f) & 0xffffu), ro,
+                                                m0 * (ldb / 2) + n * 2, acc_dr(r) * (ldb / 2), 0);
+      }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int64_t col = col0 + acc_n(wn, nb, l);
