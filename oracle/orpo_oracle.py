@@ -379,7 +379,8 @@ def backward(h, W, labels, lse, g, cap: float = 0.0, ignore_index: int = IGNORE_
 
 
 def backward_filtered(h, W, labels, lse, g, cap: float, eps: float,
-                      ignore_index: int = IGNORE_INDEX, tok_block: int = 256, k_slice: int = 64):
+                      ignore_index: int = IGNORE_INDEX, tok_block: int = 256, k_slice: int = 64,
+                      logit_operands=None):
     """The backward with the coefficient filter: dh and dW from coefficients whose negligible
     blocks are dropped.
 
@@ -390,7 +391,7 @@ def backward_filtered(h, W, labels, lse, g, cap: float, eps: float,
     tok_block tokens x k_slice vocabulary entries, for dW (K = tokens) tok_block vocabulary entries
     x k_slice tokens, aligned to multiples of their sizes from index 0. A block is dropped when
     max |coeff| over it is < eps. eps = 0 is the exact backward. Returns (dh, dW, kept_dh, kept_dw)
-    with the kept fractions of the blocks.
+    with the kept fractions of the blocks. logit_operands as for backward().
     """
     h = np.asarray(h, dtype=np.float64)
     W = np.asarray(W, dtype=np.float64)
@@ -399,7 +400,9 @@ def backward_filtered(h, W, labels, lse, g, cap: float, eps: float,
     g = np.asarray(g, dtype=np.float64)
     M, V = h.shape[0], W.shape[0]
     valid = _check_labels(labels, V, ignore_index)
-    raw = h @ W.T
+    h_l, W_l = (h, W) if logit_operands is None else (np.asarray(logit_operands[0], dtype=np.float64),
+                                                      np.asarray(logit_operands[1], dtype=np.float64))
+    raw = h_l @ W_l.T
     p = np.exp(softcap(raw, cap) - lse[:, None])
     onehot = np.zeros_like(raw)
     for t in range(M):

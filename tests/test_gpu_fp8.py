@@ -197,3 +197,34 @@ def test_fp8_full_size_sampled_parity():
     e_dh, e_dW = rel(dh[probe], rdh), rel(st.dW.cpu().numpy(), rdW)
     say(f"[fp8 fullsize] probe={len(probe)} dh={e_dh:.2e} dW={e_dW:.2e}")
     assert e_dh <= TOL_GRAD and e_dW <= TOL_GRAD
+
+
+def test_fp8_step_with_the_coefficient_filter():
+    # The FP8 head with skip_eps (filter + the cold-tile skip from the FP8 forward's per-tile
+    # maxima) against the oracle's filtered backward on the same quantised logits. Peaked logits
+    # (std 12 under the softcap), 95 % argmax labels, eps 1e-5.
+    cfg = synth.HeadConfig(0, "fp8-peaked", M=1024, d=256, V=16384, pairs=2, len_lo=200,
+                           len_hi=256, softcap=30.0, lam=0.1, w_std=12.0, p_argmax=0.95)
+    inp = synth.make_inputs(cfg, 0, label_device="cuda")
+    d = dev()
+    labels = torch.from_numpy(inp.labels).to(d)
+    off = torch.from_numpy(inp.seg_offsets).to(d)
+    eps = 1e-5
+    say("[fp8 filter] peaked eps=1e-5")
+    st = H.HeadStep(inp.h.to(d), inp.w.to(d), labels, off, cfg.V, cfg.softcap, cfg.lam, fp8=True,
+                    skip_eps=eps)
+    st.step()
+    torch.cuda.synchronize()
+    hh, W = _f64(inp.h), _f64(inp.w)
+    hq, he = fp8.quantize_rows(hh)
+    wq, we = fp8.quantize_rows(W)
+    ops = (fp8.dequantize_rows(hq, he), fp8.dequantize_rows(wq, we))
+    ora = orc.head_step(ops[0], ops[1], inp.labels, inp.seg_offsets, cfg.softcap, cfg.lam,
+                        want_dW=False)
+    assert rel(st.logp.cpu().numpy(), ora["logp"]) <= TOL_SCALAR
+    fh, fw, kh, kw = orc.backward_filtered(hh, W, inp.labels, ora["lse"], ora["g"], cfg.softcap, eps,
+                                           logit_operands=ops)
+    e_dh, e_dW = rel(st.dh.cpu().numpy(), fh), rel(st.dW.cpu().numpy(), fw)
+    say(f"[fp8 filter] kept dh {kh:.3f} dW {kw:.3f}; vs oracle filtered dh={e_dh:.2e} dW={e_dW:.2e}")
+    assert kh < 0.9 and kw < 0.9                        # the filter does drop blocks here
+    assert e_dh <= TOL_GRAD and e_dW <= TOL_GRAD

@@ -166,3 +166,29 @@ def test_split_backward_matches_finite_differences_through_the_logit_operands(ca
     assert np.allclose(a1 + a2, a3, rtol=1e-12, atol=1e-14)
     assert np.allclose(b1 + b2, b3, rtol=1e-12, atol=1e-14)
     assert not np.allclose(a1, a2)
+
+
+@pytest.mark.parametrize("cap", [0.0, 2.0])
+def test_filtered_backward_with_logit_operands_reduces_to_its_special_cases(cap):
+    h, W, labels, off = _tiny(21, cap)
+    rng = np.random.default_rng(22)
+    h_l = h + 0.05 * rng.standard_normal(h.shape)
+    W_l = W + 0.05 * rng.standard_normal(W.shape)
+    ref = orc.head_step(h_l, W_l, labels, off, cap, 0.2)
+    ops = (h_l, W_l)
+    dh, dW = orc.backward(h, W, labels, ref["lse"], ref["g"], cap, logit_operands=ops)
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, ref["lse"], ref["g"], cap, 0.0,
+                                           tok_block=4, k_slice=2, logit_operands=ops)
+    assert kh == 1.0 and kw == 1.0                      # eps = 0: the split backward itself
+    assert np.allclose(fh, dh, rtol=1e-12, atol=1e-15) and np.allclose(fw, dW, rtol=1e-12, atol=1e-15)
+    fh, fw, kh, kw = orc.backward_filtered(h, W, labels, ref["lse"], ref["g"], cap, 1e9,
+                                           tok_block=4, k_slice=2, logit_operands=ops)
+    assert kh == 0.0 and kw == 0.0 and np.all(fh == 0) and np.all(fw == 0)
+    # A middle eps keeps some blocks, decided on the coefficients of the logit operands: the same
+    # call without them (logits from h and W) keeps a different set here.
+    eps = np.quantile(np.abs(ref["g"][ref["g"] != 0]), 0.5) * 0.05
+    a = orc.backward_filtered(h, W, labels, ref["lse"], ref["g"], cap, eps, tok_block=4, k_slice=2,
+                              logit_operands=ops)
+    b = orc.backward_filtered(h, W, labels, ref["lse"], ref["g"], cap, eps, tok_block=4, k_slice=2)
+    assert 0.0 < a[2] < 1.0
+    assert not np.allclose(a[0], b[0])
