@@ -97,6 +97,7 @@ CASES = [
     (600, 256, 3000, 2, 100, 150, 30.0),      # ragged M and V, two chunks of tiles
     (512, 384, 4096, 2, 100, 128, 0.0),       # no softcap, d = 3 x 128
     (1000, 128, 5000, 3, 100, 160, 30.0),     # one K step (d = 128), ragged V
+    (300, 256, 100, 1, 100, 120, 30.0),       # V below one tile: every scale read past V
 ]
 
 
