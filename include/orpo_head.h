@@ -265,8 +265,8 @@ orpo_status orpo_head_bwd(const orpo_head_desc* desc, const void* h, orpo_weight
                           hipStream_t stream);
 
 /* ---- The FP8 head: low-precision logit operands (opt-in approximation) ----------------------
- * The pages plan a lower-precision head ("ORPO training — design", §8.1 deferred work, the "W4A16
- * head GEMM" item): half-width operands for the head's logit GEMM with fp32 accumulation, the
+ * The pages plan a lower-precision head ("Training — design", §8.1 "Deferred performance levers",
+ * the W4A16 head GEMM item): half-width operands for the head's logit GEMM with fp32 accumulation, the
  * forward first, the backward's gradient GEMMs left at the higher precision until a range probe
  * clears them (their surviving coefficients are tiny tails), the exact mode kept as the parity
  * mode. On gfx950 the next format below bf16 is the 8-bit float of its 32x32x64 MFMA, so here:

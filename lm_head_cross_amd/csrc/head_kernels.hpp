@@ -45,8 +45,9 @@ struct Softcap {
 };
 
 // ------------------------------------------------------------------------------------------
-// FP8 E4M3 row quantisation (the low-precision logit operands; "ORPO training — design", §8.1, the
-// lower-precision head GEMM item: half-width operands for the logit GEMM, fp32 accumulation). Each
+// FP8 E4M3 row quantisation (the low-precision logit operands; "Training — design", §8.1 "Deferred
+// performance levers", the W4A16 head GEMM item: half-width operands for the logit GEMM, fp32
+// accumulation). Each
 // row gets the smallest power-of-two scale 2^e with max|x| <= 448 2^e (e >= -127; e = 0 for a zero
 // row), stored as the E8M0 byte e + 127, and every element the E4M3 code nearest to x 2^-e, ties to
 // the even code, the sign kept on zero. Codes: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa

@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE, NOT PRODUCT CODE (like the rest of this package): only the tests, the smoke
 check and the bench's CPU-baseline leg may import it. It shares no code with the HIP path.
 
-The pages' lower-precision head is a plan, not a design ("ORPO training — design", §8.1 deferred
-work, the "W4A16 head GEMM" item): half-precision operands for the head's logit GEMM, forward
+The pages' lower-precision head is a plan, not a design ("Training — design", §8.1 "Deferred
+performance levers", the W4A16 head GEMM item): half-precision operands for the head's logit GEMM, forward
 first, the backward's gradient GEMMs left at the higher precision until a range probe clears them,
 fp32 accumulation throughout, and the exact mode kept as the parity mode. On gfx950 the half step
 below bf16 is an 8-bit float, so the reading built here is:
