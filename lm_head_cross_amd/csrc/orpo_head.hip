@@ -79,7 +79,7 @@ struct TraceScope {
 
 constexpr float kMaxSoftcap = 40.f;
 
-// Format combinations this build implements.
+// Format combinations the library implements.
 enum Kind { kF32, kBf16, kQ4, kBad };
 
 orpo_status check_desc(const orpo_head_desc* d, Kind* kind) {
