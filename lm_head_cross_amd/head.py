@@ -420,6 +420,11 @@ class HeadStep:
             raise OrpoError(f"unknown objective {objective!r}")
         o = dict(obj or {})
         _head_dtypes(h, w, labels, scales, biases)
+        if fp8:
+            if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or scales is not None:
+                raise OrpoError("the FP8 head approximates a bf16 head")
+            if h.shape[1] % 128:
+                raise OrpoError(f"the FP8 head needs d a multiple of 128 (d = {h.shape[1]})")
         _need_dtype("seg_offsets", seg_offsets, torch.int32)
         _need_dtype("ref_sums", o.get("ref_sums"), torch.float64)
         for k in ("old_logp", "ref_logp", "advantages"):
@@ -453,8 +458,6 @@ class HeadStep:
                          None if biases is None else biases.data_ptr())
         self.fp8 = bool(fp8)
         if self.fp8:
-            if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16 or scales is not None:
-                raise OrpoError("the FP8 head approximates a bf16 head")
             self.hq = torch.empty(self.M, self.d, dtype=torch.uint8, device=dev)
             self.h_exp = torch.empty(self.M, dtype=torch.uint8, device=dev)
             self.wq = torch.empty(V, self.d, dtype=torch.uint8, device=dev)

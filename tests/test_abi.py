@@ -246,6 +246,12 @@ def test_binding_rejects_wrong_dtypes_before_any_launch():
     # Right dtypes on the CPU: refused for placement, still before anything is launched.
     with pytest.raises(H.OrpoError, match="on a GPU"):
         H.head_fwd(h.bfloat16(), w.bfloat16(), lab.int())
+    with pytest.raises(H.OrpoError, match="multiple of 128"):
+        H.HeadStep(h.bfloat16(), w.bfloat16(), lab.int(), torch.zeros(3, dtype=torch.int32), 8, 0.0,
+                   0.1, fp8=True)
+    with pytest.raises(H.OrpoError, match="approximates a bf16 head"):
+        H.HeadStep(h.float(), w.float(), lab.int(), torch.zeros(3, dtype=torch.int32), 8, 0.0, 0.1,
+                   fp8=True)
     with pytest.raises(H.OrpoError, match="unknown objective"):
         H.HeadStep(h.bfloat16(), w.bfloat16(), lab.int(), torch.zeros(3, dtype=torch.int32), 8, 0.0,
                    0.1, objective="kto")
