@@ -73,39 +73,65 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {   // |y| <= 448
   return c | ((__float_as_uint(y) >> 31) << 7);
 }
 
-// One wave per row: pass 1 the row maximum, pass 2 the codes (8 per lane and iteration). cols is a
-// multiple of 8; x rows 16-byte and q rows 8-byte aligned.
+// The codes of 8 consecutive bf16 values (one 16-byte load) at row exponent e.
+__device__ __forceinline__ u32x2 e4m3_codes8(const u32x4& v, int e) {
+  u32x2 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = e4m3_code(__builtin_ldexpf(bf16_bits_to_f32(v[i] & 0xFFFFu), -e));
+    const uint32_t hi = e4m3_code(__builtin_ldexpf(bf16_bits_to_f32(v[i] >> 16), -e));
+    const uint32_t pair = lo | (hi << 8);
+    if (i & 1) out[i >> 1] |= pair << 16;
+    else out[i >> 1] = pair;
+  }
+  return out;
+}
+
+__device__ __forceinline__ float amax8(float m, const u32x4& v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(v[i] & 0xFFFFu)));
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(v[i] >> 16)));
+  }
+  return m;
+}
+
+// One wave per row: the row maximum, then the codes (8 per lane and iteration). Rows of up to
+// kQuantHeld x 512 values are read once and held in registers between the two passes; longer rows
+// are read twice. cols is a multiple of 8; x rows 16-byte and q rows 8-byte aligned.
+constexpr int kQuantHeld = 8;
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* x, int64_t rows, int64_t cols,
                                                         uint8_t* q, uint8_t* exps) {
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int l = threadIdx.x & 63;
   if (r >= rows) return;
   const uint16_t* xr = x + r * cols;
+  uint8_t* qr = q + r * cols;
   float amax = 0.f;
-  for (int64_t c = (int64_t)l * 8; c < cols; c += 512) {
-    const u32x4 v = *(const u32x4*)(xr + c);
+  if (cols <= kQuantHeld * 512) {
+    u32x4 v[kQuantHeld];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[i] & 0xFFFFu)));
-      amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v[i] >> 16)));
+    for (int i = 0; i < kQuantHeld; ++i) {
+      const int64_t c = (int64_t)l * 8 + i * 512;
+      v[i] = c < cols ? *(const u32x4*)(xr + c) : u32x4{0u, 0u, 0u, 0u};
+      amax = amax8(amax, v[i]);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const int e = fp8_row_exponent(amax);
+#pragma unroll
+    for (int i = 0; i < kQuantHeld; ++i) {
+      const int64_t c = (int64_t)l * 8 + i * 512;
+      if (c < cols) *(u32x2*)(qr + c) = e4m3_codes8(v[i], e);
+    }
+    if (l == 0) exps[r] = (uint8_t)(e + 127);
+    return;
   }
+  for (int64_t c = (int64_t)l * 8; c < cols; c += 512) amax = amax8(amax, *(const u32x4*)(xr + c));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const int e = fp8_row_exponent(amax);
-  for (int64_t c = (int64_t)l * 8; c < cols; c += 512) {
-    const u32x4 v = *(const u32x4*)(xr + c);
-    u32x2 out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = e4m3_code(__builtin_ldexpf(bf16_bits_to_f32(v[i] & 0xFFFFu), -e));
-      const uint32_t hi = e4m3_code(__builtin_ldexpf(bf16_bits_to_f32(v[i] >> 16), -e));
-      const uint32_t pair = lo | (hi << 8);
-      if (i & 1) out[i >> 1] |= pair << 16;
-      else out[i >> 1] = pair;
-    }
-    *(u32x2*)(q + r * cols + c) = out;
-  }
+  for (int64_t c = (int64_t)l * 8; c < cols; c += 512) *(u32x2*)(qr + c) = e4m3_codes8(*(const u32x4*)(xr + c), e);
   if (l == 0) exps[r] = (uint8_t)(e + 127);
 }
 

@@ -79,6 +79,13 @@ def test_quantisation_matches_the_oracle_bit_for_bit():
     assert np.array_equal(e, ref_e), np.nonzero(e != ref_e)
     bad = np.argwhere(q != ref_q)
     assert bad.size == 0, (bad[:5], q[tuple(bad[0])], ref_q[tuple(bad[0])])
+    # Rows longer than the kernel holds in registers (read twice), and rows of one 8-value chunk.
+    for shape in ((9, 4608), (5, 8)):
+        xl = torch.from_numpy(rng.standard_normal(shape) * 3.0).to(torch.bfloat16)
+        rq, re_ = fp8.quantize_rows(_f64(xl))
+        ql, el = H.quantize_fp8(xl.to(dev()))
+        torch.cuda.synchronize()
+        assert np.array_equal(el.cpu().numpy(), re_) and np.array_equal(ql.cpu().numpy(), rq), shape
     # An e4b-sized weight (262144 x 2560, entries N(0, (3 / sqrt(d))^2) as the workloads draw
     # them), exactly, in blocks.
     V, dd = 262144, 2560
