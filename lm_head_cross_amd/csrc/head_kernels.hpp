@@ -222,26 +222,37 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     const int64_t vw0 = vt0 + wm * 128;              // first vocabulary row of this wave
     const bool tail = vt0 + kTile > a.V;
     float rmax = kNegInf;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      // u = z * log2e (or (z - cap) * log2e under a softcap), masked past V on the last tile only
-      // (a uniform branch). Values are recomputed from the accumulators in each pass.
+    // u = z * log2e (or (z - cap) * log2e under a softcap), masked past V on the last tile only.
+    // The uniform branch on the tail encloses the whole epilogue, so that the per-element masks
+    // exist on that path alone. Values are recomputed from the accumulators in each pass.
+    auto run = [&](auto masked_tag) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
       // Valid rows of the wave, less this lane's row offset 4 (l / 32), so that each element's test
       // compares a compile-time constant (nothing per element is kept live across the K loop).
-      const int lim = (int)min<int64_t>(max<int64_t>(a.V - vw0, 0), 128) - 4 * (l >> 5);
-      auto body = [&](auto masked_tag) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        auto keep = [&](int mb, int r) {
-          return !kMasked || mb * 32 + 8 * (r >> 2) + (r & 3) < lim;
+      const int lim = kMasked ? (int)min<int64_t>(max<int64_t>(a.V - vw0, 0), 128) - 4 * (l >> 5)
+                              : 128;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // Each pass over the elements tests against its own copy of the limit, opaque to the
+        // compiler, so the tests sit where they are used instead of 64 lane masks shared between
+        // passes staying live in scalar registers.
+        auto fresh_lim = [&]() {
+          int v = lim;
+          if constexpr (kMasked) asm volatile("" : "+v"(v));
+          return v;
+        };
+        auto keep_below = [](int lim_p, int mb, int r) {
+          return !kMasked || mb * 32 + 8 * (r >> 2) + (r & 3) < lim_p;
         };
         float ref = m[nb];
         if (!SOFTCAP) {
+          const int lim_max = fresh_lim();
           float tmax = kNegInf;
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (keep(mb, r)) tmax = fmaxf(tmax, acc[mb][nb][r]);
+              if (keep_below(lim_max, mb, r)) tmax = fmaxf(tmax, acc[mb][nb][r]);
           const float mn = fmaxf(m[nb], tmax * kLog2e);
           if (mn != kNegInf) {
             s[nb] *= exp2_(m[nb] - mn);   // m = -inf gives 0
@@ -251,6 +262,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
         }
         float acc_s = 0.f;
         if (ref != kNegInf) {
+          const int lim_sum = fresh_lim();
 #pragma unroll
           for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -258,32 +270,33 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
               const float raw = acc[mb][nb][r];
               const float x = SOFTCAP ? sc.kz * sc.r_of(raw) : raw * kLog2e - ref;
               const float e = exp2_(x);
-              acc_s += keep(mb, r) ? e : 0.f;
-              if constexpr (TMAX) rmax = fmaxf(rmax, keep(mb, r) ? raw : kNegInf);
+              const bool keep = keep_below(lim_sum, mb, r);
+              acc_s += keep ? e : 0.f;
+              if constexpr (TMAX) rmax = fmaxf(rmax, keep ? raw : kNegInf);
             }
         }
-        return acc_s;
-      };
-      const float acc_s = tail ? body(std::true_type{}) : body(std::false_type{});
-      s[nb] += acc_s;
-      // Target capture: the one lane holding (v = y, t) writes z[y] to logp[t].
-      const int64_t off = (int64_t)y[nb] - vw0;
-      const bool mine = off >= 0 && off < 128 && (((int)off >> 2) & 1) == (l >> 5);
-      if (__builtin_expect(__ballot(mine) != 0, 0)) {
-        if (mine) {
-          const int o = (int)off, mb = o >> 5, ro = o & 31;
-          const int r = ((ro >> 3) << 2) | (ro & 3);
-          float zsel = 0.f;
+        s[nb] += acc_s;
+        // Target capture: the one lane holding (v = y, t) writes z[y] to logp[t].
+        const int64_t off = (int64_t)y[nb] - vw0;
+        const bool mine = off >= 0 && off < 128 && (((int)off >> 2) & 1) == (l >> 5);
+        if (__builtin_expect(__ballot(mine) != 0, 0)) {
+          if (mine) {
+            const int o = (int)off, mb = o >> 5, ro = o & 31;
+            const int r = ((ro >> 3) << 2) | (ro & 3);
+            float zsel = 0.f;
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm)
+            for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-              if (mm == mb && rr == r) zsel = acc[mm][nb][rr];
-          const float z = SOFTCAP ? sc.cap - 2.f * sc.cap * sc.r_of(zsel) : zsel;
-          a.logp[tok[nb]] = z;
+              for (int rr = 0; rr < 16; ++rr)
+                if (mm == mb && rr == r) zsel = acc[mm][nb][rr];
+            const float z = SOFTCAP ? sc.cap - 2.f * sc.cap * sc.r_of(zsel) : zsel;
+            a.logp[tok[nb]] = z;
+          }
         }
       }
-    }
+    };
+    if (tail) run(std::true_type{});
+    else run(std::false_type{});
     if constexpr (TMAX) {
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
@@ -683,6 +696,10 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     T* row = out + (tk - it.c0) * a.BVb + (vbase - it.v0);
     auto body = [&](auto masked_tag) {
       constexpr bool kMasked = decltype(masked_tag)::value;
+      // This half's own copy of the limit, opaque to the compiler, so that each element is tested
+      // where it is stored rather than through 64 lane masks kept live in scalar registers.
+      int lim_nb = lim;
+      if constexpr (kMasked) asm volatile("" : "+v"(lim_nb));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -699,7 +716,7 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
             } else {
               c = G * exp2_(__builtin_fmaf(raw, kLog2e, -L2));
             }
-            if (kMasked && !(mb * 32 + 8 * rg + ri < lim)) c = 0.f;
+            if (kMasked && !(mb * 32 + 8 * rg + ri < lim_nb)) c = 0.f;
             vals[ri] = c;
             if constexpr (SKIP) cmax[mb >> 1] = fmaxf(cmax[mb >> 1], fabsf(c));
           }
