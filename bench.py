@@ -26,13 +26,15 @@ HBM_PEAK = 8.0e12        # bytes/s
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="e4b-bf16-softcap30",
                     help="workload name (lm_head_cross_amd.synth.WORKLOADS) or its integer key")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    ap.add_argument("--trace-steps", type=int, default=5,
+                    help="steps of the separate traced pass (per-kernel HIP events) after the timed region")
     ap.add_argument("--objective", default="orpo",
                     choices=["orpo", "simpo", "dpo", "ipo", "hinge", "grpo"],
                     help="the loss between the head's forward and backward")
@@ -78,9 +80,21 @@ def _objective_inputs(objective: str, cfg, off: np.ndarray, n_valid_per_span: np
 
 
 def cpu_baseline(inp, rows: int, objective: str):
-    """The float64 oracle as it stands, on a bounded sample of the same batch, on the host cores."""
+    """The float64 oracle as it stands, on a bounded sample of the same batch, on the host cores
+    this process may run on (BLAS threads pinned to that count)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
+    n_cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=n_cores):
+        res = _cpu_baseline(inp, rows, objective)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    res["cores"] = int(min(threads, n_cores))
+    res["affinity_cores"] = n_cores
+    return res
+
+
+def _cpu_baseline(inp, rows: int, objective: str):
+    import numpy as np
     from oracle import objectives as ob
     from oracle import orpo_oracle as orc
     from lm_head_cross_amd import synth
@@ -126,9 +140,8 @@ def cpu_baseline(inp, rows: int, objective: str):
         out = ep
     dt = time.perf_counter() - t0
     assert math.isfinite(out["loss"])
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {
-        "value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "value": rows / dt, "unit": "tokens/s", "kind": "oracle",
         "sample": f"first {rows} tokens of the same batch (full V={cfg.V}, d={cfg.d}), float64 "
                   f"forward + {objective} loss + backward{' + dW' if not cfg.q4 else ''}; {dt:.1f} s",
     }
@@ -246,17 +259,32 @@ def main():
     loss0 = float(step.out[0].item())
     assert math.isfinite(loss0), "non-finite loss"
 
-    H.trace_enable(max(64, 200 * args.steps))
-    H.trace_reset()
+    # Headline: exactly `steps` steps, nothing traced; events on the launch stream mark the step
+    # boundaries for the per-step median.
+    stream = torch.cuda.current_stream(dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step.step()
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    peak = torch.cuda.max_memory_allocated()
+    free_b, total_b = torch.cuda.mem_get_info(dev)
+    reserved = torch.cuda.memory_reserved(dev)
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+
+    # Per-kernel times: a separate traced pass (HIP event pairs around every launch).
+    n_tr = max(1, args.trace_steps)
+    H.trace_enable(max(64, 200 * n_tr))
+    H.trace_reset()
+    for _ in range(n_tr):
+        step.step()
+    torch.cuda.synchronize()
     tr = H.trace_collect()
     H.trace_enable(0)
-    peak = torch.cuda.max_memory_allocated()
 
     ms = (t1 - t0) * 1e3 / args.steps
     n_valid = inp.n_valid
@@ -289,8 +317,8 @@ def main():
     t = prof_summary.read_traffic(tfile)
     if t is not None and t[0] == dom and not args.fp8 and args.skip_eps == 0:
         traffic = round(t[1])
-    per_kernel = {k: {"launches_per_step": v[0] / args.steps, "avg_ms": v[1] / max(v[0], 1),
-                      "ms_per_step": v[1] / args.steps,
+    per_kernel = {k: {"launches_per_step": v[0] / n_tr, "avg_ms": v[1] / max(v[0], 1),
+                      "ms_per_step": v[1] / n_tr,
                       "tflops": (v[2] / (v[1] / 1e3) / 1e12) if v[1] > 0 and v[2] > 0 else None}
                   for k, v in kinds.items()}
 
@@ -347,6 +375,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "median_ms_per_step": round(float(np.median(step_ms)), 3),
+        "mean_ms_per_step_events": round(float(np.mean(step_ms)), 3),
+        "median_tokens_per_s": round(n_valid / (float(np.median(step_ms)) / 1e3), 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -362,6 +393,13 @@ def main():
         "mfma_frac_of_peak": round(mfma_frac, 4),
         "algorithmic_tflops": round(work / (ms / 1e3) / 1e12, 1),
         "peak_hbm_gb": round(peak / 1e9, 3),
+        "hip_mem_used_gb": round((total_b - free_b) / 1e9, 3),
+        "torch_reserved_gb": round(reserved / 1e9, 3),
+        "mem_note": "peak_hbm_gb = torch.cuda.max_memory_allocated over the timed steps (inputs, "
+                    "outputs and workspaces all allocated through torch); hip_mem_used_gb = "
+                    "hipMemGetInfo's total - free after them (torch's reserved pool plus the "
+                    "runtime's own allocations)",
+        "kernels_traced_steps": n_tr,
         "inputs_gb": round(inputs_bytes / 1e9, 3),
         "workspace_gb": round(step.workspace_bytes() / 1e9, 3),
         "loss": loss0,

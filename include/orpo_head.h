@@ -39,7 +39,8 @@ typedef enum {
   ORPO_EINVAL = -1,        /* null pointer, negative or inconsistent size, bad option          */
   ORPO_EUNSUPPORTED = -2,  /* a valid request this library does not implement (see each call)   */
   ORPO_ENOWS = -3,         /* workspace pointer null or smaller than the *_workspace_bytes size */
-  ORPO_EHIP = -4           /* a HIP runtime call failed (see orpo_last_hip_error)               */
+  ORPO_EHIP = -4,          /* a HIP runtime call failed (see orpo_last_hip_error)               */
+  ORPO_EDATA = -5          /* orpo_check only: the device set a data-error bit in the status word */
 } orpo_status;
 
 /* Storage formats. ORPO_Q4G64: 4-bit affine codes, w = scale * q + bias per group of 64 along d,
@@ -67,9 +68,10 @@ typedef struct {
   int64_t V;            /* vocabulary size, > 0                                                 */
   int32_t h_fmt;        /* ORPO_F32 or ORPO_BF16; row-major [M,d]                               */
   int32_t w_fmt;        /* ORPO_F32 (needs h_fmt F32), ORPO_BF16 or ORPO_Q4G64 (need h_fmt BF16) */
-  float softcap;        /* > 0: z = softcap * tanh(raw / softcap); <= 0: z = raw. At most 40   */
-                        /* (ORPO_EUNSUPPORTED above: the kernels' fixed softmax reference     */
-                        /* keeps every term a normal float only up to there)                   */
+  float softcap;        /* > 0: z = softcap * tanh(raw / softcap); <= 0: z = raw. At most 1024 */
+                        /* (ORPO_EUNSUPPORTED above: z is evaluated in fp32 as               */
+                        /* softcap * (1 - 2 / (1 + e^(2 raw / softcap))), whose absolute error */
+                        /* grows like softcap * 2^-22)                                         */
   int32_t ignore_index; /* label value of ignored / padding tokens (conventionally -100)        */
   uint32_t flags;       /* ORPO_DW_ACCUMULATE | ORPO_DH_BF16                                    */
   float skip_eps;       /* backward coefficient filter: 0 = exact backward; > 0 (bf16 and 4-bit
@@ -247,6 +249,7 @@ orpo_status orpo_grpo_loss(int64_t M, int32_t n_seqs, const int32_t* seg_offsets
  *                  note).
  *   dW             (device) float [V,d] out (overwritten, or accumulated with ORPO_DW_ACCUMULATE);
  *                  NULL computes dh only. Must be NULL for ORPO_Q4G64 (a quantised head is frozen).
+ *                  With M = 0 it is set to zero (left as is with ORPO_DW_ACCUMULATE).
  *   ws             (device) >= orpo_head_bwd_workspace_bytes(desc) bytes
  *   fwd_ws         (device, optional) the workspace of the orpo_head_fwd call that produced lse,
  *                  with the same desc; read only with desc->skip_eps > 0, where its per-tile logit
@@ -302,7 +305,8 @@ orpo_status orpo_quantize_fp8(const void* x, int64_t rows, int64_t cols, uint8_t
 /*
  * orpo_head_fwd_fp8 — orpo_head_fwd with the logits taken from FP8 operands.
  *   desc   the bf16 head being approximated: h_fmt = w_fmt = ORPO_BF16 and d a multiple of 128
- *          (else ORPO_EUNSUPPORTED); M, V, softcap, ignore_index, skip_eps as for orpo_head_fwd
+ *          (else ORPO_EUNSUPPORTED); M, V, softcap, ignore_index, skip_eps as for orpo_head_fwd,
+ *          except that skip_eps > 0 with a softcap above 40 is ORPO_EUNSUPPORTED here
  *   q      the quantised h and W (orpo_quantize_fp8); NULL or a NULL member (M > 0): ORPO_EINVAL
  *   labels, logp, lse, ws, ws_bytes, stream as for orpo_head_fwd (ws: orpo_head_fwd_workspace_bytes)
  */
@@ -315,7 +319,8 @@ orpo_status orpo_head_fwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operand
  * operands, the coefficients g (onehot - softmax) sech^2 from the recomputed FP8 logits, and
  * dh = coeff . W, dW = coeff^T . h with the bf16 h and W given here. Arguments as for
  * orpo_head_bwd (ws: orpo_head_bwd_workspace_bytes, ORPO_DH_BF16 and ORPO_DW_ACCUMULATE honoured),
- * plus q as for orpo_head_fwd_fp8; fwd_ws (optional) is that forward's workspace.
+ * plus q as for orpo_head_fwd_fp8 (and desc under the same restrictions); fwd_ws (optional) is
+ * that forward's workspace.
  */
 orpo_status orpo_head_bwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operands* q,
                               const void* h, orpo_weight W, const int32_t* labels,
@@ -357,6 +362,15 @@ orpo_status orpo_trace_reset(void);                    /* forget the records, ke
 /* Waits for `stream` and copies the status word of `ws` (a workspace used by any call above) to
  * *status_out (host). Returns ORPO_EHIP if the wait or copy fails. */
 orpo_status orpo_read_status(const void* ws, uint32_t* status_out, hipStream_t stream);
+
+/*
+ * orpo_check — the data-error check of the boundary: waits for `stream`, then reads the status
+ * word of `ws` (device; a workspace used by orpo_head_fwd, orpo_loss or a sibling loss) and
+ * returns ORPO_OK when no bit is set, ORPO_EDATA when one is (orpo_read_status gives the bits:
+ * ORPO_DATA_*). The device never aborts on bad data; the affected tokens or branches are treated
+ * as documented under each call. ORPO_EINVAL for a null ws, ORPO_EHIP if the wait or copy fails.
+ */
+orpo_status orpo_check(const void* ws, hipStream_t stream);
 
 /* Text for a status code (static storage). Takes any int32 value (an orpo_status is passed as
  * one); codes outside orpo_status give "unknown status". */

@@ -54,9 +54,12 @@ constexpr int kLdsBytes = 4 * kStageBytes;  // A and B, two stages each
 constexpr uint32_t kBufferFlags = 0x00020000u;   // raw buffer descriptor word 3 (32-bit data format)
 
 // LDS swizzles (16-byte chunk index XOR a function of the row). K-major: row r's chunk c sits at
-// c ^ (r & 7), so the 8 consecutive rows one ds_read_b128 phase touches hit 8 distinct bank groups,
-// and rows 32 apart share the swizzle (a fragment's 32-row blocks are constant offsets apart).
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
+// c ^ ((r >> 1) & 7). gfx950's LDS has 64 four-byte banks and serves 16 lanes of a ds_read_b128 per
+// cycle: 16 consecutive 128-byte rows, two to a 256-byte bank row, so each pair of rows must take
+// one of 8 distinct chunk positions (a swizzle of r & 7 repeats after 8 rows and makes every read
+// a 2-way bank conflict). Rows 32 apart share the swizzle (a fragment's 32-row blocks are constant
+// offsets apart).
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_mn16(int r) { return 10 * (r & 3); }
 __device__ __forceinline__ int swz_mn32(int r) { return ((r >> 2) & 1) << 3; }
 
@@ -87,7 +90,8 @@ struct EBf16 {
   static constexpr int kGroups = 4;        // MFMA K groups per stage
   static constexpr int kReadsK = 1;        // LDS reads per K-major fragment
   static constexpr int kSets = 2;          // fragment register sets (2: next group read ahead)
-  static constexpr int kSwzK = 7;          // K-major swizzle mask (swz_k)
+  static constexpr int kSwzShift = 1;      // K-major swizzle (r >> kSwzShift) & kSwzK (swz_k)
+  static constexpr int kSwzK = 7;
   static constexpr int kMnRows = 64;       // rows of an MN-major stage
   static constexpr int kMnChunks = 32;     // 16-byte chunks per MN-major row
 
@@ -123,6 +127,7 @@ struct EF32 {
   static constexpr int kGroups = 4;
   static constexpr int kReadsK = 1;
   static constexpr int kSets = 2;
+  static constexpr int kSwzShift = 1;
   static constexpr int kSwzK = 7;
   static constexpr int kMnRows = 32;
   static constexpr int kMnChunks = 64;
@@ -170,8 +175,9 @@ struct EFp8 {
   // covers their latency.
   static constexpr int kSets = 1;
   // Swizzle r & 6: an even XOR keeps a fragment's two chunks (c even, c + 1) adjacent, so both
-  // reads share one address register (offsets 0 and 16); the 8 rows of a read phase still cover
-  // 8 distinct (row parity, chunk) bank groups.
+  // reads share one address register (offsets 0 and 16). A 128-byte row has only four such chunk
+  // pairs, so 16 lanes of one read meet a 2-way bank conflict either way.
+  static constexpr int kSwzShift = 0;
   static constexpr int kSwzK = 6;
 
   static __device__ __forceinline__ Frag frag_k(const char* s, int row0, int kg, int l) {
@@ -187,10 +193,11 @@ struct EFp8 {
   }
 };
 
-// One direct global -> LDS load: 16 bytes per lane, lane l's data lands at LDS byte (lds + 16 l);
-// bytes past the descriptor's range read as zero.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+// One direct global -> LDS load: 16 bytes per lane from byte voff + soff of the descriptor's range,
+// lane l's data landing at LDS byte (lds + 16 l); bytes past the range read as zero.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff,
+                                      uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -199,44 +206,61 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char* lds, uint
 // ------------------------------------------------------------------------------------------
 
 // K-major operand: rows [row0, row0 + 256) of a row-major matrix, bytes [kb, kb + 128) of each row,
-// chunk c of row r stored at chunk c ^ (r & kSwzMask).
-template <int kSwzMask>
+// chunk c of row r stored at chunk c ^ ((r >> kShift) & kSwzMask).
+template <int kShift, int kSwzMask>
 struct DmaKS {
   const char* base;
   int64_t ld, n_rows;
   uint32_t voff[4];
+  int wave_lds;                   // this wave's 4 KiB of a stage (uniform: an SGPR)
+  int64_t rs_row0;                // the rows the cached descriptor covers start here (-1: none)
+  __amdgpu_buffer_rsrc_t rs;
   __device__ __forceinline__ void init(const void* b, int64_t ld_bytes, int64_t rows) {
     base = (const char*)b;
     ld = ld_bytes;
     n_rows = rows;
+    rs_row0 = -1;
+    wave_lds = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) * 4096);
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = (4 * w + i) * 64 + l;
-      const int r = j >> 3, c = (j & 7) ^ ((j >> 3) & kSwzMask);
+      const int r = j >> 3, c = (j & 7) ^ ((r >> kShift) & kSwzMask);
       voff[i] = (uint32_t)(r * ld_bytes + c * 16);
     }
   }
-  __device__ __forceinline__ void issue(int64_t row0, int64_t kb, char* stage) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + row0 * ld + kb, (n_rows - row0) * ld - kb);
-    char* s = stage + (threadIdx.x >> 6) * 4096;
+  // The descriptor covers whole rows [row0, n_rows) and depends on the tile only; the K offset kb
+  // (within a row) goes in the scalar offset. A row past n_rows starts past the range, so all of it
+  // reads as zero.
+  __device__ __forceinline__ void issue(int64_t row0, int64_t kb, char* stage) {
+    if (row0 != rs_row0) {        // a new tile: rebuild the descriptor (once per tile)
+      rs = make_rsrc(base + row0 * ld, (n_rows - row0) * ld);
+      rs_row0 = row0;
+    }
+    char* s = stage + wave_lds;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i]);
+    for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i], (uint32_t)kb);
   }
   __device__ __forceinline__ void commit(char*) const {}
 };
-typedef DmaKS<7> DmaK;   // swz_k
+typedef DmaKS<1, 7> DmaK;   // swz_k
 
-// MN-major operand: rows [k0, k0 + kMnRows) of a row-major matrix, bytes [cb, cb + kMnChunks*16).
+// MN-major operand: rows [k0, k0 + kMnRows) of a row-major matrix of n_rows rows, bytes
+// [cb, cb + kMnChunks*16). The descriptor starts at column byte cb of row 0 and ends n_rows rows
+// later (it depends on the column block only); the row offset k0 ld goes in the per-lane offset,
+// so a row at or past n_rows lies past the range and reads as zero. Callers pass the matrix from
+// the first row they use, so that n_rows ld stays within 32 bits.
 template <class E>
 struct DmaMN {
   const char* base;
   int64_t ld, n_rows;
   uint32_t voff[4];
+  int wave_lds;                   // this wave's 4 KiB of a stage (uniform: an SGPR)
   __device__ __forceinline__ void init(const void* b, int64_t ld_bytes, int64_t rows) {
     base = (const char*)b;
     ld = ld_bytes;
     n_rows = rows;
+    wave_lds = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) * 4096);
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -247,10 +271,11 @@ struct DmaMN {
     }
   }
   __device__ __forceinline__ void issue(int64_t k0, int64_t cb, char* stage) const {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ld + cb, (n_rows - k0) * ld - cb);
-    char* s = stage + (threadIdx.x >> 6) * 4096;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + cb, n_rows * ld - cb);
+    const uint32_t ro = (uint32_t)(k0 * ld);
+    char* s = stage + wave_lds;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i]);
+    for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i] + ro);
   }
   __device__ __forceinline__ void commit(char*) const {}
 };
@@ -521,8 +546,20 @@ __device__ __forceinline__ void group_tail(f32x16 (&acc)[4][2], FragSets<E>& f,
 // Row scales (fp8): the last step of each tile fetches the next tile's scales (`scales(tile)`)
 // just before its wait for the step's loads, so they cost no wait of their own; they replace the
 // current ones after the tile's epilogue.
+// Step positions, counted without division: `cur` is step s (tile, K step), `ahead` step s + 2.
+struct StepPos {
+  int tile, ks;
+  __device__ __forceinline__ void next(int nk) {
+    if (++ks == nk) {
+      ks = 0;
+      ++tile;
+    }
+  }
+};
+
 template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi, class Scl>
-__device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __restrict__ ca,
+__device__ __forceinline__ void gemm_step(int s, int total, int nk, StepPos& cur, StepPos& ahead,
+                                          char* __restrict__ ca,
                                           char* __restrict__ cb, char* __restrict__ na,
                                           char* __restrict__ nb, Issue& issue, Commit& commit,
                                           Epi& epi, Scl& scales, typename E::Scales& sc,
@@ -550,12 +587,14 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
     hold_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
   }
+  const bool ends_tile = cur.ks == nk - 1;
   if (s + 1 < total) commit(na, nb);
-  if ((s + 1) % nk == 0 && s + 1 < total) sc_next = scales(s / nk + 1);
+  if (ends_tile && s + 1 < total) sc_next = scales(cur.tile + 1);
   vm_wait();
   hold_scales(sc_next);
   __syncthreads();
-  if (s + 2 < total) issue((s + 2) / nk, (s + 2) % nk, ca, cb);
+  if (s + 2 < total) issue(ahead.tile, ahead.ks, ca, cb);
+  ahead.next(nk);
   if constexpr (E::kSets == 2) {
     load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
     mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
@@ -563,11 +602,12 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
   } else {
     group_tail<E, AK, BK>(acc, f, a_last, na, nb, 0, sc, wm, wn, l);
   }
-  if ((s + 1) % nk == 0) {
-    epi(s / nk, acc);
+  if (ends_tile) {
+    epi(cur.tile, acc);
     if (kClear) zero_acc(acc);
     sc = sc_next;
   }
+  cur.next(nk);
 }
 
 // One K step with the barrier at its end, for stages read with transposing instructions (there the
@@ -575,14 +615,16 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, char* __rest
 // MFMAs of the four groups with each group's reads one group ahead (left to the compiler's
 // schedule), then the step's epilogue, wait and barrier.
 template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi, class Scl>
-__device__ __forceinline__ void gemm_step_end(int s, int total, int nk, char* __restrict__ ca,
+__device__ __forceinline__ void gemm_step_end(int s, int total, int nk, StepPos& cur,
+                                              StepPos& ahead, char* __restrict__ ca,
                                               char* __restrict__ cb, char* __restrict__ na,
                                               char* __restrict__ nb, Issue& issue, Commit& commit,
                                               Epi& epi, Scl& scales, typename E::Scales& sc,
                                               typename E::Scales& sc_next, f32x16 (&acc)[4][2],
                                               int wm, int wn, int l) {
   constexpr int kG = E::kGroups;
-  if (s + 1 < total) issue((s + 1) / nk, (s + 1) % nk, na, nb);
+  if (s + 1 < total) issue(ahead.tile, ahead.ks, na, nb);   // ahead = step s + 1 here
+  ahead.next(nk);
   static_assert(E::kSets == 2, "transposing stages read the next group ahead");
   FragSets<E> f;
   load_frags<E, AK, BK>(ca, cb, 0, wm, wn, l, f.a[0], f.b[0]);
@@ -592,13 +634,15 @@ __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, char* __
       load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
     mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
   }
+  const bool ends_tile = cur.ks == nk - 1;
   if (s + 1 < total) commit(na, nb);
-  if ((s + 1) % nk == 0 && s + 1 < total) sc_next = scales(s / nk + 1);
-  if ((s + 1) % nk == 0) {
-    epi(s / nk, acc);
+  if (ends_tile && s + 1 < total) sc_next = scales(cur.tile + 1);
+  if (ends_tile) {
+    epi(cur.tile, acc);
     if (kClear) zero_acc(acc);
     sc = sc_next;
   }
+  cur.next(nk);
   vm_wait();
   __syncthreads();
 }
@@ -622,30 +666,35 @@ __device__ __forceinline__ void gemm_run_scaled(const Smem& sm, int n_tiles, int
   const int total = n_tiles * nk;
   if (total <= 0) return;
   typename E::Scales sc = scales(0), sc_next = sc;
+  StepPos cur{0, 0}, ahead{0, 0};
   issue(0, 0, sm.a0, sm.b0);
+  ahead.next(nk);
   commit(sm.a0, sm.b0);
   vm_wait();
   __syncthreads();
   if constexpr (!(AK && BK)) {
-    // Transposing reads: barrier at the end of each step.
+    // Transposing reads: barrier at the end of each step; `ahead` runs one step ahead.
     for (int it = 0; it < total; it += 2) {
-      gemm_step_end<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit,
-                                       epi, scales, sc, sc_next, acc, wm, wn, l);
+      gemm_step_end<E, AK, BK, kClear>(it, total, nk, cur, ahead, sm.a0, sm.b0, sm.a1, sm.b1,
+                                       issue, commit, epi, scales, sc, sc_next, acc, wm, wn, l);
       if (it + 1 < total)
-        gemm_step_end<E, AK, BK, kClear>(it + 1, total, nk, sm.a1, sm.b1, sm.a0, sm.b0, issue,
-                                         commit, epi, scales, sc, sc_next, acc, wm, wn, l);
+        gemm_step_end<E, AK, BK, kClear>(it + 1, total, nk, cur, ahead, sm.a1, sm.b1, sm.a0,
+                                         sm.b0, issue, commit, epi, scales, sc, sc_next, acc, wm,
+                                         wn, l);
     }
     return;
   }
-  if (total > 1) issue(1 / nk, 1 % nk, sm.a1, sm.b1);
+  // K-major stages: `ahead` runs two steps ahead.
+  if (total > 1) issue(ahead.tile, ahead.ks, sm.a1, sm.b1);
+  ahead.next(nk);
   FragSets<E> f;
   load_frags<E, AK, BK>(sm.a0, sm.b0, 0, wm, wn, l, f.a[0], f.b[0]);
   for (int it = 0; it < total; it += 2) {
-    gemm_step<E, AK, BK, kClear>(it, total, nk, sm.a0, sm.b0, sm.a1, sm.b1, issue, commit, epi,
-                                 scales, sc, sc_next, f, acc, wm, wn, l);
+    gemm_step<E, AK, BK, kClear>(it, total, nk, cur, ahead, sm.a0, sm.b0, sm.a1, sm.b1, issue,
+                                 commit, epi, scales, sc, sc_next, f, acc, wm, wn, l);
     if (it + 1 < total)
-      gemm_step<E, AK, BK, kClear>(it + 1, total, nk, sm.a1, sm.b1, sm.a0, sm.b0, issue, commit,
-                                   epi, scales, sc, sc_next, f, acc, wm, wn, l);
+      gemm_step<E, AK, BK, kClear>(it + 1, total, nk, cur, ahead, sm.a1, sm.b1, sm.a0, sm.b0,
+                                   issue, commit, epi, scales, sc, sc_next, f, acc, wm, wn, l);
   }
 }
 

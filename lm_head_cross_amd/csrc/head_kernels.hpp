@@ -174,10 +174,19 @@ struct FwdArgs {
   int32_t n_tb, nblk, tiles_per_split, n_vtiles;
 };
 
+// Softmax reference of the forward. kSoftcapFixed: every z <= cap, so the sum is taken against
+// the fixed reference cap (no max pass, no rescaling); its smallest term 2^(-2 cap log2 e) stays a
+// normal float only for cap <= kFixedRefMaxCap. kSoftcapRunMax: larger softcaps keep a running
+// maximum, as without a softcap.
+enum FwdMode { kNoSoftcap = 0, kSoftcapFixed = 1, kSoftcapRunMax = 2 };
+constexpr float kFixedRefMaxCap = 40.f;
+
 // TMAX: the variant that also records each wave's largest raw logit per tile (the backward's
 // coefficient filter uses them to skip whole cold coefficient tiles).
-template <class E, bool Q4, bool SOFTCAP, bool TMAX>
+template <class E, bool Q4, int MODE, bool TMAX>
 __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
+  constexpr bool SOFTCAP = MODE != kNoSoftcap;
+  constexpr bool kRunMax = MODE != kSoftcapFixed;
   ORPO_DECLARE_SMEM(smem);
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, wm = w >> 2, wn = w & 3;
   const int tb = blockIdx.x % a.n_tb, split = blockIdx.x / a.n_tb;
@@ -196,14 +205,14 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     // -1 marks "no capture": rows past M and ignored tokens (ignore_index may be any value).
     const int lab = tok[nb] < a.M ? a.labels[tok[nb]] : -1;
     y[nb] = lab == a.ignore_index ? -1 : lab;
-    m[nb] = SOFTCAP ? a.cap * kLog2e : kNegInf;   // with a softcap every z <= cap: fixed reference
+    m[nb] = kRunMax ? kNegInf : a.cap * kLog2e;   // fixed reference: every z <= cap
     s[nb] = 0.f;
   }
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
 
-  typedef typename std::conditional<Q4, Q4K, DmaKS<E::kSwzK>>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K, DmaKS<E::kSwzShift, E::kSwzK>>::type LoaderA;
   LoaderA la;
-  DmaKS<E::kSwzK> lb;
+  DmaKS<E::kSwzShift, E::kSwzK> lb;
   if constexpr (Q4) la.init(a.q4); else la.init(a.w, row_bytes, a.V);
   lb.init(a.h, row_bytes, a.M);
   const int nk = (int)(a.d / E::kBK);
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
           return !kMasked || mb * 32 + 8 * (r >> 2) + (r & 3) < lim_p;
         };
         float ref = m[nb];
-        if (!SOFTCAP) {
+        if (kRunMax) {
           const int lim_max = fresh_lim();
           float tmax = kNegInf;
 #pragma unroll
@@ -253,7 +262,10 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (keep_below(lim_max, mb, r)) tmax = fmaxf(tmax, acc[mb][nb][r]);
-          const float mn = fmaxf(m[nb], tmax * kLog2e);
+          // z is monotone in raw: the tile's largest z * log2e (-cap log2e when no row is kept,
+          // which adds no term and only moves the reference).
+          const float zt = SOFTCAP ? __builtin_fmaf(sc.kz, sc.r_of(tmax), sc.cap * kLog2e) : tmax * kLog2e;
+          const float mn = fmaxf(m[nb], zt);
           if (mn != kNegInf) {
             s[nb] *= exp2_(m[nb] - mn);   // m = -inf gives 0
             m[nb] = mn;
@@ -261,6 +273,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
           ref = m[nb];
         }
         float acc_s = 0.f;
+        // u = z log2e - ref. Fixed reference: (z - cap) log2e = kz r. Running max under a softcap:
+        // kz r + (cap log2e - ref).
+        const float ub = SOFTCAP ? sc.cap * kLog2e - ref : -ref;
         if (ref != kNegInf) {
           const int lim_sum = fresh_lim();
 #pragma unroll
@@ -268,7 +283,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float raw = acc[mb][nb][r];
-              const float x = SOFTCAP ? sc.kz * sc.r_of(raw) : raw * kLog2e - ref;
+              const float x = !SOFTCAP ? __builtin_fmaf(raw, kLog2e, ub)
+                              : (kRunMax ? __builtin_fmaf(sc.kz, sc.r_of(raw), ub) : sc.kz * sc.r_of(raw));
               const float e = exp2_(x);
               const bool keep = keep_below(lim_sum, mb, r);
               acc_s += keep ? e : 0.f;
@@ -321,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const float mo = __shfl_xor(m[nb], 32), so = __shfl_xor(s[nb], 32);
-    if (!SOFTCAP) {
+    if (kRunMax) {
       const float mn = fmaxf(m[nb], mo);
       if (mn != kNegInf) {
         s[nb] = s[nb] * exp2_(m[nb] - mn) + so * exp2_(mo - mn);
@@ -342,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     for (int nb = 0; nb < 2; ++nb) {
       const float2 o = red[acc_n(wn, nb, l)];
       float mm = m[nb], ss = s[nb];
-      if (!SOFTCAP) {
+      if (kRunMax) {
         const float mn = fmaxf(mm, o.x);
         if (mn != kNegInf) {
           ss = ss * exp2_(mm - mn) + o.y * exp2_(o.x - mn);
@@ -354,6 +370,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
       if (tok[nb] < a.M) a.part[(int64_t)split * a.M + tok[nb]] = make_float2(mm, ss);
     }
   }
+}
+
+// Fills n floats with zeros (a kernel rather than hipMemsetAsync, so that a captured graph holds no
+// memset node).
+__global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = 0.f;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -643,9 +666,9 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     }
   }
 
-  typedef typename std::conditional<Q4, Q4K, DmaKS<EL::kSwzK>>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K, DmaKS<EL::kSwzShift, EL::kSwzK>>::type LoaderA;
   LoaderA la;
-  DmaKS<EL::kSwzK> lb;
+  DmaKS<EL::kSwzShift, EL::kSwzK> lb;
   if constexpr (Q4) la.init(a.q4); else la.init(kF8 ? a.wq : a.w, row_bytes, a.V);
   lb.init(kF8 ? a.hq : a.h, row_bytes, t_end);
   const int nk = (int)(a.d / EL::kBK);
@@ -686,13 +709,17 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     const int y = tv ? a.labels[tk] : a.ignore_index;
     const bool yv = tv && y != a.ignore_index && y >= 0 && (int64_t)y < a.V;   // else: ignored
     const float gt = yv ? a.g[tk] : 0.f;
-    const float L2 = yv ? a.lse[tk] * kLog2e : 0.f;
+    // An ignored token gets L2 = +inf: every exponential below is then exactly 0, whatever its
+    // logits, so its coefficients are 0 (never 0 * inf = NaN from an overflowing exp2).
+    const float L2 = yv ? a.lse[tk] * kLog2e : __builtin_huge_valf();
     // Off the label, coeff = -g p sech^2. Under a softcap, with rr = 1 / (1 + 2^(raw c1)) (so
     // tanh = 1 - 2 rr, z log2e = cap log2e + kz rr, sech^2 = 4 rr (1 - rr)), that is
-    //   coeff = G (rr - rr^2) 2^(kz rr),   G = -4 g 2^(cap log2e - L2)  (one factor per token);
-    // without one, coeff = -g 2^(raw log2e - L2). Both exponents stay in float range for
-    // softcaps up to 40 (the library's limit). The label's own entry adds g sech^2 (patched below).
-    const float G = SOFTCAP ? -4.f * gt * exp2_(sc.cap * kLog2e - L2) : -gt;
+    //   coeff = G (rr - rr^2) 2^(kz rr + B),   G = -4 g,  B = cap log2e - L2  (per token);
+    // without one, coeff = G 2^(raw log2e + B) with G = -g, B = -L2. The exponent is
+    // (z - lse) log2e <= 0 as one sum, so no intermediate factor leaves float range, for any
+    // softcap. The label's own entry adds g sech^2 (patched below).
+    const float G = SOFTCAP ? -4.f * gt : -gt;
+    const float B = SOFTCAP ? sc.cap * kLog2e - L2 : -L2;
     T* row = out + (tk - it.c0) * a.BVb + (vbase - it.v0);
     auto body = [&](auto masked_tag) {
       constexpr bool kMasked = decltype(masked_tag)::value;
@@ -712,9 +739,9 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
             float c;
             if (SOFTCAP) {
               const float rr = sc.r_of(raw);
-              c = G * (__builtin_fmaf(-rr, rr, rr) * exp2_(sc.kz * rr));
+              c = G * (__builtin_fmaf(-rr, rr, rr) * exp2_(__builtin_fmaf(sc.kz, rr, B)));
             } else {
-              c = G * exp2_(__builtin_fmaf(raw, kLog2e, -L2));
+              c = G * exp2_(__builtin_fmaf(raw, kLog2e, B));
             }
             if (kMasked && !(mb * 32 + 8 * rg + ri < lim_nb)) c = 0.f;
             vals[ri] = c;
@@ -934,7 +961,8 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   la.init(it.coeff, cpitch, it.C_cur);
   typedef typename std::conditional<Q4, Q4N, DmaMN<E>>::type LoaderB;
   LoaderB lb;                                                       // W [v][j], N-major
-  if constexpr (Q4) lb.init(a.q4, v_end); else lb.init(a.w, row_bytes, v_end);
+  if constexpr (Q4) lb.init(a.q4, v_end);
+  else lb.init((const char*)a.w + it.v0 * row_bytes, row_bytes, v_end - it.v0);   // block rows
   // Coefficient filter: run only the vocabulary slices some coefficient of this token tile needs.
   constexpr bool filt = SKIP;
   const int n_run = filt ? build_klist(it.fdh + (int64_t)ti * a.nsl_v * 4, nk, 4, klist, wave_tot) : nk;
@@ -943,7 +971,7 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
     const int64_t k0 = (int64_t)step * E::kBK;
     la.issue(i0, k0 * E::kSize, sa);
     if constexpr (Q4) lb.issue(it.v0 + k0, j0, sb);
-    else lb.issue(it.v0 + k0, j0 * E::kSize, sb);
+    else lb.issue(k0, j0 * E::kSize, sb);
   };
   auto commit = [&](char* sa, char* sb) {
     la.commit(sa);
@@ -979,7 +1007,7 @@ __device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, cons
   DmaMN<E> la;                                                      // coeff [i][v], M-major
   la.init(it.coeff, cpitch, it.C_cur);
   DmaMN<E> lb;                                                      // h [t][j], N-major
-  lb.init(a.h, row_bytes, t_end);
+  lb.init((const char*)a.h + it.c0 * row_bytes, row_bytes, t_end - it.c0);   // chunk rows
   // Coefficient filter: run only the token slices some coefficient of this vocabulary tile needs.
   constexpr bool filt = SKIP;
   const int n_run = filt ? build_klist(it.fdw + (int64_t)vt * a.nsl_t * 2, nk, 2, klist, wave_tot) : nk;
@@ -987,7 +1015,7 @@ __device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, cons
     const int step = filt ? __builtin_amdgcn_readfirstlane(klist[ks]) : ks;
     const int64_t k0 = (int64_t)step * E::kBK;
     la.issue(k0, vl0 * E::kSize, sa);
-    lb.issue(it.c0 + k0, j0 * E::kSize, sb);
+    lb.issue(k0, j0 * E::kSize, sb);
   };
   auto commit = [&](char* sa, char* sb) {
     la.commit(sa);

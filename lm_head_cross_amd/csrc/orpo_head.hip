@@ -77,7 +77,11 @@ struct TraceScope {
   }
 };
 
-constexpr float kMaxSoftcap = 40.f;
+// z = cap (1 - 2 r) is evaluated in fp32 with r = 1 / (1 + e^(2 raw / cap)) near 1/2, so each
+// logit carries an absolute error of about cap 2^-22 (2.4e-4 at 1024): beyond that the softcap's
+// own rounding would reach the 1e-3 log-prob tolerance. Softcaps up to kFixedRefMaxCap use the
+// fixed softmax reference, larger ones the running maximum.
+constexpr float kMaxSoftcap = 1024.f;
 
 // Format combinations the library implements.
 enum Kind { kF32, kBf16, kQ4, kBad };
@@ -88,8 +92,6 @@ orpo_status check_desc(const orpo_head_desc* d, Kind* kind) {
   if (d->V > INT32_MAX || d->M > INT32_MAX || d->d > (int64_t(1) << 20)) return ORPO_EUNSUPPORTED;
   if ((d->flags & ~uint32_t(ORPO_DW_ACCUMULATE | ORPO_DH_BF16)) != 0) return ORPO_EINVAL;
   if (!(d->softcap <= 0.f || d->softcap > 0.f)) return ORPO_EINVAL;   // NaN
-  // The softcapped kernels sum 2^((z - softcap) log2 e) with z >= -softcap: every term stays a
-  // normal float while 2 softcap log2 e < 126, and the backward's per-token factor likewise.
   if (d->softcap > kMaxSoftcap) return ORPO_EUNSUPPORTED;
   Kind k = kBad;
   if (d->h_fmt == ORPO_F32 && d->w_fmt == ORPO_F32) k = kF32;
@@ -145,10 +147,19 @@ struct BwdPlan {
 BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
   BwdPlan p;
   const int64_t esize = k == kF32 ? 4 : 2;
-  p.C = std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), kTile) * kTile, g_chunk);
+  // The backward's loaders address a token chunk of h, a vocabulary block of W and a coefficient
+  // buffer each through one buffer descriptor with 32-bit offsets: every one of them is kept
+  // within kSpan bytes (never binding at the shapes of the pages; a 256-row tile always fits).
+  const int64_t kSpan = int64_t(1) << 31;
+  const int64_t row = d->d * esize;
+  const int64_t rows_cap = std::max<int64_t>(kTile, kSpan / row / kTile * kTile);
+  p.C = std::min<int64_t>(std::min<int64_t>(cdiv(std::max<int64_t>(d->M, 1), kTile) * kTile, g_chunk),
+                          rows_cap);
   const size_t budget = g_coeff_budget ? g_coeff_budget : kCoeffDefault;
   int64_t bv = std::max<int64_t>(kTile, int64_t(budget) / (p.C * esize) / kTile * kTile);
   if (!g_coeff_budget) bv = std::min(bv, std::max(kBvMin, cdiv(cdiv(d->V, kBvItems), kTile) * kTile));
+  bv = std::min(bv, rows_cap);
+  bv = std::min(bv, std::max<int64_t>(kTile, kSpan / (p.C * esize) / kTile * kTile));
   p.BVb = std::min<int64_t>(cdiv(d->V, kTile) * kTile, bv);
   // With the coefficient filter: per buffer, dh flags [C/256][BVb/64][4 waves] and dW flags
   // [BVb/256][C/64][2 waves], one byte each.
@@ -168,17 +179,28 @@ bool bwd_plan_supported(const orpo_head_desc* d, const BwdPlan& p) {
   return !(d->skip_eps > 0.f) || (p.BVb / 64 <= kMaxKSteps && p.C / 64 <= kMaxKSteps);
 }
 
-template <class E, bool Q4, bool SC>
-orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
+template <class E, bool Q4, int MODE>
+orpo_status launch_fwd_mode(const FwdArgs& a, int grid, hipStream_t st) {
   TraceScope ts(ORPO_K_FWD, 2.0 * double(a.M) * double(a.V) * double(a.d), st);
-  if constexpr (E::kSize <= 2) {   // bf16, 4-bit and fp8 heads (the coefficient filter's formats)
+  // bf16, 4-bit and fp8 heads (the coefficient filter's formats); not the FP8 head's running-max
+  // mode, whose extra live state would spill (check_fp8 refuses that combination).
+  constexpr bool kTmax = E::kSize <= 2 && !(E::kSize == 1 && MODE == kSoftcapRunMax);
+  if constexpr (kTmax) {
     if (a.tmax) {
-      hipLaunchKernelGGL((fwd_kernel<E, Q4, SC, true>), dim3(grid), dim3(kThreads), 0, st, a);
+      hipLaunchKernelGGL((fwd_kernel<E, Q4, MODE, true>), dim3(grid), dim3(kThreads), 0, st, a);
       return launched();
     }
   }
-  hipLaunchKernelGGL((fwd_kernel<E, Q4, SC, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<E, Q4, MODE, false>), dim3(grid), dim3(kThreads), 0, st, a);
   return launched();
+}
+
+// The forward's softmax mode for a softcap: none, the fixed reference, or the running maximum.
+template <class E, bool Q4>
+orpo_status launch_fwd(const FwdArgs& a, int grid, hipStream_t st) {
+  if (!(a.cap > 0.f)) return launch_fwd_mode<E, Q4, kNoSoftcap>(a, grid, st);
+  if (a.cap <= kFixedRefMaxCap) return launch_fwd_mode<E, Q4, kSoftcapFixed>(a, grid, st);
+  return launch_fwd_mode<E, Q4, kSoftcapRunMax>(a, grid, st);
 }
 
 template <class E, bool Q4, bool SC, bool F8 = false>
@@ -203,6 +225,7 @@ orpo_status launch_bwd(const BwdArgs& a, int grid, hipStream_t st) {
 orpo_status check_fp8(const orpo_head_desc* d, Kind k, const orpo_fp8_operands* q) {
   if (!q) return ORPO_EINVAL;
   if (k != kBf16 || d->d % 128 != 0) return ORPO_EUNSUPPORTED;
+  if (d->softcap > kFixedRefMaxCap && d->skip_eps > 0.f) return ORPO_EUNSUPPORTED;
   if (d->M > 0 && (!q->hq || !q->h_exp || !q->wq || !q->w_exp)) return ORPO_EINVAL;
   return ORPO_OK;
 }
@@ -276,12 +299,11 @@ orpo_status fwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
   a.tiles_per_split = p.tps;
   a.n_vtiles = p.n_vtiles;
   const int grid = p.n_tb * p.nblk;
-  const bool sc = desc->softcap > 0.f;
   orpo_status st;
-  if (q8) st = sc ? launch_fwd<EFp8, false, true>(a, grid, stream) : launch_fwd<EFp8, false, false>(a, grid, stream);
-  else if (k == kF32) st = sc ? launch_fwd<EF32, false, true>(a, grid, stream) : launch_fwd<EF32, false, false>(a, grid, stream);
-  else if (k == kBf16) st = sc ? launch_fwd<EBf16, false, true>(a, grid, stream) : launch_fwd<EBf16, false, false>(a, grid, stream);
-  else st = sc ? launch_fwd<EBf16, true, true>(a, grid, stream) : launch_fwd<EBf16, true, false>(a, grid, stream);
+  if (q8) st = launch_fwd<EFp8, false>(a, grid, stream);
+  else if (k == kF32) st = launch_fwd<EF32, false>(a, grid, stream);
+  else if (k == kBf16) st = launch_fwd<EBf16, false>(a, grid, stream);
+  else st = launch_fwd<EBf16, true>(a, grid, stream);
   if (st != ORPO_OK) return st;
   TraceScope ts(ORPO_K_MERGE, 0.0, stream);
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)cdiv(desc->M, 256)), dim3(256), 0, stream,
@@ -472,7 +494,16 @@ orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
   const BwdPlan p = plan_bwd(desc, k);
   if (!bwd_plan_supported(desc, p)) return ORPO_EUNSUPPORTED;
   if (!ws || ws_bytes < p.ws || (uintptr_t)ws % 256) return ORPO_ENOWS;
-  if (desc->M == 0) return ORPO_OK;
+  if (desc->M == 0) {
+    // No token: the weight gradient is zero (overwritten unless accumulating).
+    if (dW && !(desc->flags & ORPO_DW_ACCUMULATE)) {
+      const int64_t n = desc->V * desc->d;
+      const int64_t blocks = std::min<int64_t>(cdiv(n, 256), 65536);
+      hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dW, n);
+      return launched();
+    }
+    return ORPO_OK;
+  }
   if (!h || !labels || !lse || !g || !dh) return ORPO_EINVAL;
 
   BwdArgs a{};
@@ -640,6 +671,13 @@ orpo_status orpo_read_status(const void* ws, uint32_t* status_out, hipStream_t s
   return ORPO_OK;
 }
 
+orpo_status orpo_check(const void* ws, hipStream_t stream) {
+  uint32_t v = 0;
+  const orpo_status st = orpo_read_status(ws, &v, stream);
+  if (st != ORPO_OK) return st;
+  return v ? ORPO_EDATA : ORPO_OK;
+}
+
 const char* orpo_status_string(int32_t status) {
   switch (status) {
     case ORPO_OK: return "ok";
@@ -647,6 +685,7 @@ const char* orpo_status_string(int32_t status) {
     case ORPO_EUNSUPPORTED: return "unsupported shape or format";
     case ORPO_ENOWS: return "workspace missing, misaligned or too small";
     case ORPO_EHIP: return "HIP runtime error";
+    case ORPO_EDATA: return "data error reported by the device (see the status word)";
   }
   return "unknown status";
 }

@@ -68,6 +68,7 @@ _SIGS = {
     "orpo_head_bwd_fp8": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Fp8Operands), _P,
                                          Weight, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]),
     "orpo_read_status": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint32), _P]),
+    "orpo_check": (ctypes.c_int, [_P, _P]),
     "orpo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orpo_last_hip_error": (ctypes.c_int32, []),
     "orpo_set_bwd_tiling": (ctypes.c_int, [ctypes.c_int64, ctypes.c_size_t]),
@@ -142,6 +143,41 @@ def _head_dtypes(h, w, labels, scales=None, biases=None):
         _need_dtype("w", w, h.dtype)
 
 
+def _need_shape(what: str, t, shape):
+    """Raise unless `t` (None allowed) has exactly `shape`: the kernels index raw memory with the
+    sizes derived from h and w, so a mismatch would read or write out of bounds."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise OrpoError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _head_shapes(h, w, labels, scales=None, biases=None):
+    """(M, d, V) of a head call, after checking every operand's shape against them."""
+    if h.dim() != 2:
+        raise OrpoError(f"h must be [M, d], got shape {tuple(h.shape)}")
+    M, d = h.shape
+    if w.dim() != 2:
+        raise OrpoError(f"w must be 2-D, got shape {tuple(w.shape)}")
+    V = w.shape[0]
+    if scales is not None or biases is not None:
+        if d % 64:
+            raise OrpoError(f"a 4-bit head needs d a multiple of 64 (d = {d})")
+        _need_shape("w (packed 4-bit words)", w, (V, d // 8))
+        _need_shape("scales", scales, (V, d // 64))
+        _need_shape("biases", biases, (V, d // 64))
+    else:
+        _need_shape("w", w, (V, d))
+    _need_shape("labels", labels, (M,))
+    return M, d, V
+
+
+def _need_offsets(seg_offsets, spans: int) -> int:
+    """Number of groups (pairs, or completions for spans = 1) described by seg_offsets."""
+    if seg_offsets.dim() != 1 or seg_offsets.shape[0] < spans + 1 or (seg_offsets.shape[0] - 1) % spans:
+        raise OrpoError(f"seg_offsets must be 1-D with {spans} * n + 1 entries (n >= 1), "
+                        f"got shape {tuple(seg_offsets.shape)}")
+    return (seg_offsets.shape[0] - 1) // spans
+
+
 def make_desc(M, d, V, h_dtype, w_fmt, softcap, ignore_index=IGNORE_INDEX, flags=0,
               skip_eps=0.0) -> Desc:
     if h_dtype not in (torch.float32, torch.bfloat16):
@@ -156,12 +192,20 @@ def _w_fmt(w, scales):
     return ORPO_F32 if w.dtype == torch.float32 else ORPO_BF16
 
 
-def _vocab(w, scales):
-    return w.shape[0]
-
-
 def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+def _need_fwd_ws(fwd_ws, desc):
+    """The backward reads the forward workspace's per-tile maxima (skip_eps > 0) at an offset the
+    descriptor fixes: the tensor must be the uint8 workspace of a forward with the same sizes."""
+    if fwd_ws is None:
+        return
+    _need_dtype("fwd_ws", fwd_ws, torch.uint8)
+    need = lib().orpo_head_fwd_workspace_bytes(ctypes.byref(desc))
+    if fwd_ws.dim() != 1 or fwd_ws.numel() < need:
+        raise OrpoError(f"fwd_ws must be a forward workspace of at least {need} bytes, "
+                        f"got shape {tuple(fwd_ws.shape)}")
 
 
 def set_bwd_tiling(chunk_tokens: int = 0, coeff_bytes: int = 0):
@@ -175,14 +219,26 @@ def read_status(ws: torch.Tensor) -> int:
     return int(v.value)
 
 
+ORPO_EDATA = -5
+
+
+def check(ws: torch.Tensor) -> bool:
+    """orpo_check: True when the workspace's status word holds no data-error bit (waits for the
+    stream); False when the device reported one (read_status gives the bits)."""
+    st = lib().orpo_check(_ptr(ws), _stream(ws.device))
+    if st == ORPO_EDATA:
+        return False
+    _check(st, "orpo_check")
+    return True
+
+
 def head_fwd(h, w, labels, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None, biases=None,
              return_ws=False, skip_eps=0.0):
     """logp[M], lse[M] (float32). `w` is W[V,d] (f32/bf16) or the packed q4 words [V,d/8] (int32).
     skip_eps > 0 also records the per-tile logit maxima the backward's cold-tile skip reads."""
     _head_dtypes(h, w, labels, scales, biases)
+    M, d, V = _head_shapes(h, w, labels, scales, biases)
     _need_gpu(h, w, labels, scales, biases)
-    M, d = h.shape
-    V = _vocab(w, scales)
     desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, skip_eps=skip_eps)
     L = lib()
     ws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(desc)), h.device)
@@ -206,10 +262,13 @@ def orpo_loss(logp, labels, seg_offsets, V, lam, ignore_index=IGNORE_INDEX, retu
     _need_dtype("logp", logp, torch.float32)
     _need_dtype("labels", labels, torch.int32)
     _need_dtype("seg_offsets", seg_offsets, torch.int32)
-    _need_gpu(logp, labels, seg_offsets)
     S = SCOPES[scope]
+    if logp.dim() != 1:
+        raise OrpoError(f"logp must be [M], got shape {tuple(logp.shape)}")
     M = logp.shape[0]
-    P = (seg_offsets.shape[0] - 1) // S
+    _need_shape("labels", labels, (M,))
+    P = _need_offsets(seg_offsets, S)
+    _need_gpu(logp, labels, seg_offsets)
     L = lib()
     ws = _workspace(L.orpo_loss_workspace_bytes(M, P), logp.device)
     out = torch.empty(5 + (S if S == 3 else 2) * P, dtype=torch.float64, device=logp.device)
@@ -231,12 +290,17 @@ def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNOR
     _need_dtype("lse", lse, torch.float32)
     _need_dtype("g", g, torch.float32)
     _need_dtype("dW", dW, torch.float32)
+    M, d, V = _head_shapes(h, w, labels, scales, biases)
+    _need_shape("lse", lse, (M,))
+    _need_shape("g", g, (M,))
+    _need_shape("dW", dW, (V, d))
+    if scales is not None and (want_dW or dW is not None):
+        raise OrpoError("a 4-bit head is frozen: it has no dW (pass want_dW=False)")
     _need_gpu(h, w, labels, lse, g, scales, biases, dW, fwd_ws)
-    M, d = h.shape
-    V = _vocab(w, scales)
     flags = (ORPO_DW_ACCUMULATE if accumulate else 0) | (ORPO_DH_BF16 if dh_bf16 else 0)
     desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index, flags, skip_eps)
     L = lib()
+    _need_fwd_ws(fwd_ws, desc)
     ws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc)), h.device)
     dh = torch.empty(M, d, dtype=torch.bfloat16 if dh_bf16 else torch.float32, device=h.device)
     if want_dW and dW is None:
@@ -275,9 +339,11 @@ def quantize_fp8(x, q=None, exps=None):
 def _fp8_operands(hq, h_exp, wq, w_exp):
     for name, t in (("hq", hq), ("h_exp", h_exp), ("wq", wq), ("w_exp", w_exp)):
         _need_dtype(name, t, torch.uint8)
-    _need_gpu(hq, h_exp, wq, w_exp)
-    if hq.shape[0] != h_exp.shape[0] or wq.shape[0] != w_exp.shape[0] or hq.shape[1] != wq.shape[1]:
-        raise OrpoError("FP8 operand shapes disagree")
+    if hq.dim() != 2 or wq.dim() != 2:
+        raise OrpoError("hq and wq must be 2-D")
+    _need_shape("h_exp", h_exp, (hq.shape[0],))
+    _need_shape("w_exp", w_exp, (wq.shape[0],))
+    _need_shape("wq", wq, (wq.shape[0], hq.shape[1]))
     return Fp8Operands(hq.data_ptr(), h_exp.data_ptr(), wq.data_ptr(), w_exp.data_ptr())
 
 
@@ -286,9 +352,10 @@ def head_fwd_fp8(hq, h_exp, wq, w_exp, labels, softcap=0.0, ignore_index=IGNORE_
     """logp[M], lse[M] of the FP8 head: logits from the quantised operands (quantize_fp8)."""
     _need_dtype("labels", labels, torch.int32)
     q8 = _fp8_operands(hq, h_exp, wq, w_exp)
-    _need_gpu(hq, labels)
     M, d = hq.shape
     V = wq.shape[0]
+    _need_shape("labels", labels, (M,))
+    _need_gpu(hq, h_exp, wq, w_exp, labels)
     desc = make_desc(M, d, V, torch.bfloat16, ORPO_BF16, softcap, ignore_index, skip_eps=skip_eps)
     L = lib()
     ws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(desc)), hq.device)
@@ -309,14 +376,17 @@ def head_bwd_fp8(hq, h_exp, wq, w_exp, h, w, labels, lse, g, softcap=0.0, want_d
     _need_dtype("g", g, torch.float32)
     _need_dtype("dW", dW, torch.float32)
     q8 = _fp8_operands(hq, h_exp, wq, w_exp)
-    _need_gpu(hq, h, w, labels, lse, g, dW, fwd_ws)
-    M, d = h.shape
-    V = w.shape[0]
+    M, d, V = _head_shapes(h, w, labels)
     if hq.shape != (M, d) or wq.shape != (V, d):
         raise OrpoError("FP8 operands must have the shapes of h and w")
+    _need_shape("lse", lse, (M,))
+    _need_shape("g", g, (M,))
+    _need_shape("dW", dW, (V, d))
+    _need_gpu(hq, h_exp, wq, w_exp, h, w, labels, lse, g, dW, fwd_ws)
     flags = (ORPO_DW_ACCUMULATE if accumulate else 0) | (ORPO_DH_BF16 if dh_bf16 else 0)
     desc = make_desc(M, d, V, h.dtype, ORPO_BF16, softcap, ignore_index, flags, skip_eps)
     L = lib()
+    _need_fwd_ws(fwd_ws, desc)
     ws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(desc)), h.device)
     dh = torch.empty(M, d, dtype=torch.bfloat16 if dh_bf16 else torch.float32, device=h.device)
     if want_dW and dW is None:
@@ -367,9 +437,15 @@ def pref_loss(kind, logp, labels, seg_offsets, V, beta, gamma=0.0, ref_sums=None
     _need_dtype("labels", labels, torch.int32)
     _need_dtype("seg_offsets", seg_offsets, torch.int32)
     _need_dtype("ref_sums", ref_sums, torch.float64)
-    _need_gpu(logp, labels, seg_offsets, ref_sums)
+    if logp.dim() != 1:
+        raise OrpoError(f"logp must be [M], got shape {tuple(logp.shape)}")
     M = logp.shape[0]
-    P = (seg_offsets.shape[0] - 1) // 2
+    _need_shape("labels", labels, (M,))
+    P = _need_offsets(seg_offsets, 2)
+    _need_shape("ref_sums", ref_sums, (2 * P,))
+    if kind not in PREF_KINDS:
+        raise OrpoError(f"unknown preference objective {kind!r}")
+    _need_gpu(logp, labels, seg_offsets, ref_sums)
     L = lib()
     ws = _workspace(L.orpo_objective_workspace_bytes(M, 2 * P), logp.device)
     out = torch.empty(3 + 2 * P, dtype=torch.float64, device=logp.device)
@@ -389,9 +465,14 @@ def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip
         _need_dtype(name, t, torch.float32)
     _need_dtype("labels", labels, torch.int32)
     _need_dtype("seg_offsets", seg_offsets, torch.int32)
-    _need_gpu(logp, old_logp, ref_logp, advantages, labels, seg_offsets)
+    if logp.dim() != 1:
+        raise OrpoError(f"logp must be [M], got shape {tuple(logp.shape)}")
     M = logp.shape[0]
-    S = seg_offsets.shape[0] - 1
+    for name, t in (("old_logp", old_logp), ("ref_logp", ref_logp), ("labels", labels)):
+        _need_shape(name, t, (M,))
+    S = _need_offsets(seg_offsets, 1)
+    _need_shape("advantages", advantages, (S,))
+    _need_gpu(logp, old_logp, ref_logp, advantages, labels, seg_offsets)
     L = lib()
     ws = _workspace(L.orpo_objective_workspace_bytes(M, S), logp.device)
     out = torch.empty(4, dtype=torch.float64, device=logp.device)
@@ -429,15 +510,34 @@ class HeadStep:
         _need_dtype("ref_sums", o.get("ref_sums"), torch.float64)
         for k in ("old_logp", "ref_logp", "advantages"):
             _need_dtype(k, o.get(k), torch.float32)
+        M, d, Vw = _head_shapes(h, w, labels, scales, biases)
+        if V != Vw:
+            raise OrpoError(f"V = {V} but the head has {Vw} vocabulary rows")
+        if scales is not None and want_dW:
+            raise OrpoError("a 4-bit head is frozen: it has no dW (pass want_dW=False)")
+        S = SCOPES[scope] if objective == "orpo" else (1 if objective == "grpo" else 2)
+        P = _need_offsets(seg_offsets, S)
+        if objective in ("dpo", "ipo", "hinge"):
+            _need_shape("ref_sums", o.get("ref_sums"), (2 * P,))
+        if objective == "grpo":
+            for k in ("old_logp", "ref_logp"):
+                if o.get(k) is None:
+                    raise OrpoError(f"grpo needs obj[{k!r}]")
+                _need_shape(k, o[k], (M,))
+            if o.get("advantages") is None:
+                raise OrpoError("grpo needs obj['advantages']")
+            _need_shape("advantages", o["advantages"], (P,))
+        if objective == "dpo" and o.get("ref_sums") is None:
+            raise OrpoError("dpo needs obj['ref_sums']")
         _need_gpu(h, w, labels, seg_offsets, scales, biases,
                   *(o.get(k) for k in ("ref_sums", "old_logp", "ref_logp", "advantages")))
         self.h, self.w, self.labels, self.off = h, w, labels, seg_offsets
         self.scales, self.biases = scales, biases
-        self.M, self.d = h.shape
+        self.M, self.d = M, d
         self.V, self.softcap, self.lam, self.ignore = V, float(softcap), float(lam), ignore_index
         self.objective, self.obj = objective, dict(obj or {})
-        self.S = SCOPES[scope] if objective == "orpo" else (1 if objective == "grpo" else 2)
-        self.P = (seg_offsets.shape[0] - 1) // self.S
+        self.S = S
+        self.P = P
         dev = h.device
         self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index,
                               flags=ORPO_DH_BF16 if dh_bf16 else 0, skip_eps=skip_eps)

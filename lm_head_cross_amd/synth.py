@@ -78,6 +78,10 @@ CONFIGS = {
     # labels the argmax): the data the backward's coefficient filter is meant for.
     7: HeadConfig(7, "e4b-bf16-softcap30-peaked", M=8192, d=2560, V=262144, pairs=16, len_lo=192,
                   len_hi=320, softcap=30.0, lam=0.1, w_std=12.0, p_argmax=0.95),
+    # The 4-bit head at the e4b shape (d = 2560, V = 262144): the shape of the pages' own quantised
+    # head; lengths, softcap and lambda as the 4-bit workload at the MiniCPM shape. dh only.
+    8: HeadConfig(8, "q4g64-e4b-shape-softcap30", M=8192, d=2560, V=262144, pairs=16, len_lo=128,
+                  len_hi=384, softcap=30.0, lam=0.1, q4=True),
     # The e4b head with the full-scope NLL: each pair's chosen sequence also carries its prompt span.
     6: HeadConfig(6, "e4b-bf16-softcap30-fullnll", M=8192, d=2560, V=262144, pairs=16, len_lo=144,
                   len_hi=240, softcap=30.0, lam=0.1, prompt_lo=64, prompt_hi=128),

@@ -73,10 +73,12 @@ void check_head(const orpo_head_desc& d) {
     else if (with_dw && d.w_fmt == ORPO_Q4G64) EXPECT(st == ORPO_EUNSUPPORTED);   // frozen head
     else EXPECT(st == ORPO_ENOWS);
   }
-  // The FP8 head: the same sizes; refused unless the head is bf16 with d a multiple of 128.
+  // The FP8 head: the same sizes; refused unless the head is bf16 with d a multiple of 128, and
+  // not with both a softcap above 40 and the coefficient filter.
   const orpo_fp8_operands q8 = {(const uint8_t*)p, (const uint8_t*)p, (const uint8_t*)p,
                                 (const uint8_t*)p};
-  const bool fp8_ok = d.h_fmt == ORPO_BF16 && d.w_fmt == ORPO_BF16 && d.d % 128 == 0;
+  const bool fp8_ok = d.h_fmt == ORPO_BF16 && d.w_fmt == ORPO_BF16 && d.d % 128 == 0 &&
+                      !(d.softcap > 40.f && d.skip_eps > 0.f);
   st = orpo_head_fwd_fp8(&d, &q8, (const int32_t*)p, (float*)p, (float*)p, fake(kWs),
                          fw ? fw - 1 : std::numeric_limits<size_t>::max(), nullptr);
   if (fw == 0) EXPECT(refused(st));
@@ -105,7 +107,7 @@ void sweep_head() {
   const int64_t ds[] = {-64, 0, 32, 64, 2560, int64_t(1) << 20, (int64_t(1) << 20) + 64, I64};
   const int64_t Vs[] = {-1, 0, 1, 257, 262144, int64_t(1) << 22, I32, I32 + 1, I64};
   const int32_t fmts[] = {-1, ORPO_F32, ORPO_BF16, ORPO_Q4G64, 3};
-  const float caps[] = {0.f, -1.f, 30.f, 40.f, 40.5f, inf, -inf, nan};
+  const float caps[] = {0.f, -1.f, 30.f, 40.f, 40.5f, 1024.f, 1024.5f, inf, -inf, nan};
   const uint32_t flags[] = {0u, ORPO_DW_ACCUMULATE, ORPO_DH_BF16, ORPO_DW_ACCUMULATE | ORPO_DH_BF16, 4u,
                             0x80000000u};
   const float eps[] = {0.f, 1e-5f, -1.f, inf, nan};

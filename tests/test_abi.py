@@ -64,7 +64,7 @@ def test_workspace_sizes():
     (dict(flags=8), EINVAL),
     (dict(flags=4), EINVAL),
     (dict(cap=float("nan")), EINVAL),
-    (dict(cap=40.5), EUNSUP),                 # beyond the softcap range the kernels support
+    (dict(cap=1024.5), EUNSUP),               # beyond the softcap range evaluated to fp32 accuracy
 ])
 def test_fwd_rejects_bad_descriptors(kw, code):
     L = H.lib()
@@ -141,13 +141,16 @@ def test_bwd_tiling_bounds_keep_workspace_sizes_from_wrapping():
     assert L.orpo_set_bwd_tiling(0, (1 << 40) + 1) == EINVAL
     big = _desc(M=(1 << 31) - 1, d=1 << 20, V=(1 << 31) - 1, flags=2)   # bf16 dh: the fp32 chunk accumulator
     try:
+        # Every backward loader addresses at most 2^31 bytes through one descriptor: with rows of
+        # d = 2^20 bf16 (2 MiB) a token chunk and a vocabulary block hold at most 1024 rows,
+        # whatever the knob asks for.
         assert L.orpo_set_bwd_tiling(1 << 31, 1 << 40) == 0
-        # C = 2^31 tokens, so the 2^40-byte budget leaves one 256-entry block: 2 tiles of 2^31 x 256 bf16.
-        expect = 256 + 2 * (1 << 31) * 256 * 2 + (1 << 31) * (1 << 20) * 4
+        # C = 1024 tokens, BVb = 1024 entries: 2 tiles of 1024 x 1024 bf16 + the fp32 [C, d] accumulator.
+        expect = 256 + 2 * 1024 * 1024 * 2 + 1024 * (1 << 20) * 4
         assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == expect
         assert L.orpo_set_bwd_tiling(256, 1 << 40) == 0
-        # C = 256: the budget allows 2^31 entries, capped at V rounded up to 256 (one block, no accumulator).
-        expect = 256 + 2 * 256 * (1 << 31) * 2
+        # C = 256 tokens, BVb = 1024 entries (the row cap, below the budget's 2^31).
+        expect = 256 + 2 * 256 * 1024 * 2 + 256 * (1 << 20) * 4
         assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == expect
     finally:
         assert L.orpo_set_bwd_tiling(0, 0) == 0
@@ -157,6 +160,9 @@ def test_status_strings():
     L = H.lib()
     assert L.orpo_status_string(0) == b"ok"
     assert b"workspace" in L.orpo_status_string(ENOWS)
+    assert b"data error" in L.orpo_status_string(-5)
+    # orpo_check validates its workspace pointer before touching the stream.
+    assert L.orpo_check(None, None) == EINVAL
 
 
 def test_objective_entry_points_reject_bad_arguments():
@@ -274,6 +280,11 @@ def test_fp8_entry_points_validate_before_any_launch():
     assert L.orpo_head_fwd_fp8(ctypes.byref(d64), ctypes.byref(q8), 16, 16, 16, base, 1 << 30, None) == EUNSUP
     f32 = _desc(h=H.ORPO_F32, w=H.ORPO_F32)                 # the FP8 head approximates a bf16 head
     assert L.orpo_head_fwd_fp8(ctypes.byref(f32), ctypes.byref(q8), 16, 16, 16, base, 1 << 30, None) == EUNSUP
+    # A softcap above 40 (running maximum) with the coefficient filter's tile maxima: refused.
+    big = H.Desc(512, 256, 4096, H.ORPO_BF16, H.ORPO_BF16, 50.0, -100, 0, 1e-5)
+    assert L.orpo_head_fwd_fp8(ctypes.byref(big), ctypes.byref(q8), 16, 16, 16, base, 1 << 30, None) == EUNSUP
+    assert L.orpo_head_bwd_fp8(ctypes.byref(big), ctypes.byref(q8), 16, H.Weight(16, None, None), 16,
+                               16, 16, 16, 16, base, 1 << 30, None, None) == EUNSUP
     bws = L.orpo_head_bwd_workspace_bytes(ctypes.byref(d))
     w = H.Weight(16, None, None)
     assert L.orpo_head_bwd_fp8(ctypes.byref(d), ctypes.byref(q8), 16, w, 16, 16, 16, 16, 16, base,

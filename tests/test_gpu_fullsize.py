@@ -16,7 +16,8 @@ import torch
 from lm_head_cross_amd import head as H
 from lm_head_cross_amd import synth
 from oracle import orpo_oracle as orc
-from tests.gpu_helpers import TOL_GRAD, TOL_SCALAR, dev, oracle_weight, rel, say
+from tests.gpu_helpers import (TOL_GRAD, TOL_SCALAR, dev, mfma_operand_weight, oracle_weight, rel,
+                               row_gate, say, token_gate)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +34,8 @@ def _sample_rows(inp, n_per_branch=2, seed=0):
 
 
 @pytest.mark.parametrize("name", ["minicpm-like-bf16", "e4b-bf16-softcap30",
-                                  "q4g64-minicpm-shape-softcap30", "12b-like-bf16-softcap30",
-                                  "e4b-bf16-softcap30-fullnll"])
+                                  "q4g64-minicpm-shape-softcap30", "q4g64-e4b-shape-softcap30",
+                                  "12b-like-bf16-softcap30", "e4b-bf16-softcap30-fullnll"])
 def test_full_size_sampled_parity(name):
     cfg = synth.workload(name)
     say(f"[fullsize] {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}")
@@ -62,11 +63,21 @@ def test_full_size_sampled_parity(name):
     W = oracle_weight(inp)
     hh = inp.h.float().numpy().astype(np.float64)
 
-    # Forward on sampled rows.
+    # Forward on sampled rows: norm-wise against the definition, per token against the oracle on
+    # the operands the kernels multiply (the same weights except for the 4-bit head, whose
+    # dequantised values the kernels round to bf16).
     rows = _sample_rows(inp)
     ref_logp, ref_lse = orc.forward(hh[rows], W, inp.labels[rows], cfg.softcap)
     e_logp, e_lse = rel(logp[rows], ref_logp), rel(lse[rows], ref_lse)
-    say(f"[fullsize {cfg.name}] rows={len(rows)} logp={e_logp:.2e} lse={e_lse:.2e}")
+    W_op = mfma_operand_weight(inp) if cfg.q4 else W
+    if cfg.q4:
+        op_logp, op_lse = orc.forward(hh[rows], W_op, inp.labels[rows], cfg.softcap)
+    else:
+        op_logp, op_lse = ref_logp, ref_lse
+    m_logp = token_gate("logp", logp[rows], op_logp)
+    m_lse = token_gate("lse", lse[rows], op_lse)
+    say(f"[fullsize {cfg.name}] rows={len(rows)} logp={e_logp:.2e} lse={e_lse:.2e} "
+        f"max|dlogp|={m_logp:.2e} max|dlse|={m_lse:.2e}")
     assert e_logp <= TOL_SCALAR and e_lse <= TOL_SCALAR
 
     # Loss epilogue on the GPU's logp vector, in float64.
@@ -101,11 +112,20 @@ def test_full_size_sampled_parity(name):
     e_dh = rel(dh[probe], rdh)
     others = np.setdiff1d(np.arange(cfg.M), probe)
     assert np.all(dh[others] == 0.0)
-    msg = f"[fullsize {cfg.name}] probe={len(probe)} dh={e_dh:.2e}"
+    if cfg.q4:   # per row against the probe on the MFMA's operands
+        _, plse_op = orc.forward(hh[probe], W_op, inp.labels[probe], cfg.softcap)
+        rdh_op, _ = orc.backward(hh[probe], W_op, inp.labels[probe], plse_op,
+                                 gs[probe].astype(np.float64), cfg.softcap, want_dW=False)
+    else:
+        rdh_op = rdh
+    r_dh = row_gate("dh", dh[probe], rdh_op)
+    msg = f"[fullsize {cfg.name}] probe={len(probe)} dh={e_dh:.2e} dh_row={r_dh:.2e}"
     assert e_dh <= TOL_GRAD
     if not cfg.q4:
-        e_dW = rel(step.dW.cpu().numpy(), rdW)
-        msg += f" dW={e_dW:.2e}"
+        dW = step.dW.cpu().numpy()
+        e_dW = rel(dW, rdW)
+        r_dW = row_gate("dW", dW, rdW)
+        msg += f" dW={e_dW:.2e} dW_row={r_dW:.2e}"
         assert e_dW <= TOL_GRAD
     say(msg)
 

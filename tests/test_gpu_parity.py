@@ -50,10 +50,14 @@ def test_12b_shape_short_pair():
 # Hand-built shapes: ragged M and V, ignored tokens inside branches, padding, softcap on/off,
 # and the backward's token-chunk x vocabulary-block loop forced to several iterations.
 # ------------------------------------------------------------------------------------------
-def _custom(M, d, V, dtype, cap, lam, seed, pairs=2, q4=False):
+def _custom(M, d, V, dtype, cap, lam, seed, pairs=2, q4=False, pad=True):
+    """Seeded inputs of an arbitrary shape: ragged branches over the first 7/8 of M (all of M with
+    pad=False, so the last token tile can hold a single valid token), the rest padding, and one
+    ignored token inside every branch of 3 or more tokens."""
     rng = np.random.default_rng(seed)
-    cfg = synth.HeadConfig(0, f"custom-M{M}-d{d}-V{V}-{dtype}-cap{cap}", M=M, d=d, V=V, pairs=pairs,
-                           len_lo=1, len_hi=M, softcap=cap, lam=lam, dtype=dtype, q4=q4)
+    cfg = synth.HeadConfig(0, f"custom-M{M}-d{d}-V{V}-{dtype}-cap{cap}{'' if pad else '-nopad'}",
+                           M=M, d=d, V=V, pairs=pairs, len_lo=1, len_hi=M, softcap=cap, lam=lam,
+                           dtype=dtype, q4=q4)
     h64 = rng.standard_normal((M, d))
     w32 = (rng.standard_normal((V, d)) * (3.0 / np.sqrt(d))).astype(np.float32)
     if dtype == "f32":
@@ -61,7 +65,7 @@ def _custom(M, d, V, dtype, cap, lam, seed, pairs=2, q4=False):
     else:
         h, w = synth.to_bf16(h64), synth.to_bf16(w32)
     # Branch lengths: ragged, leaving a padded tail.
-    used = max(2 * pairs, (M * 7) // 8)
+    used = max(2 * pairs, (M * 7) // 8) if pad else M
     cuts = np.sort(rng.choice(np.arange(1, used), size=2 * pairs - 1, replace=False))
     off = np.concatenate([[0], cuts, [used]]).astype(np.int32)
     labels = rng.integers(0, V, size=M).astype(np.int32)
@@ -83,6 +87,9 @@ CUSTOM = [
     (37, 192, 7, "bf16", 5.0, 1.0),
     (260, 256, 2000, "f32", 2.0, 0.1),
     (700, 320, 3001, "bf16", 30.0, 0.2),
+    # Softcaps above the fixed-reference range: the forward keeps a running maximum.
+    (300, 128, 1000, "bf16", 50.0, 0.1),
+    (700, 320, 3001, "bf16", 200.0, 0.2),
 ]
 
 
@@ -91,6 +98,38 @@ def test_ragged_shapes(M, d, V, dtype, cap, lam):
     inp = _custom(M, d, V, dtype, cap, lam, seed=M + V)
     say(f"[case] {inp.cfg.name}")
     assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name)
+
+
+# Every position inside a branch (no padding): the last token tile holds exactly one valid token
+# (M = 257, 513) and the last vocabulary tile one row (V = 257), so a tail-tile error is a whole
+# token's or a whole dW row's and the per-token / per-row gates see it undiluted.
+ONE_IN_TAIL = [
+    (257, 64, 257, "bf16", 30.0, 0.1),
+    (513, 128, 1000, "bf16", 0.0, 0.1),
+    (257, 128, 257, "f32", 0.0, 0.5),
+    (513, 192, 257, "bf16", 50.0, 0.1),
+]
+
+
+@pytest.mark.parametrize("M,d,V,dtype,cap,lam", ONE_IN_TAIL)
+def test_one_token_and_one_row_tails(M, d, V, dtype, cap, lam):
+    inp = _custom(M, d, V, dtype, cap, lam, seed=3 * M + V, pad=False)
+    say(f"[case] {inp.cfg.name}")
+    assert inp.labels[-1] != -100
+    assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name)
+
+
+def test_ignored_rows_with_huge_logits_no_softcap():
+    # Without a softcap, padding and ignored tokens whose raw logits exceed the float range of
+    # e^raw must still get zero coefficients: dh rows exactly zero, dW finite and at parity.
+    inp = _custom(300, 128, 1000, "bf16", 0.0, 0.1, seed=12)
+    ign = np.nonzero(inp.labels == -100)[0]
+    inp.h[ign] = inp.h[ign] * 40.0             # raw logits of std ~120 on these rows
+    say(f"[case] ignored rows with logits up to {float((inp.h[ign].float() @ inp.w.float().T).max()):.0f}")
+    gpu = run_gpu(inp)
+    assert np.isfinite(gpu["dW"]).all() and np.isfinite(gpu["dh"]).all()
+    assert np.all(gpu["dh"][ign] == 0.0)
+    assert_parity(gpu, run_oracle(inp), "huge-ignored-logits")
 
 
 def test_ragged_q4():
@@ -226,23 +265,56 @@ def test_dh_bf16_is_the_fp32_dh_rounded_once(case):
         assert e <= TOL_GRAD
 
 
-def test_softcap_limit_with_saturated_logits():
-    # The supported edge: softcap 40 with every raw logit hugely negative, so every z sits at the
-    # lower end -40 and the forward's fixed-reference terms are e^(z - cap) ~ e^-80 (still normal
-    # floats). All logits then tie: logp = -ln V exactly (up to rounding), lse = -40 + ln V, and
+@pytest.mark.parametrize("cap", [40.0, 50.0, 1024.0])
+def test_softcap_with_saturated_logits(cap):
+    # Every raw logit hugely negative, so every z sits at the lower end -cap: at 40 the edge of the
+    # fixed softmax reference (terms e^(z - cap) ~ e^-80, still normal floats), above it the running
+    # maximum. All logits then tie: logp = -ln V exactly (up to rounding), lse = -cap + ln V, and
     # sech^2 underflows so dh and dW vanish. The oracle agrees.
-    inp = _custom(300, 64, 1000, "bf16", 40.0, 0.1, seed=11)
+    inp = _custom(300, 64, 1000, "bf16", cap, 0.1, seed=11)
     inp.h.copy_(torch.ones_like(inp.h))
-    inp.w.copy_(torch.full_like(inp.w, -40.0))          # raw = -2560 for every (token, vocab)
-    say("[case] softcap 40, saturated logits")
+    inp.w.copy_(torch.full_like(inp.w, -2.0 * cap))      # raw = -128 cap for every (token, vocab)
+    say(f"[case] softcap {cap}, saturated logits")
     gpu = run_gpu(inp)
     valid = inp.labels != -100
     assert gpu["fwd_status"] == 0
-    assert np.allclose(gpu["logp"][valid], -np.log(1000.0), rtol=0, atol=1e-5)
-    assert np.allclose(gpu["lse"][valid], -40.0 + np.log(1000.0), rtol=0, atol=1e-4)
+    # z and lse are fp32 values of magnitude ~cap: allow 16 units in the last place of cap.
+    atol = 1e-5 + 16.0 * cap * 2.0 ** -24
+    assert np.allclose(gpu["logp"][valid], -np.log(1000.0), rtol=0, atol=atol)
+    assert np.allclose(gpu["lse"][valid], -cap + np.log(1000.0), rtol=0, atol=atol)
     assert np.all(gpu["dh"] == 0) and np.all(gpu["dW"] == 0)
     ora = run_oracle(inp)
-    assert rel(gpu["logp"], ora["logp"]) < 1e-5
+    assert np.max(np.abs(gpu["logp"] - ora["logp"])) <= atol
+
+
+def test_empty_batch_zeroes_dW():
+    # M = 0: nothing to compute; dW (overwritten by default) is set to zero, or left as it is when
+    # accumulating.
+    d = dev()
+    h = torch.empty(0, 128, dtype=torch.bfloat16, device=d)
+    w = torch.randn(300, 128, device=d).to(torch.bfloat16)
+    labels = torch.empty(0, dtype=torch.int32, device=d)
+    lse = torch.empty(0, dtype=torch.float32, device=d)
+    dW = torch.full((300, 128), 7.0, device=d)
+    H.head_bwd(h, w, labels, lse, lse, 30.0, dW=dW, accumulate=True)
+    torch.cuda.synchronize()
+    assert bool((dW == 7.0).all())
+    H.head_bwd(h, w, labels, lse, lse, 30.0, dW=dW)
+    torch.cuda.synchronize()
+    assert bool((dW == 0.0).all())
+
+
+def test_orpo_check_reports_data_errors():
+    d = dev()
+    inp = _custom(300, 64, 1000, "bf16", 0.0, 0.1, seed=13)
+    h, w = inp.h.to(d), inp.w.to(d)
+    lab = torch.from_numpy(inp.labels).to(d)
+    _, _, ws = H.head_fwd(h, w, lab, 0.0, return_ws=True)
+    assert H.check(ws)
+    bad = inp.labels.copy()
+    bad[3] = 1000                          # == V: out of range
+    _, _, ws = H.head_fwd(h, w, torch.from_numpy(bad).to(d), 0.0, return_ws=True)
+    assert not H.check(ws) and H.read_status(ws) == 1
 
 
 def test_head_step_dh_bf16_matches_rounded_fp32():

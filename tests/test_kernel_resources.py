@@ -66,8 +66,11 @@ def test_gemm_kernels_keep_two_waves_per_simd(resources):
 
 
 def test_scalar_spills_stay_small(resources):
+    # Forward: up to 40. The running-maximum variants with per-tile maxima park the 16 LDS
+    # addresses of their direct loads in VGPR lanes (one v_readlane per load, the cost of the
+    # v_readfirstlane each load took when the addresses were computed per lane).
     for name, res in _kernels(resources, "_ZN4orpo10fwd_kernel").items():
-        assert int(res["SGPRs Spill"]) <= 32, (name, res["SGPRs Spill"])
+        assert int(res["SGPRs Spill"]) <= 40, (name, res["SGPRs Spill"])
     for name, res in _kernels(resources, "_ZN4orpo10bwd_kernel").items():
         # The last template flag selects FP8 logit operands (more live scale state).
         f8 = name.endswith("ELb1EEEvNS_7BwdArgsE")
