@@ -118,6 +118,26 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
                           size_t ws_bytes, hipStream_t stream);
 
 /*
+ * orpo_head_fwd_noalloc — orpo_head_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * kernels and results, bit for bit, with the workspace taken from a file-scope device array of
+ * ORPO_NOALLOC_SCRATCH_BYTES bytes (4 MiB) that the library holds on each GPU it runs on
+ * until the process ends. No hipMalloc, hipFree or other allocation happens in the call.
+ *   desc, h, W, labels, logp, lse, stream as for orpo_head_fwd (no ws arguments).
+ *   Returns ORPO_ENOWS when the forward's workspace for desc (orpo_head_fwd_workspace_bytes)
+ *   exceeds that size: about 256 + 8 * max(65536, M) bytes (+ 32 per 256 x 256 tile with
+ *   skip_eps > 0), i.e. up to ~500k tokens; nothing is enqueued then.
+ *   Every call on a GPU shares that GPU's array, so calls that overlap on one GPU (different
+ *   streams, or threads) race and must be ordered by the caller. The array's device status word
+ *   is overwritten by the next call: data-error bits are not reported by this entry point (a bad
+ *   label is still treated as ignored, as in orpo_head_fwd).
+ */
+#define ORPO_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+orpo_status orpo_head_fwd_noalloc(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                                  const int32_t* labels, float* logp, float* lse,
+                                  hipStream_t stream);
+
+/*
  * orpo_loss — segmented per-branch mean, scalar ORPO epilogue (float64) and per-token cotangent.
  *   ell_b = mean of logp over the valid tokens of branch b = [off[b], off[b+1]); branch 2p is the
  *   chosen, 2p+1 the rejected response of pair p. With log1mexp(x) = log(max(1 - e^x, 1e-12)):

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/orpo_head.h"
@@ -324,6 +325,56 @@ orpo_status orpo_head_fwd(const orpo_head_desc* desc, const void* h, orpo_weight
   if (st != ORPO_OK) return st;
   if ((st = check_weight(k, W)) != ORPO_OK) return st;
   return fwd_impl(desc, k, h, W, nullptr, labels, logp, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The allocation-free forward's workspace: one file-scope array per GPU, held until the process
+// ends. Host code never passes the array's name to a kernel (in host code it is a stand-in, not a
+// device address): hipGetSymbolAddress gives each device's own copy, taken once per device on the
+// first call there, with that device current.
+constexpr size_t kNoAllocBytes = ORPO_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kNoAllocBytes];
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+orpo_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  ORPO_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return ORPO_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    ORPO_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return ORPO_EHIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ORPO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+orpo_status orpo_head_fwd_noalloc(const orpo_head_desc* desc, const void* h, orpo_weight W,
+                                  const int32_t* labels, float* logp, float* lse,
+                                  hipStream_t stream) {
+  Kind k;
+  orpo_status st = check_desc(desc, &k);
+  if (st != ORPO_OK) return st;
+  if ((st = check_weight(k, W)) != ORPO_OK) return st;
+  const FwdPlan p = plan_fwd(desc);
+  if (p.ws > kNoAllocBytes) return ORPO_ENOWS;   // the scratch array is too small for this call
+  if (desc->M == 0) return ORPO_OK;
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != ORPO_OK) return st;
+  // Nothing in the workspace needs clearing: the forward kernel zeroes the status word itself and
+  // every partial it later reads is written by this call.
+  return fwd_impl(desc, k, h, W, nullptr, labels, logp, lse, ws, p.ws, stream);
 }
 
 orpo_status orpo_head_fwd_fp8(const orpo_head_desc* desc, const orpo_fp8_operands* q,

@@ -48,6 +48,7 @@ _SIGS = {
     "orpo_head_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(Desc)]),
     "orpo_loss_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32]),
     "orpo_head_fwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "orpo_head_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P]),
     "orpo_loss": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
                                  ctypes.c_int32, ctypes.c_double, _P, _P, _P, ctypes.c_size_t, _P]),
     "orpo_loss_full": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
@@ -249,6 +250,25 @@ def head_fwd(h, w, labels, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None, 
     _check(L.orpo_head_fwd(ctypes.byref(desc), _ptr(h), wt, _ptr(labels), _ptr(logp), _ptr(lse),
                            _ptr(ws), ws.numel(), _stream(h.device)), "orpo_head_fwd")
     return (logp, lse, ws) if return_ws else (logp, lse)
+
+
+def head_fwd_noalloc(h, w, labels, logp, lse, softcap=0.0, ignore_index=IGNORE_INDEX, scales=None,
+                     biases=None):
+    """orpo_head_fwd_noalloc: logp[M] and lse[M] written into the caller's float32 tensors, the
+    workspace taken from the library's own device array (nothing allocated, here or in the call)."""
+    _head_dtypes(h, w, labels, scales, biases)
+    _need_dtype("logp", logp, torch.float32)
+    _need_dtype("lse", lse, torch.float32)
+    M, d, V = _head_shapes(h, w, labels, scales, biases)
+    _need_shape("logp", logp, (M,))
+    _need_shape("lse", lse, (M,))
+    _need_gpu(h, w, labels, scales, biases, logp, lse)
+    desc = make_desc(M, d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index)
+    wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
+                None if biases is None else biases.data_ptr())
+    _check(lib().orpo_head_fwd_noalloc(ctypes.byref(desc), _ptr(h), wt, _ptr(labels), _ptr(logp),
+                                       _ptr(lse), _stream(h.device)), "orpo_head_fwd_noalloc")
+    return logp, lse
 
 
 SCOPES = {"response": 2, "full": 3}   # spans per pair in seg_offsets
