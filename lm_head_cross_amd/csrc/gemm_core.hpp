@@ -233,10 +233,7 @@ struct DmaKS {
   // (within a row) goes in the scalar offset. A row past n_rows starts past the range, so all of it
   // reads as zero.
   __device__ __forceinline__ void issue(int64_t row0, int64_t kb, char* stage) {
-    if (row0 != rs_row0) {        // a new tile: rebuild the descriptor (once per tile)
-      rs = make_rsrc(base + row0 * ld, (n_rows - row0) * ld);
-      rs_row0 = row0;
-    }
+    rs = make_rsrc(base + row0 * ld, (n_rows - row0) * ld);   // branch-free: see gemm_step
     char* s = stage + wave_lds;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(rs, s + i * 1024, voff[i], (uint32_t)kb);
@@ -436,6 +433,23 @@ __device__ __forceinline__ void sched_groups() {
   }
 }
 
+// The post-barrier region of a K-major step: one K group's MFMAs, the next stage's first-group
+// reads after the first ones, and one direct load (VMEM read) after each MFMA.
+template <class E, bool AK, bool BK>
+__device__ __forceinline__ void sched_groups_loads() {
+  constexpr int kReads = 4 * reads_per_frag<E, AK>() + 2 * reads_per_frag<E, BK>();
+  constexpr int kMfma = 8 * mfma_per_mma<E>();
+  constexpr int kSpan = kMfma * 3 / 4;
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    const int n = i < kSpan ? (i + 1) * kReads / kSpan - i * kReads / kSpan : 0;
+    if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
 // Row scales fetched before a step's wait are taken here, right after it: the compiler then counts
 // their loads as done at this point and does not place its own wait for them after the next
 // step's direct loads are issued (which would make the fragment reads wait for those loads).
@@ -557,7 +571,8 @@ struct StepPos {
   }
 };
 
-template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi, class Scl>
+template <class E, bool AK, bool BK, bool kClear, bool kDmaOnly, class Issue, class Commit,
+          class Epi, class Scl>
 __device__ __forceinline__ void gemm_step(int s, int total, int nk, StepPos& cur, StepPos& ahead,
                                           char* __restrict__ ca,
                                           char* __restrict__ cb, char* __restrict__ na,
@@ -593,13 +608,25 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, StepPos& cur
   vm_wait();
   hold_scales(sc_next);
   __syncthreads();
-  if (s + 2 < total) issue(ahead.tile, ahead.ks, ca, cb);
-  ahead.next(nk);
-  if constexpr (E::kSets == 2) {
+  if constexpr (E::kSets == 2 && kDmaOnly) {
+    // The loads of step s + 2 go out one after each MFMA of this region instead of as one burst
+    // of every wave after the barrier. They are issued unconditionally so that they share the
+    // MFMAs' basic block: only for direct loads through buffer descriptors, which past the last
+    // step read zeros or bytes inside the operand's range into a stage that is never read again.
+    issue(ahead.tile, ahead.ks, ca, cb);
+    ahead.next(nk);
+    load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+    mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
+    sched_groups_loads<E, AK, BK>();
+  } else if constexpr (E::kSets == 2) {
+    if (s + 2 < total) issue(ahead.tile, ahead.ks, ca, cb);
+    ahead.next(nk);
     load_frags<E, AK, BK>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
     mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
     sched_groups<E, AK, BK, 1>();
   } else {
+    if (s + 2 < total) issue(ahead.tile, ahead.ks, ca, cb);
+    ahead.next(nk);
     group_tail<E, AK, BK>(acc, f, a_last, na, nb, 0, sc, wm, wn, l);
   }
   if (ends_tile) {
@@ -614,7 +641,8 @@ __device__ __forceinline__ void gemm_step(int s, int total, int nk, StepPos& cur
 // barrier before the last group measured slower): the next step's loads are issued first, then the
 // MFMAs of the four groups with each group's reads one group ahead (left to the compiler's
 // schedule), then the step's epilogue, wait and barrier.
-template <class E, bool AK, bool BK, bool kClear, class Issue, class Commit, class Epi, class Scl>
+template <class E, bool AK, bool BK, bool kClear, bool kDmaOnly, class Issue, class Commit,
+          class Epi, class Scl>
 __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, StepPos& cur,
                                               StepPos& ahead, char* __restrict__ ca,
                                               char* __restrict__ cb, char* __restrict__ na,
@@ -623,7 +651,10 @@ __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, StepPos&
                                               typename E::Scales& sc_next, f32x16 (&acc)[4][2],
                                               int wm, int wn, int l) {
   constexpr int kG = E::kGroups;
-  if (s + 1 < total) issue(ahead.tile, ahead.ks, na, nb);   // ahead = step s + 1 here
+  // ahead = step s + 1 here. Direct loads only: issued unconditionally (as in gemm_step) and
+  // pinned one after each of the step's first MFMAs rather than as one burst before them.
+  if constexpr (kDmaOnly) issue(ahead.tile, ahead.ks, na, nb);
+  else if (s + 1 < total) issue(ahead.tile, ahead.ks, na, nb);
   ahead.next(nk);
   static_assert(E::kSets == 2, "transposing stages read the next group ahead");
   FragSets<E> f;
@@ -633,6 +664,13 @@ __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, StepPos&
     if (kg + 1 < kG)
       load_frags<E, AK, BK>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
     mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
+  }
+  if constexpr (kDmaOnly) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
   }
   const bool ends_tile = cur.ks == nk - 1;
   if (s + 1 < total) commit(na, nb);
@@ -656,8 +694,8 @@ __device__ __forceinline__ void gemm_step_end(int s, int total, int nk, StepPos&
 //   scales(tile): the MFMA row scales of a tile (fp8; gemm_run passes none for other formats).
 // Two stages: step s + 1's loads are in flight during step s's MFMAs. The loop is unrolled by two
 // so that every step reads and fills statically known stages.
-template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi,
-          class Scl>
+template <class E, bool AK, bool BK, bool kClear = true, bool kDmaOnly = false, class Issue,
+          class Commit, class Epi, class Scl>
 __device__ __forceinline__ void gemm_run_scaled(const Smem& sm, int n_tiles, int nk, Issue&& issue,
                                                 Commit&& commit, Epi&& epi, Scl&& scales,
                                                 f32x16 (&acc)[4][2]) {
@@ -675,13 +713,15 @@ __device__ __forceinline__ void gemm_run_scaled(const Smem& sm, int n_tiles, int
   if constexpr (!(AK && BK)) {
     // Transposing reads: barrier at the end of each step; `ahead` runs one step ahead.
     for (int it = 0; it < total; it += 2) {
-      gemm_step_end<E, AK, BK, kClear>(it, total, nk, cur, ahead, sm.a0, sm.b0, sm.a1, sm.b1,
-                                       issue, commit, epi, scales, sc, sc_next, acc, wm, wn, l);
+      gemm_step_end<E, AK, BK, kClear, kDmaOnly>(it, total, nk, cur, ahead, sm.a0, sm.b0, sm.a1,
+                                                 sm.b1, issue, commit, epi, scales, sc, sc_next,
+                                                 acc, wm, wn, l);
       if (it + 1 < total)
-        gemm_step_end<E, AK, BK, kClear>(it + 1, total, nk, cur, ahead, sm.a1, sm.b1, sm.a0,
-                                         sm.b0, issue, commit, epi, scales, sc, sc_next, acc, wm,
-                                         wn, l);
+        gemm_step_end<E, AK, BK, kClear, kDmaOnly>(it + 1, total, nk, cur, ahead, sm.a1, sm.b1,
+                                                   sm.a0, sm.b0, issue, commit, epi, scales, sc,
+                                                   sc_next, acc, wm, wn, l);
     }
+    vm_wait();   // the loads past the last step
     return;
   }
   // K-major stages: `ahead` runs two steps ahead.
@@ -690,19 +730,23 @@ __device__ __forceinline__ void gemm_run_scaled(const Smem& sm, int n_tiles, int
   FragSets<E> f;
   load_frags<E, AK, BK>(sm.a0, sm.b0, 0, wm, wn, l, f.a[0], f.b[0]);
   for (int it = 0; it < total; it += 2) {
-    gemm_step<E, AK, BK, kClear>(it, total, nk, cur, ahead, sm.a0, sm.b0, sm.a1, sm.b1, issue,
-                                 commit, epi, scales, sc, sc_next, f, acc, wm, wn, l);
+    gemm_step<E, AK, BK, kClear, kDmaOnly>(it, total, nk, cur, ahead, sm.a0, sm.b0, sm.a1, sm.b1,
+                                           issue, commit, epi, scales, sc, sc_next, f, acc, wm,
+                                           wn, l);
     if (it + 1 < total)
-      gemm_step<E, AK, BK, kClear>(it + 1, total, nk, cur, ahead, sm.a1, sm.b1, sm.a0, sm.b0,
-                                   issue, commit, epi, scales, sc, sc_next, f, acc, wm, wn, l);
+      gemm_step<E, AK, BK, kClear, kDmaOnly>(it + 1, total, nk, cur, ahead, sm.a1, sm.b1, sm.a0,
+                                             sm.b0, issue, commit, epi, scales, sc, sc_next, f,
+                                             acc, wm, wn, l);
   }
+  vm_wait();   // the loads past the last step, before the caller reuses the LDS
 }
 
-template <class E, bool AK, bool BK, bool kClear = true, class Issue, class Commit, class Epi>
+template <class E, bool AK, bool BK, bool kClear = true, bool kDmaOnly = false, class Issue,
+          class Commit, class Epi>
 __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Issue&& issue,
                                          Commit&& commit, Epi&& epi, f32x16 (&acc)[4][2]) {
-  gemm_run_scaled<E, AK, BK, kClear>(sm, n_tiles, nk, issue, commit, epi,
-                                     [](int) { return typename E::Scales{}; }, acc);
+  gemm_run_scaled<E, AK, BK, kClear, kDmaOnly>(sm, n_tiles, nk, issue, commit, epi,
+                                               [](int) { return typename E::Scales{}; }, acc);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   };
   f32x16 acc[4][2];
   zero_acc(acc);
-  gemm_run_scaled<E, true, true>(smem, n_tiles, nk, issue, commit, epi, scales, acc);
+  gemm_run_scaled<E, true, true, true, !Q4>(smem, n_tiles, nk, issue, commit, epi, scales, acc);
 
   // Combine the lane pair (l, l ^ 32), then the two m-waves, and write this split's partials.
 #pragma unroll
@@ -692,7 +692,7 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run_scaled<EL, true, true, false>(smem, 1, nk, issue, commit, nop, scales, acc);
+  gemm_run_scaled<EL, true, true, false, !Q4>(smem, 1, nk, issue, commit, nop, scales, acc);
 
   typedef typename E::T T;
   T* out = (T*)it.coeff;
@@ -980,7 +980,7 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, true, false, false>(smem, 1, n_run, issue, commit, nop, acc);
+  gemm_run<E, true, false, false, !Q4 && !SKIP>(smem, 1, n_run, issue, commit, nop, acc);
   (void)tid;
   if (!a.dh16) {
     if (n_run > 0 || it.dh_first)
@@ -1024,7 +1024,7 @@ __device__ __forceinline__ void dw_tile(const Smem& smem, const BwdArgs& a, cons
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, false, false, false>(smem, 1, n_run, issue, commit, nop, acc);
+  gemm_run<E, false, false, false, !SKIP>(smem, 1, n_run, issue, commit, nop, acc);
   if (n_run > 0 || it.dw_first)
     store_out<E>(a.dW, a.d, it.v0 + vl0, min(a.V, it.v0 + it.BV_cur), j0, a.d, it.dw_first != 0, acc);
 }
