@@ -282,19 +282,26 @@ struct DmaMN {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (lo in the low half), each rounded to nearest even: one
+// v_cvt_pk_bf16_f32 (converting the halves one at a time costs two of them plus a shift and an or).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;   // round to nearest even
-  return (uint32_t)__builtin_bit_cast(unsigned short, a) |
-         ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// 8 codes of one packed word -> 8 bf16 (16 bytes): w = scale * q + bias in fp32, then RNE.
+// 8 codes of one packed word -> 8 bf16 (16 bytes): w = scale * q + bias in fp32, then RNE. The
+// even and odd codes are masked into the four bytes of two words, which the byte-to-float
+// conversions (v_cvt_f32_ubyte0..3) read directly.
 __device__ __forceinline__ u32x4 dequant_word(uint32_t w, float scale, float bias) {
+  const uint32_t even = w & 0x0F0F0F0Fu;           // codes 0, 2, 4, 6
+  const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;     // codes 1, 3, 5, 7
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float q0 = (float)((w >> (8 * i)) & 0xFu);
-    const float q1 = (float)((w >> (8 * i + 4)) & 0xFu);
+    const float q0 = (float)((even >> (8 * i)) & 0xFFu);
+    const float q1 = (float)((odd >> (8 * i)) & 0xFFu);
     o[i] = pack_bf16x2(__builtin_fmaf(scale, q0, bias), __builtin_fmaf(scale, q1, bias));
   }
   return o;

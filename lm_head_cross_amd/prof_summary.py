@@ -3,6 +3,7 @@
   python -m lm_head_cross_amd.prof_summary stats  KERNEL_STATS.csv  OUT.md  "<command>"
   python -m lm_head_cross_amd.prof_summary traffic FETCH.csv WRITE.csv KERNEL_SUBSTRING OUT.txt "<commands>" [KIND]
   python -m lm_head_cross_amd.prof_summary mfma   COUNTERS.csv OUT.txt "<command>"
+  python -m lm_head_cross_amd.prof_summary stalls OUT.md "<commands>" PASS1.csv PASS2.csv ...
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same counters read for the
 plain 1 GiB device copy that `bench.py --copy-calibration` runs, averages them over the dispatches of
@@ -158,6 +159,67 @@ def mfma_txt(counters_csv: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
+# Counters of the stall table: (counter, unit, meaning). SQ counters are summed over the GPU's
+# shader engines; "quad" counters count units of 4 cycles per wave, the others cycles per CU.
+STALL_COUNTERS = [
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "simd", "MFMA pipe busy"),
+    ("SQ_VALU_MFMA_COEXEC_CYCLES", "simd", "MFMA busy while a VALU instruction issues"),
+    ("SQ_ACTIVE_INST_VALU", "quad", "waves issuing VALU"),
+    ("SQ_ACTIVE_INST_SCA", "quad", "waves issuing SALU / SMEM"),
+    ("SQ_ACTIVE_INST_LDS", "quad", "waves issuing LDS"),
+    ("SQ_ACTIVE_INST_VMEM", "quad", "waves issuing VMEM"),
+    ("SQ_WAIT_INST_ANY", "quad", "waves waiting to issue (dependency, waitcnt, barrier)"),
+    ("SQ_WAIT_INST_LDS", "quad", "waves waiting to issue an LDS instruction"),
+    ("SQ_WAIT_ANY", "quad", "waves waiting for anything"),
+    ("SQ_LDS_IDX_ACTIVE", "cu", "LDS busy with indexed (ds_*) accesses"),
+    ("SQ_LDS_BANK_CONFLICT", "cu", "LDS stalled by bank conflicts"),
+    ("SQ_LDS_ADDR_CONFLICT", "cu", "LDS stalled by address conflicts"),
+    ("SQ_WAVE_CYCLES", "quad", "resident waves"),
+]
+CUS = 256
+
+
+def stalls_md(csvs, command: str, kernel_substr: str = "orpo::") -> str:
+    """Per kernel and grid size: each counter of STALL_COUNTERS normalised to the dispatch's own
+    cycles (GRBM_GUI_ACTIVE / 8 XCDs), as a fraction of SIMD cycles (MFMA counters), of wave
+    slots on a CU (quad counters x 4 / 8 waves), or of CU cycles (LDS counters)."""
+    per = {}   # (kernel, grid) -> counter -> [values], plus "cyc"
+    for path in csvs:
+        disp = {}
+        for r in _rows(path):
+            if kernel_substr not in r["Kernel_Name"]:
+                continue
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))
+            disp.setdefault((key, r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        for (key, _), d in disp.items():
+            if "GRBM_GUI_ACTIVE" not in d:
+                continue
+            cyc = d["GRBM_GUI_ACTIVE"] / XCDS
+            e = per.setdefault(key, {})
+            for c, v in d.items():
+                if c != "GRBM_GUI_ACTIVE":
+                    e.setdefault(c, []).append(v / cyc)
+    out = ["Where the cycles of the head's kernels go (rocprofv3 counters, one pass per 8 SQ counters;",
+           "each value normalised to the dispatch's own cycles, GRBM_GUI_ACTIVE / 8 XCDs).",
+           "simd = fraction of SIMD cycles (1024 SIMDs); wave = fraction of the 8 wave slots of a CU",
+           "(quad-cycle counters x 4 / 8); cu = fraction of CU cycles (256 CUs).", "",
+           f"commands: {command}", f"source_hash: {source_hash()}", ""]
+    for (name, grid), e in sorted(per.items(), key=lambda kv: -kv[0][1]):
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in e:
+            continue
+        short = name if len(name) <= 70 else name[:67] + "..."
+        out += [f"## `{short}` (grid {grid} threads)", "", "| counter | unit | value | meaning |",
+                "|---|---|---|---|"]
+        for c, unit, meaning in STALL_COUNTERS:
+            if c not in e:
+                continue
+            v = sum(e[c]) / len(e[c])
+            frac = v / (CUS * 4) if unit == "simd" else (v * 4 / (CUS * 8) if unit == "quad" else v / CUS)
+            out.append(f"| {c} | {unit} | {frac:.3f} | {meaning} |")
+        out.append("")
+    return "\n".join(out)
+
+
 def main(argv):
     if argv[1] == "stats":
         open(argv[3], "w").write(kernel_stats_md(argv[2], os.path.basename(argv[3]), argv[4]))
@@ -166,6 +228,8 @@ def main(argv):
         open(argv[5], "w").write(traffic_txt(argv[2], argv[3], argv[4], argv[6], kind))
     elif argv[1] == "mfma":
         open(argv[3], "w").write(mfma_txt(argv[2], argv[4]))
+    elif argv[1] == "stalls":   # stalls OUT.md "<commands>" CSV...
+        open(argv[2], "w").write(stalls_md(argv[4:], argv[3]))
     else:
         raise SystemExit(__doc__)
 

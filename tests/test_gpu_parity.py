@@ -41,6 +41,11 @@ def test_q4_head_one_pair():
     _check_config(synth.reduced(synth.workload("q4g64-minicpm-shape-softcap30"), 1))
 
 
+def test_q4_head_e4b_shape_one_pair():
+    # The 4-bit head at the e4b shape (d = 2560, V = 262144), one pair against the full oracle.
+    _check_config(synth.reduced(synth.workload("q4g64-e4b-shape-softcap30"), 1))
+
+
 def test_12b_shape_short_pair():
     cfg = synth.workload("12b-like-bf16-softcap30").replace(pairs=1, M=512, len_lo=200, len_hi=256, name="12b-like-short")
     _check_config(cfg)
