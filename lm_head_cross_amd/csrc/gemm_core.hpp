@@ -65,6 +65,11 @@ __device__ __forceinline__ int swz_mn32(int r) { return ((r >> 2) & 1) << 3; }
 
 // Wait until this wave's outstanding vector-memory operations (including LDS-direct loads) are done.
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same wait as an instruction the compiler's wait insertion sees (s_waitcnt immediate on gfx9:
+// vmcnt bits [3:0] and [15:14] zero, expcnt 7 and lgkmcnt 15, i.e. not waited on): loads issued
+// before it then count as complete, so no later vmcnt wait is added for them, also where the
+// paths into a loop header would otherwise merge to vmcnt(0).
+__device__ __forceinline__ void vm_wait_seen() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
@@ -213,13 +218,11 @@ struct DmaKS {
   int64_t ld, n_rows;
   uint32_t voff[4];
   int wave_lds;                   // this wave's 4 KiB of a stage (uniform: an SGPR)
-  int64_t rs_row0;                // the rows the cached descriptor covers start here (-1: none)
   __amdgpu_buffer_rsrc_t rs;
   __device__ __forceinline__ void init(const void* b, int64_t ld_bytes, int64_t rows) {
     base = (const char*)b;
     ld = ld_bytes;
     n_rows = rows;
-    rs_row0 = -1;
     wave_lds = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) * 4096);
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
@@ -295,8 +298,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // even and odd codes are masked into the four bytes of two words, which the byte-to-float
 // conversions (v_cvt_f32_ubyte0..3) read directly.
 __device__ __forceinline__ u32x4 dequant_word(uint32_t w, float scale, float bias) {
-  const uint32_t even = w & 0x0F0F0F0Fu;           // codes 0, 2, 4, 6
-  const uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;     // codes 1, 3, 5, 7
+  uint32_t even = w & 0x0F0F0F0Fu;                 // codes 0, 2, 4, 6
+  uint32_t odd = (w >> 4) & 0x0F0F0F0Fu;           // codes 1, 3, 5, 7
+  // Opaque to the compiler, which would otherwise fold the masks into one bit-field extract per
+  // code: each byte then converts in one instruction (v_cvt_f32_ubyte0..3).
+  asm("" : "+v"(even));
+  asm("" : "+v"(odd));
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -344,6 +351,46 @@ struct Q4K {
     for (int w = 0; w < 4; ++w)
       *(u32x4*)(row + (((tid & 1) * 4 + w) ^ swz_k(r)) * 16) = dequant_word(q[w], scale, bias);
   }
+};
+
+// 4-bit weights as a K-major operand with two register sets (gemm_run_q4k): the words of a step
+// are loaded three steps ahead into set S and dequantised into LDS during the step before their
+// use, interleaved with that step's MFMAs. Same layout per thread as Q4K. Rows past the vocabulary
+// read row 0 (in bounds) and are zeroed at commit; callers keep k0 inside the row.
+struct Q4K2 {
+  Q4Weight W;
+  u32x4 q[2];
+  // bf16 bits of the group's scale and bias, each in a register of its own: nothing combines
+  // them before the commit, so no ALU op waits on these loads where they are issued.
+  uint16_t sbits[2], bbits[2];
+  bool ok[2];
+  __device__ __forceinline__ void init(const Q4Weight& w) { W = w; }
+  // live = false stages zeros (the words are still read, from row0's group at k0, in bounds).
+  template <int S>
+  __device__ __forceinline__ void issue(int64_t row0, int64_t k0, bool live) {
+    const int tid = threadIdx.x;
+    const int64_t gr = row0 + (tid >> 1);
+    const bool in = gr < W.V && live;
+    const int64_t r = in ? gr : 0;
+    q[S] = *(const u32x4*)(W.wq + r * (W.d >> 3) + (k0 >> 3) + (tid & 1) * 4);
+    const int64_t gi = r * (W.d >> 6) + (k0 >> 6);
+    sbits[S] = W.scales[gi];
+    bbits[S] = W.biases[gi];
+    ok[S] = in;
+  }
+  // Words [W0, W1) of set S (8 codes each) into the stage, one 16-byte LDS write per word.
+  template <int S, int W0, int W1>
+  __device__ __forceinline__ void commit_words(char* stage) const {
+    const int tid = threadIdx.x, r = tid >> 1;
+    const float scale = ok[S] ? bf16_bits_to_f32(sbits[S]) : 0.f;
+    const float bias = ok[S] ? bf16_bits_to_f32(bbits[S]) : 0.f;
+    char* row = stage + r * kKBytes;
+#pragma unroll
+    for (int w = W0; w < W1; ++w)
+      *(u32x4*)(row + (((tid & 1) * 4 + w) ^ swz_k(r)) * 16) = dequant_word(q[S][w], scale, bias);
+  }
+  template <int S>
+  __device__ __forceinline__ void commit(char* stage) const { commit_words<S, 0, 4>(stage); }
 };
 
 // 4-bit weights as an N-major operand (rows = vocabulary = k, columns = hidden = n): 64 rows x
@@ -754,6 +801,118 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
                                          Commit&& commit, Epi&& epi, f32x16 (&acc)[4][2]) {
   gemm_run_scaled<E, AK, BK, kClear, kDmaOnly>(sm, n_tiles, nk, issue, commit, epi,
                                                [](int) { return typename E::Scales{}; }, acc);
+}
+
+// ------------------------------------------------------------------------------------------
+// The 4-bit head's K-major loop (forward and coefficient tiles, A = the 4-bit weights, B dense).
+// The two-stage schedule of gemm_step with the A operand one step further ahead: at step s's
+// barrier the words of step s + 3 are loaded (register set (s + 1) % 2) and B's direct loads of
+// step s + 2 issued; during step s's first three K groups the words of step s + 1 (loaded at step
+// s - 2's barrier, complete since step s - 1's) are dequantised into step s + 1's stage, their
+// VALU work and LDS writes pinned between the MFMAs, where the dequantisation used to run alone
+// before the barrier.
+//   issue_a(set, tile, ks): load the words of step (tile, ks) into set `set` (integral_constant)
+//   commit_a(set, stageA, w0, w1): dequantise words [w0, w1) of set `set` into stageA
+//   issue_b(tile, ks, stageB): B's direct loads of step (tile, ks)
+// With an odd number nk of K steps a tile runs nk + 1, the last (ks == nk) staging zeros in both
+// operands, so that the steps come in pairs; issue_a and issue_b see ks == nk there.
+// ------------------------------------------------------------------------------------------
+// One K group of region 1 in a 4-bit step: per MFMA its share of the next group's fragment
+// reads and of the VALU work of `kWords` dequantised words, each word's LDS write after its
+// share. Each group is its own scheduling region (sched_barrier(0) after it), so that the
+// dequantisation cannot gather in one block.
+template <class E, int kWords>
+__device__ __forceinline__ void sched_group_dequant() {
+  constexpr int kReads = 4 * reads_per_frag<E, true>() + 2 * reads_per_frag<E, true>();
+  constexpr int kMfma = 8 * mfma_per_mma<E>();
+  constexpr int kSpan = kMfma * 3 / 4;
+  constexpr int kValu = (kWords * 30 + kMfma - 1) / kMfma;   // ~28 VALU a word + the scale
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    const int n = i < kSpan ? (i + 1) * kReads / kSpan - i * kReads / kSpan : 0;
+    if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (kWords > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    if (kWords > 0 && (i + 1) % (kMfma / kWords) == 0)
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+  }
+}
+
+template <bool kClear, class IssueA, class CommitA, class IssueB, class Epi>
+__device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk, IssueA&& issue_a,
+                                             CommitA&& commit_a, IssueB&& issue_b, Epi&& epi,
+                                             f32x16 (&acc)[4][2]) {
+  typedef EBf16 E;
+  constexpr int kG = E::kGroups;
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  // An odd nk gets one more K step per tile that stages zeros (see above), for an even total.
+  const int nkp = nk + (nk & 1);
+  const int total = n_tiles * nkp;
+  if (total <= 0) return;
+  const typename E::Scales sc{};
+  const std::integral_constant<int, 0> set0{};
+  const std::integral_constant<int, 1> set1{};
+  StepPos cur{0, 0}, pa{0, 0}, pb{0, 0};
+  issue_b(pb.tile, pb.ks, sm.b0);
+  pb.next(nkp);
+  issue_a(set0, pa.tile, pa.ks);   // step 0
+  pa.next(nkp);
+  issue_a(set1, pa.tile, pa.ks);   // step 1
+  pa.next(nkp);
+  commit_a(set0, sm.a0, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+  issue_a(set0, pa.tile, pa.ks);   // step 2
+  pa.next(nkp);
+  issue_b(pb.tile, pb.ks, sm.b1);  // step 1
+  pb.next(nkp);
+  vm_wait_seen();
+  __syncthreads();
+  FragSets<E> f;
+  load_frags<E, true, true>(sm.a0, sm.b0, 0, wm, wn, l, f.a[0], f.b[0]);
+  auto step = [&](auto parity, int s, char* __restrict__ ca, char* __restrict__ cb,
+                  char* __restrict__ na, char* __restrict__ nb) {
+    const std::integral_constant<int, 1 - decltype(parity)::value> next_set{};
+    // Step s + 1's words into its stage (unused past the end): words 0, 1 and 2-3 with groups
+    // 0, 1 and 2.
+    static_assert(kG == 4, "the dequantisation is split over three K groups");
+    auto group = [&](auto kg_c, auto w0_c, auto w1_c) {
+      constexpr int kg = decltype(kg_c)::value;
+      load_frags<E, true, true>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
+      mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
+      commit_a(next_set, na, w0_c, w1_c);
+      sched_group_dequant<E, decltype(w1_c)::value - decltype(w0_c)::value>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    group(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+          std::integral_constant<int, 1>{});
+    group(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{},
+          std::integral_constant<int, 2>{});
+    group(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{},
+          std::integral_constant<int, 4>{});
+    const bool ends_tile = cur.ks == nkp - 1;
+    vm_wait_seen();
+    __syncthreads();
+    issue_b(pb.tile, pb.ks, cb);  // step s + 2
+    pb.next(nkp);
+    issue_a(next_set, pa.tile, pa.ks);   // step s + 3 into the set just committed
+    pa.next(nkp);
+    load_frags<E, true, true>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+    mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
+    sched_groups_loads<E, true, true>();
+    if (ends_tile) {
+      epi(cur.tile, acc);
+      if (kClear) zero_acc(acc);
+    }
+    cur.next(nkp);
+  };
+  // An even number of steps, so that no path leads from the first step's loads back to the loop
+  // header (the compiler would then wait there, on every iteration, for the words just issued).
+  for (int it = 0; it < total; it += 2) {
+    step(set0, it, sm.a0, sm.b0, sm.a1, sm.b1);
+    step(set1, it + 1, sm.a1, sm.b1, sm.a0, sm.b0);
+  }
+  vm_wait_seen();   // the loads past the last step
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with

@@ -196,35 +196,52 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int64_t t0 = (int64_t)tb * kTile;
   const int64_t row_bytes = a.d * E::kSize;
 
-  int64_t tok[2];
+  // The token of accumulator column block nb, recomputed where needed rather than held (as two
+  // 64-bit values) across the K loop.
+  auto tok_of = [&](int nb) { return t0 + acc_n(wn, nb, l); };
   int y[2];
   float m[2], s[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    tok[nb] = t0 + acc_n(wn, nb, l);
+    const int64_t tok = tok_of(nb);
     // -1 marks "no capture": rows past M and ignored tokens (ignore_index may be any value).
-    const int lab = tok[nb] < a.M ? a.labels[tok[nb]] : -1;
+    const int lab = tok < a.M ? a.labels[tok] : -1;
     y[nb] = lab == a.ignore_index ? -1 : lab;
     m[nb] = kRunMax ? kNegInf : a.cap * kLog2e;   // fixed reference: every z <= cap
     s[nb] = 0.f;
   }
   const Softcap sc(SOFTCAP ? a.cap : 1.f);
 
-  typedef typename std::conditional<Q4, Q4K, DmaKS<E::kSwzShift, E::kSwzK>>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K2, DmaKS<E::kSwzShift, E::kSwzK>>::type LoaderA;
   LoaderA la;
   DmaKS<E::kSwzShift, E::kSwzK> lb;
   if constexpr (Q4) la.init(a.q4); else la.init(a.w, row_bytes, a.V);
   lb.init(a.h, row_bytes, a.M);
   const int nk = (int)(a.d / E::kBK);
+  // Dense weights: both operands by direct loads. 4-bit weights (gemm_run_q4k): the words of a
+  // step by register loads into one of two sets (rows past V read row 0 and are zeroed), the hidden
+  // states by direct loads.
   auto issue = [&](int tile, int ks, char* sa, char* sb) {
-    const int64_t v0 = (int64_t)(tile0 + tile) * kTile;
-    if constexpr (Q4) la.issue(v0, (int64_t)ks * E::kBK, sa);
-    else la.issue(v0, (int64_t)ks * kKBytes, sa);
+    if constexpr (!Q4) la.issue((int64_t)(tile0 + tile) * kTile, (int64_t)ks * kKBytes, sa);
     lb.issue(t0, (int64_t)ks * kKBytes, sb);
   };
   auto commit = [&](char* sa, char* sb) {
-    la.commit(sa);
+    if constexpr (!Q4) la.commit(sa);
     lb.commit(sb);
+  };
+  // ks == nk: the zero step of an odd nk (gemm_run_q4k); B then reads nothing (an empty range).
+  auto issue_a = [&](auto set, int tile, int ks) {
+    if constexpr (Q4)
+      la.template issue<decltype(set)::value>((int64_t)(tile0 + tile) * kTile,
+                                              (int64_t)min(ks, nk - 1) * E::kBK, ks < nk);
+  };
+  auto commit_a = [&](auto set, char* sa, auto w0, auto w1) {
+    if constexpr (Q4)
+      la.template commit_words<decltype(set)::value, decltype(w0)::value, decltype(w1)::value>(sa);
+  };
+  auto issue_b = [&](int, int ks, char* sb) {
+    const bool live = ks < nk;
+    lb.issue(live ? t0 : a.M, live ? (int64_t)ks * kKBytes : 0, sb);
   };
   auto epi = [&](int tile, f32x16(&acc)[4][2]) {
     const int64_t vt0 = (int64_t)(tile0 + tile) * kTile;
@@ -306,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
               for (int rr = 0; rr < 16; ++rr)
                 if (mm == mb && rr == r) zsel = acc[mm][nb][rr];
             const float z = SOFTCAP ? sc.cap - 2.f * sc.cap * sc.r_of(zsel) : zsel;
-            a.logp[tok[nb]] = z;
+            a.logp[tok_of(nb)] = z;
           }
         }
       }
@@ -331,7 +348,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   };
   f32x16 acc[4][2];
   zero_acc(acc);
-  gemm_run_scaled<E, true, true, true, !Q4>(smem, n_tiles, nk, issue, commit, epi, scales, acc);
+  if constexpr (Q4) gemm_run_q4k<true>(smem, n_tiles, nk, issue_a, commit_a, issue_b, epi, acc);
+  else gemm_run_scaled<E, true, true, true, true>(smem, n_tiles, nk, issue, commit, epi, scales, acc);
 
   // Combine the lane pair (l, l ^ 32), then the two m-waves, and write this split's partials.
 #pragma unroll
@@ -367,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
       } else {
         ss += o.y;
       }
-      if (tok[nb] < a.M) a.part[(int64_t)split * a.M + tok[nb]] = make_float2(mm, ss);
+      const int64_t tok = tok_of(nb);
+      if (tok < a.M) a.part[(int64_t)split * a.M + tok] = make_float2(mm, ss);
     }
   }
 }
@@ -666,19 +685,31 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
     }
   }
 
-  typedef typename std::conditional<Q4, Q4K, DmaKS<EL::kSwzShift, EL::kSwzK>>::type LoaderA;
+  typedef typename std::conditional<Q4, Q4K2, DmaKS<EL::kSwzShift, EL::kSwzK>>::type LoaderA;
   LoaderA la;
   DmaKS<EL::kSwzShift, EL::kSwzK> lb;
   if constexpr (Q4) la.init(a.q4); else la.init(kF8 ? a.wq : a.w, row_bytes, a.V);
   lb.init(kF8 ? a.hq : a.h, row_bytes, t_end);
   const int nk = (int)(a.d / EL::kBK);
+  // As in the forward: 4-bit words through gemm_run_q4k's two register sets, the rest direct.
   auto issue = [&](int, int ks, char* sa, char* sb) {
-    if constexpr (Q4) la.issue(vbase, (int64_t)ks * E::kBK, sa);
-    else la.issue(vbase, (int64_t)ks * kKBytes, sa);
+    if constexpr (!Q4) la.issue(vbase, (int64_t)ks * kKBytes, sa);
     lb.issue(tbase, (int64_t)ks * kKBytes, sb);
   };
+  auto issue_a = [&](auto set, int, int ks) {
+    if constexpr (Q4)
+      la.template issue<decltype(set)::value>(vbase, (int64_t)min(ks, nk - 1) * E::kBK, ks < nk);
+  };
+  auto commit_a = [&](auto set, char* sa, auto w0, auto w1) {
+    if constexpr (Q4)
+      la.template commit_words<decltype(set)::value, decltype(w0)::value, decltype(w1)::value>(sa);
+  };
+  auto issue_b = [&](int, int ks, char* sb) {
+    const bool live = ks < nk;
+    lb.issue(live ? tbase : t_end, live ? (int64_t)ks * kKBytes : 0, sb);
+  };
   auto commit = [&](char* sa, char* sb) {
-    la.commit(sa);
+    if constexpr (!Q4) la.commit(sa);
     lb.commit(sb);
   };
   auto scales = [&](int) {
@@ -692,7 +723,8 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run_scaled<EL, true, true, false, !Q4>(smem, 1, nk, issue, commit, nop, scales, acc);
+  if constexpr (Q4) gemm_run_q4k<false>(smem, 1, nk, issue_a, commit_a, issue_b, nop, acc);
+  else gemm_run_scaled<EL, true, true, false, true>(smem, 1, nk, issue, commit, nop, scales, acc);
 
   typedef typename E::T T;
   T* out = (T*)it.coeff;

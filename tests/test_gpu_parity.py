@@ -137,8 +137,20 @@ def test_ignored_rows_with_huge_logits_no_softcap():
     assert_parity(gpu, run_oracle(inp), "huge-ignored-logits")
 
 
-def test_ragged_q4():
-    inp = _custom(300, 128, 1000, "bf16", 30.0, 0.1, seed=9, q4=True)
+# The 4-bit head: K steps of 64 codes, an odd count (d = 64, 192, 320) adding a step of zeros per
+# tile; a one-token tail (pad False); softcaps 0, 30 and 50 (the running maximum).
+RAGGED_Q4 = [
+    (300, 128, 1000, 30.0, True),
+    (257, 64, 257, 30.0, False),
+    (513, 192, 1000, 50.0, True),
+    (300, 320, 3001, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("M,d,V,cap,pad", RAGGED_Q4)
+def test_ragged_q4(M, d, V, cap, pad):
+    inp = _custom(M, d, V, "bf16", cap, 0.1, seed=9 if (M, d) == (300, 128) else M + d, q4=True,
+                  pad=pad)
     say(f"[case] {inp.cfg.name} q4")
     assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name + "-q4")
 

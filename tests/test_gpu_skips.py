@@ -9,7 +9,7 @@ import torch
 from lm_head_cross_amd import head as H
 from lm_head_cross_amd import synth
 from oracle import orpo_oracle as orc
-from tests.gpu_helpers import TOL_GRAD, dev, oracle_weight, rel, say
+from tests.gpu_helpers import TOL_GRAD, dev, mfma_operand_weight, oracle_weight, rel, say
 
 pytestmark = pytest.mark.gpu
 
@@ -107,6 +107,47 @@ def test_filter_with_4bit_weights():
     fh, _, kh, _ = orc.backward_filtered(hh, W, inp.labels, ora["lse"], ora["g"], cfg.softcap, eps)
     e = rel(dh, fh)
     say(f"[filter q4] kept dh {kh:.3f} vs filtered dh={e:.2e}")
+    assert e <= TOL_GRAD
+
+
+def test_q4_filter_running_max_odd_k_steps():
+    # The 4-bit head with the filter and the cold-tile skip under a softcap of 50 (the forward's
+    # running maximum with per-tile maxima) and d = 192 (three K steps, padded to four with zeros):
+    # the forward at parity with the oracle on the MFMA's operands, the backward equal to the
+    # filter-only result bit for bit and to the oracle's filtered backward within the gate.
+    cfg = synth.HeadConfig(0, "peaked-q4-cap50-d192", M=512, d=192, V=4096, pairs=1, len_lo=200,
+                           len_hi=256, softcap=50.0, lam=0.1, q4=True, w_std=12.0, p_argmax=0.95)
+    inp = synth.make_inputs(cfg, 0, label_device="cuda")
+    d = dev()
+    hh = inp.h.float().numpy().astype(np.float64)
+    Wop = mfma_operand_weight(inp)
+    h, lab = inp.h.to(d), torch.from_numpy(inp.labels).to(d)
+    w = torch.from_numpy(inp.wq.view(np.int32)).to(d)
+    sc, bi = inp.scales.to(d), inp.biases.to(d)
+    eps = 1e-5
+    logp, lse, fws = H.head_fwd(h, w, lab, cfg.softcap, scales=sc, biases=bi, return_ws=True,
+                                skip_eps=eps)
+    torch.cuda.synchronize()
+    assert H.read_status(fws) == 0
+    lp_o, lse_o = orc.forward(hh, Wop, inp.labels, cfg.softcap)
+    ok = inp.labels != -100
+    e_lp = float(np.max(np.abs(logp.cpu().numpy()[ok] - lp_o[ok]) / (np.abs(lp_o[ok]) + 1.0)))
+    e_lse = float(np.max(np.abs(lse.cpu().numpy() - lse_o) / (np.abs(lse_o) + 1.0)))
+    say(f"[q4 cap50 d192] forward logp {e_lp:.2e} lse {e_lse:.2e}")
+    assert e_lp <= 1e-4 and e_lse <= 1e-4
+    g = np.random.default_rng(5).standard_normal(cfg.M) * 1e-2
+    g[~ok] = 0
+    gg = torch.from_numpy(g.astype(np.float32)).to(d)
+    dh0, _ = H.head_bwd(h, w, lab, lse, gg, cfg.softcap, want_dW=False, scales=sc, biases=bi,
+                        skip_eps=eps)
+    dh1, _ = H.head_bwd(h, w, lab, lse, gg, cfg.softcap, want_dW=False, scales=sc, biases=bi,
+                        skip_eps=eps, fwd_ws=fws)
+    torch.cuda.synchronize()
+    assert torch.equal(dh0, dh1)
+    fh, _, kh, _ = orc.backward_filtered(hh, Wop, inp.labels, lse.cpu().numpy().astype(np.float64),
+                                         g, cfg.softcap, eps)
+    e = rel(dh0.cpu().numpy(), fh)
+    say(f"[q4 cap50 d192] kept dh {kh:.3f}; vs filtered dh={e:.2e}")
     assert e <= TOL_GRAD
 
 
