@@ -364,6 +364,7 @@ struct Q4K2 {
   // them before the commit, so no ALU op waits on these loads where they are issued.
   uint16_t sbits[2], bbits[2];
   bool ok[2];
+  static constexpr int kLoads = 3;   // vector-memory loads per issue: the words, scale, bias
   __device__ __forceinline__ void init(const Q4Weight& w) { W = w; }
   // live = false stages zeros (the words are still read, from row0's group at k0, in bounds).
   template <int S>
@@ -807,44 +808,46 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
 // The 4-bit head's K-major loop (forward and coefficient tiles, A = the 4-bit weights, B dense).
 // The two-stage schedule of gemm_step with the A operand one step further ahead: at step s's
 // barrier the words of step s + 3 are loaded (register set (s + 1) % 2) and B's direct loads of
-// step s + 2 issued; during step s's first three K groups the words of step s + 1 (loaded at step
-// s - 2's barrier, complete since step s - 1's) are dequantised into step s + 1's stage, their
-// VALU work and LDS writes pinned between the MFMAs, where the dequantisation used to run alone
-// before the barrier.
+// step s + 2 issued. The words of a step t (loaded at step t - 3's barrier, complete since step
+// t - 2's) are dequantised one word (8 codes a thread) per K group over the last group of step
+// t - 2 (after its barrier, when step t - 2's stage, which is step t's, is no longer read) and the
+// first three of step t - 1, their VALU work and LDS writes pinned between the MFMAs.
 //   issue_a(set, tile, ks): load the words of step (tile, ks) into set `set` (integral_constant)
 //   commit_a(set, stageA, w0, w1): dequantise words [w0, w1) of set `set` into stageA
 //   issue_b(tile, ks, stageB): B's direct loads of step (tile, ks)
 // With an odd number nk of K steps a tile runs nk + 1, the last (ks == nk) staging zeros in both
 // operands, so that the steps come in pairs; issue_a and issue_b see ks == nk there.
 // ------------------------------------------------------------------------------------------
-// One K group of region 1 in a 4-bit step: per MFMA its share of the next group's fragment
-// reads and of the VALU work of `kWords` dequantised words, each word's LDS write after its
-// share. Each group is its own scheduling region (sched_barrier(0) after it), so that the
-// dequantisation cannot gather in one block.
-template <class E, int kWords>
+// One K group of a 4-bit step: per MFMA its share of the next group's fragment reads, of kLoads
+// vector-memory loads (the post-barrier group: the next steps' loads) and of the VALU work of one
+// dequantised word, whose LDS write follows the last MFMA. Each group is its own scheduling
+// region (sched_barrier(0) after it), so that the dequantisation cannot gather in one block.
+template <class E, int kLoads>
 __device__ __forceinline__ void sched_group_dequant() {
   constexpr int kReads = 4 * reads_per_frag<E, true>() + 2 * reads_per_frag<E, true>();
   constexpr int kMfma = 8 * mfma_per_mma<E>();
   constexpr int kSpan = kMfma * 3 / 4;
-  constexpr int kValu = (kWords * 30 + kMfma - 1) / kMfma;   // ~28 VALU a word + the scale
+  constexpr int kValu = (30 + kMfma - 1) / kMfma;   // ~23 VALU a word + the scale and bias
+  static_assert(kLoads <= kMfma, "one load per MFMA");
 #pragma unroll
   for (int i = 0; i < kMfma; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     const int n = i < kSpan ? (i + 1) * kReads / kSpan - i * kReads / kSpan : 0;
     if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    if (kWords > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-    if (kWords > 0 && (i + 1) % (kMfma / kWords) == 0)
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (i < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
 }
 
-template <bool kClear, class IssueA, class CommitA, class IssueB, class Epi>
+template <bool kClear, int kLoadsA, class IssueA, class CommitA, class IssueB, class Epi>
 __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk, IssueA&& issue_a,
                                              CommitA&& commit_a, IssueB&& issue_b, Epi&& epi,
                                              f32x16 (&acc)[4][2]) {
   typedef EBf16 E;
   constexpr int kG = E::kGroups;
+  static_assert(kG == 4, "the dequantisation of a step is split over four K groups");
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
   // An odd nk gets one more K step per tile that stages zeros (see above), for an even total.
@@ -854,6 +857,11 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
   const typename E::Scales sc{};
   const std::integral_constant<int, 0> set0{};
   const std::integral_constant<int, 1> set1{};
+  typedef std::integral_constant<int, 0> W0;
+  typedef std::integral_constant<int, 1> W1;
+  typedef std::integral_constant<int, 2> W2;
+  typedef std::integral_constant<int, 3> W3;
+  typedef std::integral_constant<int, 4> W4;
   StepPos cur{0, 0}, pa{0, 0}, pb{0, 0};
   issue_b(pb.tile, pb.ks, sm.b0);
   pb.next(nkp);
@@ -861,9 +869,10 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
   pa.next(nkp);
   issue_a(set1, pa.tile, pa.ks);   // step 1
   pa.next(nkp);
-  commit_a(set0, sm.a0, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+  commit_a(set0, sm.a0, W0{}, W4{});
   issue_a(set0, pa.tile, pa.ks);   // step 2
   pa.next(nkp);
+  commit_a(set1, sm.a1, W0{}, W1{});   // step 1's first word; step 0 commits the rest
   issue_b(pb.tile, pb.ks, sm.b1);  // step 1
   pb.next(nkp);
   vm_wait_seen();
@@ -873,33 +882,32 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
   auto step = [&](auto parity, int s, char* __restrict__ ca, char* __restrict__ cb,
                   char* __restrict__ na, char* __restrict__ nb) {
     const std::integral_constant<int, 1 - decltype(parity)::value> next_set{};
-    // Step s + 1's words into its stage (unused past the end): words 0, 1 and 2-3 with groups
-    // 0, 1 and 2.
-    static_assert(kG == 4, "the dequantisation is split over three K groups");
-    auto group = [&](auto kg_c, auto w0_c, auto w1_c) {
+    // Groups 0-2: words 1, 2 and 3 of step s + 1 (set s + 1) into its stage.
+    auto group = [&](auto kg_c, auto w0_c) {
       constexpr int kg = decltype(kg_c)::value;
       load_frags<E, true, true>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
       mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
-      commit_a(next_set, na, w0_c, w1_c);
-      sched_group_dequant<E, decltype(w1_c)::value - decltype(w0_c)::value>();
+      commit_a(next_set, na, w0_c, std::integral_constant<int, decltype(w0_c)::value + 1>{});
+      sched_group_dequant<E, 0>();
       __builtin_amdgcn_sched_barrier(0);
     };
-    group(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
-          std::integral_constant<int, 1>{});
-    group(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{},
-          std::integral_constant<int, 2>{});
-    group(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{},
-          std::integral_constant<int, 4>{});
+    group(W0{}, W1{});
+    group(W1{}, W2{});
+    group(W2{}, W3{});
     const bool ends_tile = cur.ks == nkp - 1;
     vm_wait_seen();
     __syncthreads();
-    issue_b(pb.tile, pb.ks, cb);  // step s + 2
+    // Group 3, after the barrier (step s's stage is free): step s + 2's B loads and its first
+    // word (set s, complete since the barrier) into step s's stage, and step s + 3's words into
+    // the set committed above, with the next step's first fragment reads.
+    issue_b(pb.tile, pb.ks, cb);
     pb.next(nkp);
-    issue_a(next_set, pa.tile, pa.ks);   // step s + 3 into the set just committed
+    commit_a(parity, ca, W0{}, W1{});
+    issue_a(next_set, pa.tile, pa.ks);
     pa.next(nkp);
     load_frags<E, true, true>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
     mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
-    sched_groups_loads<E, true, true>();
+    sched_group_dequant<E, 4 + kLoadsA>();
     if (ends_tile) {
       epi(cur.tile, acc);
       if (kClear) zero_acc(acc);

@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   };
   f32x16 acc[4][2];
   zero_acc(acc);
-  if constexpr (Q4) gemm_run_q4k<true>(smem, n_tiles, nk, issue_a, commit_a, issue_b, epi, acc);
+  if constexpr (Q4)
+    gemm_run_q4k<true, Q4K2::kLoads>(smem, n_tiles, nk, issue_a, commit_a, issue_b, epi, acc);
   else gemm_run_scaled<E, true, true, true, true>(smem, n_tiles, nk, issue, commit, epi, scales, acc);
 
   // Combine the lane pair (l, l ^ 32), then the two m-waves, and write this split's partials.
@@ -441,6 +442,80 @@ __device__ __forceinline__ double log1mexp_d(double x, bool* clamped) {
   return x > -0.6931471805599453 ? log(v) : log1p(-exp(x));
 }
 
+// Span offsets valid (0 <= off[0], off[i] <= off[i+1], off[n] <= M)? Checked by every thread of
+// the workgroup on a strided share of the offsets. Thread 0 then resets the status word (or sets
+// the bad-offsets bit), before a barrier, so that it precedes every later atomicOr into it.
+__device__ __forceinline__ bool check_offsets(const int32_t* off, int n, int64_t M, uint32_t* status) {
+  int b = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) b |= off[i + 1] < off[i];
+  if (threadIdx.x == 0) b |= off[0] < 0 || (int64_t)off[n] > M;
+  b = __syncthreads_or(b);
+  if (threadIdx.x == 0) *status = b ? kStatusBadOffsets : 0u;
+  __syncthreads();
+  return b != 0;
+}
+
+// Sum of logp over the valid tokens of span s and their count, one wave per span (fixed order:
+// each lane's tokens in order, then a fixed butterfly). Both loads are unconditional (in bounds)
+// and the loop unrolled, so that several are in flight; an invalid token adds +0.0, which changes
+// no sum.
+__device__ __forceinline__ void span_sum(const int32_t* off, int s, const float* logp,
+                                         const int32_t* labels, int32_t ignore, int64_t V,
+                                         double* sum_out, long long* n_out) {
+  const int l = threadIdx.x & 63;
+  double sum = 0.0;
+  long long n = 0;
+  const int64_t end = off[s + 1];
+#pragma unroll 4
+  for (int64_t t = off[s] + l; t < end; t += 64) {
+    const int y = labels[t];
+    const float lp = logp[t];
+    const bool ok = y != ignore && y >= 0 && (int64_t)y < V;
+    sum += ok ? (double)lp : 0.0;
+    n += ok ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o);
+    n += __shfl_xor(n, o);
+  }
+  *sum_out = sum;
+  *n_out = n;
+}
+
+// A fixed-order sum of n terms by one wave: lane l adds terms l, l + 64, ... in order, then a
+// butterfly, after which every lane holds the same total (lanes l and l ^ o add the same two
+// values at each level). Deterministic, and its loads are all in flight at once, unlike one
+// thread's sequential loop.
+template <class T, class F>
+__device__ __forceinline__ T wave_sum(int n, F&& term) {
+  const int l = threadIdx.x & 63;
+  T s = T(0);
+  for (int i = l; i < n; i += 64) s += term(i);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
+// The per-token cotangent g[0, M), span by span in the waves' order of the sums (wave w takes
+// spans w, w + 16, ...): per_span(s) gives span s's token function (its span constants read once),
+// applied to each valid token of the span; invalid tokens and tokens outside every span get 0.
+template <class PerSpan>
+__device__ __forceinline__ void fill_g_by_span(const int32_t* off, int ns, int64_t M,
+                                               const int32_t* labels, int32_t ignore, int64_t V,
+                                               float* g, PerSpan&& per_span) {
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  for (int s = w; s < ns; s += 16) {
+    auto tok = per_span(s);
+    for (int64_t t = off[s] + l; t < off[s + 1]; t += 64) {
+      const int y = labels[t];
+      g[t] = y != ignore && y >= 0 && (int64_t)y < V ? tok(t) : 0.f;
+    }
+  }
+  for (int64_t t = tid; t < off[0]; t += 1024) g[t] = 0.f;
+  for (int64_t t = off[ns] + tid; t < M; t += 1024) g[t] = 0.f;
+}
+
 struct LossArgs {
   int64_t M, V;
   int32_t P;
@@ -467,38 +542,19 @@ struct LossArgs {
 // odds ratio keeps the response means. A prompt span without a valid token is allowed (weight 0,
 // reported mean 0); then every result equals the S = 2 one bit for bit.
 __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
-  __shared__ int bad;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int S = a.S, ns = S * a.P, nout = 5 + (S == 3 ? 3 : 2) * a.P;
-  if (tid == 0) {
-    int b = a.off[0] < 0 || (int64_t)a.off[ns] > a.M;
-    for (int i = 0; i < ns; ++i) b |= a.off[i + 1] < a.off[i];
-    bad = b;
-    *a.status = b ? kStatusBadOffsets : 0u;
-  }
-  __syncthreads();
   const double nan = __builtin_nan("");
-  if (bad) {
+  if (check_offsets(a.off, ns, a.M, a.status)) {
     for (int i = tid; i < nout; i += 1024) a.out[i] = nan;
     for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
     return;
   }
   // Span sums: wave w takes spans w, w + 16, ...
   for (int b = w; b < ns; b += 16) {
-    double sum = 0.0;
-    long long n = 0;
-    for (int64_t t = a.off[b] + l; t < a.off[b + 1]; t += 64) {
-      const int y = a.labels[t];
-      if (y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
-        sum += (double)a.logp[t];
-        ++n;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      sum += __shfl_xor(sum, o);
-      n += __shfl_xor(n, o);
-    }
+    double sum;
+    long long n;
+    span_sum(a.off, b, a.logp, a.labels, a.ignore_index, a.V, &sum, &n);
     if (l == 0) {
       const bool prompt = S == 3 && b % 3 == 0;
       a.cnt[b] = n;
@@ -535,38 +591,28 @@ __global__ __launch_bounds__(1024) void loss_kernel(LossArgs a) {
     a.out[5 + a.P + p] = lr;
   }
   __syncthreads();
-  if (tid == 0) {
-    double nll = 0.0, orv = 0.0, acc = 0.0, mar = 0.0;
-    for (int p = 0; p < a.P; ++p) {
-      if (S == 3)
-        nll -= (a.sum[3 * p] + a.sum[3 * p + 1]) / (double)(a.cnt[3 * p] + a.cnt[3 * p + 1]);
-      else
-        nll -= a.ell[2 * p];
-      orv += a.pair[a.P + p];
-      acc += a.pair[2 * a.P + p];
-      mar += a.pair[p];
+  if (w == 0) {
+    const double nll = -wave_sum<double>(a.P, [&](int p) {
+      return S == 3 ? (a.sum[3 * p] + a.sum[3 * p + 1]) / (double)(a.cnt[3 * p] + a.cnt[3 * p + 1])
+                    : a.ell[2 * p];
+    });
+    const double orv = wave_sum<double>(a.P, [&](int p) { return a.pair[a.P + p]; });
+    const double acc = wave_sum<double>(a.P, [&](int p) { return a.pair[2 * a.P + p]; });
+    const double mar = wave_sum<double>(a.P, [&](int p) { return a.pair[p]; });
+    if (l == 0) {
+      const double P = (double)a.P;
+      a.out[0] = nll / P + a.lam * (orv / P);
+      a.out[1] = nll / P;
+      a.out[2] = orv / P;
+      a.out[3] = acc / P;
+      a.out[4] = mar / P;
     }
-    const double P = (double)a.P;
-    a.out[0] = nll / P + a.lam * (orv / P);
-    a.out[1] = nll / P;
-    a.out[2] = orv / P;
-    a.out[3] = acc / P;
-    a.out[4] = mar / P;
   }
-  // g_t = (dL/d ell_s) / n_s for a valid token of span s (binary search over the offsets).
-  for (int64_t t = tid; t < a.M; t += 1024) {
-    float gv = 0.f;
-    const int y = a.labels[t];
-    if (t >= a.off[0] && t < a.off[ns] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
-      int lo = 0, hi = ns;   // find s with off[s] <= t < off[s+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int64_t)a.off[mid] <= t) lo = mid; else hi = mid;
-      }
-      gv = (float)(a.dl[lo] / (double)a.cnt[lo]);
-    }
-    a.g[t] = gv;
-  }
+  // g_t = (dL/d ell_s) / n_s for a valid token of span s.
+  fill_g_by_span(a.off, ns, a.M, a.labels, a.ignore_index, a.V, a.g, [&](int s) {
+    const float gs = a.cnt[s] > 0 ? (float)(a.dl[s] / (double)a.cnt[s]) : 0.f;
+    return [gs](int64_t) { return gs; };
+  });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -723,7 +769,7 @@ __device__ __forceinline__ void coeff_tile(const Smem& smem, const BwdArgs& a, c
   f32x16 acc[4][2];
   zero_acc(acc);
   auto nop = [](int, f32x16(&)[4][2]) {};
-  if constexpr (Q4) gemm_run_q4k<false>(smem, 1, nk, issue_a, commit_a, issue_b, nop, acc);
+  if constexpr (Q4) gemm_run_q4k<false, Q4K2::kLoads>(smem, 1, nk, issue_a, commit_a, issue_b, nop, acc);
   else gemm_run_scaled<EL, true, true, false, true>(smem, 1, nk, issue, commit, nop, scales, acc);
 
   typedef typename E::T T;

@@ -16,52 +16,6 @@ __device__ __forceinline__ double sigmoid_d(double x) {
   return x >= 0 ? 1.0 / (1.0 + exp(-x)) : exp(x) / (1.0 + exp(x));
 }
 
-// Checks that off[0..n] is monotone within [0, M]; sets the status word; true when it is not.
-__device__ __forceinline__ bool check_offsets(const int32_t* off, int n, int64_t M, uint32_t* status,
-                                              int* bad) {
-  if (threadIdx.x == 0) {
-    int b = off[0] < 0 || (int64_t)off[n] > M;
-    for (int i = 0; i < n; ++i) b |= off[i + 1] < off[i];
-    *bad = b;
-    *status = b ? kStatusBadOffsets : 0u;
-  }
-  __syncthreads();
-  return *bad != 0;
-}
-
-// Sum of logp over the valid tokens of span s and their count, one wave per span (fixed order).
-__device__ __forceinline__ void span_sum(const int32_t* off, int s, const float* logp,
-                                         const int32_t* labels, int32_t ignore, int64_t V,
-                                         double* sum_out, long long* n_out) {
-  const int l = threadIdx.x & 63;
-  double sum = 0.0;
-  long long n = 0;
-  for (int64_t t = off[s] + l; t < off[s + 1]; t += 64) {
-    const int y = labels[t];
-    if (y != ignore && y >= 0 && (int64_t)y < V) {
-      sum += (double)logp[t];
-      ++n;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    sum += __shfl_xor(sum, o);
-    n += __shfl_xor(n, o);
-  }
-  *sum_out = sum;
-  *n_out = n;
-}
-
-// Span index of token t (off[s] <= t < off[s+1]) by binary search over off[0..n].
-__device__ __forceinline__ int span_of(const int32_t* off, int n, int64_t t) {
-  int lo = 0, hi = n;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)off[mid] <= t) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 struct PrefArgs {
   int32_t kind;           // kPref*
   int64_t M, V;
@@ -90,10 +44,9 @@ struct PrefArgs {
 // gradient at the kink). loss = mean over pairs; g_t = dL/dvalue_s / n_s (means) or dL/dvalue_s
 // (sums) for a valid token of span s.
 __global__ __launch_bounds__(1024) void pref_loss_kernel(PrefArgs a) {
-  __shared__ int bad;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, ns = 2 * a.P;
   const double nan = __builtin_nan("");
-  if (check_offsets(a.off, ns, a.M, a.status, &bad)) {
+  if (check_offsets(a.off, ns, a.M, a.status)) {
     for (int i = tid; i < 3 + ns; i += 1024) a.out[i] = nan;
     for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
     return;
@@ -148,26 +101,21 @@ __global__ __launch_bounds__(1024) void pref_loss_kernel(PrefArgs a) {
     a.out[3 + a.P + p] = vr;
   }
   __syncthreads();
-  if (tid == 0) {
-    double lo = 0.0, ac = 0.0, mg = 0.0;
-    for (int p = 0; p < a.P; ++p) {
-      lo += a.pair[p];
-      ac += a.pair[a.P + p];
-      mg += a.pair[2 * a.P + p];
+  if (w == 0) {
+    const double lo = wave_sum<double>(a.P, [&](int p) { return a.pair[p]; });
+    const double ac = wave_sum<double>(a.P, [&](int p) { return a.pair[a.P + p]; });
+    const double mg = wave_sum<double>(a.P, [&](int p) { return a.pair[2 * a.P + p]; });
+    if (l == 0) {
+      a.out[0] = lo / (double)a.P;
+      a.out[1] = ac / (double)a.P;
+      a.out[2] = mg / (double)a.P;
     }
-    a.out[0] = lo / (double)a.P;
-    a.out[1] = ac / (double)a.P;
-    a.out[2] = mg / (double)a.P;
   }
-  for (int64_t t = tid; t < a.M; t += 1024) {
-    float gv = 0.f;
-    const int y = a.labels[t];
-    if (t >= a.off[0] && t < a.off[ns] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
-      const int s = span_of(a.off, ns, t);
-      gv = (float)(pref_mean(a.kind) ? a.dv[s] / (double)a.cnt[s] : a.dv[s]);
-    }
-    a.g[t] = gv;
-  }
+  fill_g_by_span(a.off, ns, a.M, a.labels, a.ignore_index, a.V, a.g, [&](int s) {
+    const float gs = a.cnt[s] > 0 ? (float)(pref_mean(a.kind) ? a.dv[s] / (double)a.cnt[s] : a.dv[s])
+                                  : 0.f;
+    return [gs](int64_t) { return gs; };
+  });
 }
 
 struct GrpoArgs {
@@ -214,10 +162,9 @@ __device__ __forceinline__ GrpoToken grpo_token(double lp, double old, double re
 // loss = mean over completions of (mean over the completion's valid tokens of pg + beta k3);
 // g_t = (dpg + beta dk3) / (n_s S).
 __global__ __launch_bounds__(1024) void grpo_loss_kernel(GrpoArgs a) {
-  __shared__ int bad;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const double nan = __builtin_nan("");
-  if (check_offsets(a.off, a.S, a.M, a.status, &bad)) {
+  if (check_offsets(a.off, a.S, a.M, a.status)) {
     for (int i = tid; i < 4; i += 1024) a.out[i] = nan;
     for (int64_t t = tid; t < a.M; t += 1024) a.g[t] = nan;
     return;
@@ -252,32 +199,25 @@ __global__ __launch_bounds__(1024) void grpo_loss_kernel(GrpoArgs a) {
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    double pg = 0.0, kl = 0.0;
-    long long n = 0, c = 0;
-    for (int s = 0; s < a.S; ++s) {
-      pg += a.pg[s];
-      kl += a.kl[s];
-      n += a.cnt[s];
-      c += a.clipped[s];
+  if (w == 0) {
+    const double pg = wave_sum<double>(a.S, [&](int s) { return a.pg[s]; }) / (double)a.S;
+    const double kl = wave_sum<double>(a.S, [&](int s) { return a.kl[s]; }) / (double)a.S;
+    const long long n = wave_sum<long long>(a.S, [&](int s) { return (long long)a.cnt[s]; });
+    const long long c = wave_sum<long long>(a.S, [&](int s) { return (long long)a.clipped[s]; });
+    if (l == 0) {
+      a.out[0] = pg + a.beta * kl;
+      a.out[1] = pg;
+      a.out[2] = kl;
+      a.out[3] = n ? (double)c / (double)n : nan;
     }
-    pg /= (double)a.S;
-    kl /= (double)a.S;
-    a.out[0] = pg + a.beta * kl;
-    a.out[1] = pg;
-    a.out[2] = kl;
-    a.out[3] = n ? (double)c / (double)n : nan;
   }
-  for (int64_t t = tid; t < a.M; t += 1024) {
-    float gv = 0.f;
-    const int y = a.labels[t];
-    if (t >= a.off[0] && t < a.off[a.S] && y != a.ignore_index && y >= 0 && (int64_t)y < a.V) {
-      const int s = span_of(a.off, a.S, t);
-      const GrpoToken r = grpo_token(a.logp[t], a.old_logp[t], a.ref_logp[t], (double)a.adv[s], a.eps);
-      gv = (float)((r.dpg + a.beta * r.dk3) / ((double)a.cnt[s] * (double)a.S));
-    }
-    a.g[t] = gv;
-  }
+  fill_g_by_span(a.off, a.S, a.M, a.labels, a.ignore_index, a.V, a.g, [&](int s) {
+    const double adv = (double)a.adv[s], den = (double)a.cnt[s] * (double)a.S;
+    return [&a, adv, den](int64_t t) {
+      const GrpoToken r = grpo_token(a.logp[t], a.old_logp[t], a.ref_logp[t], adv, a.eps);
+      return (float)((r.dpg + a.beta * r.dk3) / den);
+    };
+  });
 }
 
 }  // namespace orpo
