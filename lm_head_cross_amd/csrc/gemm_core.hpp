@@ -426,6 +426,43 @@ struct Q4N {
   }
 };
 
+// 4-bit weights as an N-major operand with two register sets (gemm_run_q4n): same layout per
+// thread as Q4N; the words of a step are loaded two steps ahead into set S and dequantised into
+// LDS during the step before their use, interleaved with its MFMAs. live = false stages zeros.
+struct Q4N2 {
+  Q4Weight W;
+  int64_t v_end;             // rows >= v_end read as zero
+  u32x4 q[2];
+  uint16_t sbits[2], bbits[2];   // bf16 bits of the group's scale and bias, separate registers
+  bool ok[2];
+  static constexpr int kLoads = 3;   // vector-memory loads per issue: the words, scale, bias
+  __device__ __forceinline__ void init(const Q4Weight& w, int64_t vend) { W = w; v_end = vend; }
+  template <int S>
+  __device__ __forceinline__ void issue(int64_t k0, int64_t n0, bool live) {
+    const int tid = threadIdx.x;
+    const int64_t gr = k0 + (tid >> 3);
+    const int64_t gc = n0 + (tid & 7) * 32;
+    const bool in = live && gr < v_end && gc < W.d;
+    const int64_t r = in ? gr : 0, c = in ? gc : 0;
+    q[S] = *(const u32x4*)(W.wq + r * (W.d >> 3) + (c >> 3));
+    const int64_t gi = r * (W.d >> 6) + (c >> 6);
+    sbits[S] = W.scales[gi];
+    bbits[S] = W.biases[gi];
+    ok[S] = in;
+  }
+  // Words [W0, W1) of set S (8 codes each) into the stage, one 16-byte LDS write per word.
+  template <int S, int W0, int W1>
+  __device__ __forceinline__ void commit_words(char* stage) const {
+    const int tid = threadIdx.x, r = tid >> 3;
+    const float scale = ok[S] ? bf16_bits_to_f32(sbits[S]) : 0.f;
+    const float bias = ok[S] ? bf16_bits_to_f32(bbits[S]) : 0.f;
+    char* row = stage + r * (EBf16::kMnChunks * 16);
+#pragma unroll
+    for (int w = W0; w < W1; ++w)
+      *(u32x4*)(row + (((tid & 7) * 4 + w) ^ swz_mn16(r)) * 16) = dequant_word(q[S][w], scale, bias);
+  }
+};
+
 // ------------------------------------------------------------------------------------------
 // Compute one LDS stage into the wave's 4 x 2 accumulator blocks.
 // ------------------------------------------------------------------------------------------
@@ -822,9 +859,9 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
 // vector-memory loads (the post-barrier group: the next steps' loads) and of the VALU work of one
 // dequantised word, whose LDS write follows the last MFMA. Each group is its own scheduling
 // region (sched_barrier(0) after it), so that the dequantisation cannot gather in one block.
-template <class E, int kLoads>
+template <class E, int kLoads, bool AK = true, bool BK = true, bool kNextReads = true>
 __device__ __forceinline__ void sched_group_dequant() {
-  constexpr int kReads = 4 * reads_per_frag<E, true>() + 2 * reads_per_frag<E, true>();
+  constexpr int kReads = kNextReads ? 4 * reads_per_frag<E, AK>() + 2 * reads_per_frag<E, BK>() : 0;
   constexpr int kMfma = 8 * mfma_per_mma<E>();
   constexpr int kSpan = kMfma * 3 / 4;
   constexpr int kValu = (30 + kMfma - 1) / kMfma;   // ~23 VALU a word + the scale and bias
@@ -921,6 +958,72 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
     step(set1, it + 1, sm.a1, sm.b1, sm.a0, sm.b0);
   }
   vm_wait_seen();   // the loads past the last step
+}
+
+// ------------------------------------------------------------------------------------------
+// The 4-bit head's dh loop: one tile, A (coefficients) K-major by direct loads, B the 4-bit weights
+// N-major (transposing fragment reads, so the barrier sits at the end of each step, as in
+// gemm_step_end). Step s issues A's loads of step s + 1 and the words of step s + 2 (into register
+// set s % 2, dequantised during step s - 1), then runs its four K groups, dequantising the words of
+// step s + 1 (set (s + 1) % 2, complete since the previous barrier) one word per group between the
+// MFMAs into step s + 1's stage, which no wave reads after that barrier.
+//   issue_a(ks, stageA): A's direct loads of step ks;  issue_b(set, ks): the words of step ks;
+//   commit_b(set, stageB, w0, w1): dequantise words [w0, w1) of `set` into stageB.
+// An odd step count gets one more step that stages zeros (both operands; issue_a and issue_b see
+// ks == nk there), so that steps come in pairs.
+// ------------------------------------------------------------------------------------------
+template <int kLoadsB, class IssueA, class IssueB, class CommitB>
+__device__ __forceinline__ void gemm_run_q4n(const Smem& sm, int nk, IssueA&& issue_a,
+                                             IssueB&& issue_b, CommitB&& commit_b,
+                                             f32x16 (&acc)[4][2]) {
+  typedef EBf16 E;
+  constexpr int kG = E::kGroups;
+  static_assert(kG == 4, "the dequantisation of a step is split over four K groups");
+  constexpr int kLoadsA = 4;   // DmaKS issues four direct loads per thread
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  const int wm = w >> 2, wn = w & 3;
+  const int total = nk + (nk & 1);
+  if (total <= 0) return;
+  const typename E::Scales sc{};
+  const std::integral_constant<int, 0> set0{};
+  const std::integral_constant<int, 1> set1{};
+  typedef std::integral_constant<int, 0> W0;
+  typedef std::integral_constant<int, 4> W4;
+  issue_a(0, sm.a0);
+  issue_b(set0, 0);
+  issue_b(set1, 1);
+  commit_b(set0, sm.b0, W0{}, W4{});
+  vm_wait_seen();
+  __syncthreads();
+  auto step = [&](auto parity, int s, char* __restrict__ ca, char* __restrict__ cb,
+                  char* __restrict__ na, char* __restrict__ nb) {
+    const std::integral_constant<int, 1 - decltype(parity)::value> next_set{};
+    issue_a(s + 1, na);
+    issue_b(parity, s + 2);          // the set committed during the previous step
+    FragSets<E> f;
+    load_frags<E, true, false>(ca, cb, 0, wm, wn, l, f.a[0], f.b[0]);
+    auto group = [&](auto kg_c) {
+      constexpr int kg = decltype(kg_c)::value;
+      if constexpr (kg + 1 < kG)
+        load_frags<E, true, false>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
+      mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
+      commit_b(next_set, nb, kg_c, std::integral_constant<int, kg + 1>{});
+      sched_group_dequant<E, kg == 0 ? kLoadsA + kLoadsB : 0, true, false, (kg + 1 < kG)>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    group(std::integral_constant<int, 0>{});
+    group(std::integral_constant<int, 1>{});
+    group(std::integral_constant<int, 2>{});
+    group(std::integral_constant<int, 3>{});
+    vm_wait_seen();
+    __syncthreads();
+  };
+  // Steps in pairs: no path from the first step's loads back to the loop header.
+  for (int it = 0; it < total; it += 2) {
+    step(set0, it, sm.a0, sm.b0, sm.a1, sm.b1);
+    step(set1, it + 1, sm.a1, sm.b1, sm.a0, sm.b0);
+  }
+  vm_wait_seen();
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each with

@@ -1037,28 +1037,45 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   const int64_t v_end = min(a.V, it.v0 + it.BV_cur);
   DmaK la;                                                          // coeff [i][v], K-major
   la.init(it.coeff, cpitch, it.C_cur);
-  typedef typename std::conditional<Q4, Q4N, DmaMN<E>>::type LoaderB;
+  typedef typename std::conditional<Q4, Q4N2, DmaMN<E>>::type LoaderB;
   LoaderB lb;                                                       // W [v][j], N-major
   if constexpr (Q4) lb.init(a.q4, v_end);
   else lb.init((const char*)a.w + it.v0 * row_bytes, row_bytes, v_end - it.v0);   // block rows
   // Coefficient filter: run only the vocabulary slices some coefficient of this token tile needs.
   constexpr bool filt = SKIP;
   const int n_run = filt ? build_klist(it.fdh + (int64_t)ti * a.nsl_v * 4, nk, 4, klist, wave_tot) : nk;
-  auto issue = [&](int, int ks, char* sa, char* sb) {
-    const int step = filt ? __builtin_amdgcn_readfirstlane(klist[ks]) : ks;
-    const int64_t k0 = (int64_t)step * E::kBK;
-    la.issue(i0, k0 * E::kSize, sa);
-    if constexpr (Q4) lb.issue(it.v0 + k0, j0, sb);
-    else lb.issue(k0, j0 * E::kSize, sb);
-  };
-  auto commit = [&](char* sa, char* sb) {
-    la.commit(sa);
-    lb.commit(sb);
+  // The vocabulary step of run position ks (positions past n_run: the last one, in bounds).
+  auto step_of = [&](int ks) {
+    return filt ? __builtin_amdgcn_readfirstlane(klist[min(ks, n_run - 1)]) : min(ks, nk - 1);
   };
   f32x16 acc[4][2];
   zero_acc(acc);
-  auto nop = [](int, f32x16(&)[4][2]) {};
-  gemm_run<E, true, false, false, !Q4 && !SKIP>(smem, 1, n_run, issue, commit, nop, acc);
+  if constexpr (Q4) {
+    // gemm_run_q4n: positions ks >= n_run (its zero step and the loads past the end) stage zeros.
+    auto issue_a = [&](int ks, char* sa) {
+      const bool live = ks < n_run;
+      la.issue(live ? i0 : it.C_cur, live ? (int64_t)step_of(ks) * E::kBK * E::kSize : 0, sa);
+    };
+    auto issue_b = [&](auto set, int ks) {
+      lb.template issue<decltype(set)::value>(it.v0 + (int64_t)step_of(ks) * E::kBK, j0, ks < n_run);
+    };
+    auto commit_b = [&](auto set, char* sb, auto w0, auto w1) {
+      lb.template commit_words<decltype(set)::value, decltype(w0)::value, decltype(w1)::value>(sb);
+    };
+    gemm_run_q4n<Q4N2::kLoads>(smem, n_run, issue_a, issue_b, commit_b, acc);
+  } else {
+    auto issue = [&](int, int ks, char* sa, char* sb) {
+      const int64_t k0 = (int64_t)(filt ? __builtin_amdgcn_readfirstlane(klist[ks]) : ks) * E::kBK;
+      la.issue(i0, k0 * E::kSize, sa);
+      lb.issue(k0, j0 * E::kSize, sb);
+    };
+    auto commit = [&](char* sa, char* sb) {
+      la.commit(sa);
+      lb.commit(sb);
+    };
+    auto nop = [](int, f32x16(&)[4][2]) {};
+    gemm_run<E, true, false, false, !SKIP>(smem, 1, n_run, issue, commit, nop, acc);
+  }
   (void)tid;
   if (!a.dh16) {
     if (n_run > 0 || it.dh_first)
