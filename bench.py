@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--fp8", action="store_true",
                     help="the FP8 head (row-wise E4M3 logit operands; an approximation, reported "
                          "with its distance from the exact head)")
+    ap.add_argument("--no-dw", action="store_true",
+                    help="frozen head: the backward computes dh only (no dW), as for the 4-bit head")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--mfma-peak", nargs="?", const="both", default=None,
@@ -79,21 +81,21 @@ def _objective_inputs(objective: str, cfg, off: np.ndarray, n_valid_per_span: np
     return {}
 
 
-def cpu_baseline(inp, rows: int, objective: str):
+def cpu_baseline(inp, rows: int, objective: str, want_dw: bool):
     """The float64 oracle as it stands, on a bounded sample of the same batch, on the host cores
     this process may run on (BLAS threads pinned to that count)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
     n_cores = len(os.sched_getaffinity(0))
     with threadpool_limits(limits=n_cores):
-        res = _cpu_baseline(inp, rows, objective)
+        res = _cpu_baseline(inp, rows, objective, want_dw)
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     res["cores"] = int(min(threads, n_cores))
     res["affinity_cores"] = n_cores
     return res
 
 
-def _cpu_baseline(inp, rows: int, objective: str):
+def _cpu_baseline(inp, rows: int, objective: str, want_dw: bool):
     import numpy as np
     from oracle import objectives as ob
     from oracle import orpo_oracle as orc
@@ -112,10 +114,10 @@ def _cpu_baseline(inp, rows: int, objective: str):
     t0 = time.perf_counter()
     if objective == "orpo" and cfg.scope == "full":     # prompt, chosen, rejected thirds
         off = np.array([0, rows // 3, 2 * rows // 3, rows], dtype=np.int32)
-        out = orc.head_step_full(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
+        out = orc.head_step_full(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=want_dw)
     elif objective == "orpo":
         off = np.array([0, rows // 2, rows], dtype=np.int32)
-        out = orc.head_step(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=not cfg.q4)
+        out = orc.head_step(h, W, labels, off, cfg.softcap, cfg.lam, want_dW=want_dw)
     else:
         off = np.array([0, rows // 2, rows], dtype=np.int32)
         logp, lse = orc.forward(h, W, labels, cfg.softcap)
@@ -136,14 +138,14 @@ def _cpu_baseline(inp, rows: int, objective: str):
         else:
             ep = ob.grpo_loss(logp, logp - 0.1, logp + 0.1, labels, off, np.array([1.0, -1.0]), 0.2, 0.04)
             g = ep["g"]
-        orc.backward(h, W, labels, lse, g, cfg.softcap, want_dW=not cfg.q4)
+        orc.backward(h, W, labels, lse, g, cfg.softcap, want_dW=want_dw)
         out = ep
     dt = time.perf_counter() - t0
     assert math.isfinite(out["loss"])
     return {
         "value": rows / dt, "unit": "tokens/s", "kind": "oracle",
         "sample": f"first {rows} tokens of the same batch (full V={cfg.V}, d={cfg.d}), float64 "
-                  f"forward + {objective} loss + backward{' + dW' if not cfg.q4 else ''}; {dt:.1f} s",
+                  f"forward + {objective} loss + backward{' + dW' if want_dw else ''}; {dt:.1f} s",
     }
 
 
@@ -248,8 +250,9 @@ def main():
     if args.fp8 and (cfg.q4 or cfg.dtype != "bf16"):
         print("--fp8 approximates a bf16 head: pick a bf16 workload", file=sys.stderr)
         sys.exit(2)
+    want_dw = not cfg.q4 and not args.no_dw      # the 4-bit head is frozen: dh only
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                      want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj,
+                      want_dW=want_dw, scope=cfg.scope, objective=args.objective, obj=obj,
                       skip_eps=args.skip_eps, fp8=args.fp8)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -291,12 +294,14 @@ def main():
     tok_s = n_valid / (ms / 1e3)
     peak_flops = PEAK_F32 if cfg.dtype == "f32" else PEAK_BF16
     # Algorithmic work credited: valid tokens only (padding and ignored rows are processed, not
-    # credited), 8 V d FLOP each (fwd 2, bwd 6; 6 V d for the dh-only 4-bit head).
-    work = (6 if cfg.q4 else 8) * n_valid * cfg.V * cfg.d
+    # credited), 8 V d FLOP each (fwd 2, bwd 6; 6 V d for a dh-only backward: the 4-bit head, or
+    # --no-dw).
+    work = (8 if want_dw else 6) * n_valid * cfg.V * cfg.d
     if args.fp8:
-        # The logit GEMMs (forward 2 V d, recompute 2 V d) run at the fp8 rate, dh and dW (4 V d) at
-        # the bf16 rate: the step's peak is the harmonic mix.
-        peak_flops = 8.0 / (4.0 / PEAK_FP8 + 4.0 / PEAK_BF16)
+        # The logit GEMMs (forward 2 V d, recompute 2 V d) run at the fp8 rate, dh and dW (4 V d;
+        # dh alone 2 V d) at the bf16 rate: the step's peak is the harmonic mix.
+        g_flop = 4.0 if want_dw else 2.0
+        peak_flops = (4.0 + g_flop) / (4.0 / PEAK_FP8 + g_flop / PEAK_BF16)
     mfma_frac = work / (ms / 1e3) / peak_flops
 
     # Dominant kernel: the kind with the most traced time; achieved = its algorithmic FLOPs per
@@ -327,7 +332,7 @@ def main():
     fidelity = None
     if args.skip_eps > 0:
         ex = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                        want_dW=not cfg.q4, scope=cfg.scope, objective=args.objective, obj=obj)
+                        want_dW=want_dw, scope=cfg.scope, objective=args.objective, obj=obj)
         ex.step()
         torch.cuda.synchronize()
         rel = lambda a, b: float(torch.linalg.norm(a - b) / torch.linalg.norm(b))
@@ -339,7 +344,7 @@ def main():
     # The FP8 head: its distance from the exact head on this batch.
     fp8_fid = None
     if args.fp8:
-        ex = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, want_dW=True,
+        ex = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, want_dW=want_dw,
                         scope=cfg.scope, objective=args.objective, obj=obj)
         ex.step()
         torch.cuda.synchronize()
@@ -347,7 +352,8 @@ def main():
         m = labels != synth.IGNORE_INDEX
         fp8_fid = {"logp_rel": rel(step.logp[m], ex.logp[m]), "lse_rel": rel(step.lse, ex.lse),
                    "loss_rel": abs(float(step.out[0]) - float(ex.out[0])) / abs(float(ex.out[0])),
-                   "dh_rel": rel(step.dh, ex.dh), "dW_rel": rel(step.dW, ex.dW),
+                   "dh_rel": rel(step.dh, ex.dh),
+                   "dW_rel": None if step.dW is None else rel(step.dW, ex.dW),
                    "against": "the exact bf16 head on the same batch (HIP)"}
         del ex
 
@@ -365,7 +371,7 @@ def main():
         auto = int(4e12 / (6 * cfg.V * cfg.d)) // 128 * 128
         rows = args.cpu_rows or max(128, min(cfg.M, auto))
         print(f"[bench] oracle cpu baseline on {rows} rows", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp, rows, args.objective)
+        cpu = cpu_baseline(inp, rows, args.objective, want_dw)
 
     line = {
         "metric": "ORPO head fwd+bwd tokens/s (d=2560,V=262144); % bf16 MFMA peak; peak GB",
@@ -387,6 +393,7 @@ def main():
             "workload": cfg.name, "M": cfg.M, "valid_tokens": n_valid, "d": cfg.d, "V": cfg.V,
             "pairs": cfg.pairs, "softcap": cfg.softcap, "lambda": cfg.lam, "nll_scope": cfg.scope,
             "objective": args.objective, "skip_eps": args.skip_eps, "fp8": args.fp8,
+            "dW": want_dw,
             "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
             "parallelism": "single GPU",
         },

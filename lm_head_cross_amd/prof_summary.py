@@ -105,6 +105,20 @@ def traffic_txt(fetch_csv, write_csv, substr, commands, kind=None) -> str:
         raise SystemExit(f"kernel {substr!r} not found")
     fetch = fs * sum(f) / len(f)
     write = ws * sum(w) / len(w)
+    # Every launch kind of the head (kernel and grid size), copy-scaled, for the breakdown.
+    kinds = {}
+    for rows, counter, scale, col in ((fr, "FETCH_SIZE", fs, 0), (wr, "WRITE_SIZE", ws, 1)):
+        for r in rows:
+            if r["Counter_Name"] != counter or "orpo::" not in r["Kernel_Name"]:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("orpo::", "")
+            e = kinds.setdefault((name, int(r["Grid_Size"])), ([], []))
+            e[col].append(float(r["Counter_Value"]) * 1024 * scale)
+    table = ["", "breakdown (GB per launch, copy-scaled; kernel, grid threads, dispatches):"]
+    for (name, g), (fv, wv) in sorted(kinds.items(), key=lambda kv: -sum(kv[1][0])):
+        if fv and wv:
+            table.append(f"  {name} | {g} | {len(fv)} | fetch {sum(fv) / len(fv) / 1e9:.3f} | "
+                         f"write {sum(wv) / len(wv) / 1e9:.3f}")
     return "\n".join([
         f"kernel: {kind}",
         f"kernel_name: {substr}" + (f" (grid {grid} threads)" if grid else ""),
@@ -116,7 +130,7 @@ def traffic_txt(fetch_csv, write_csv, substr, commands, kind=None) -> str:
         f"write_bytes_per_launch: {write:.0f}",
         f"traffic_bytes_per_launch: {fetch + write:.0f}",
         f"commands: {commands}",
-    ]) + "\n"
+    ] + table) + "\n"
 
 
 def read_traffic(path: str):

@@ -34,16 +34,20 @@ def test_no_gpu_is_an_error_not_a_fallback():
 @pytest.mark.parametrize("objective,q4,full", [("orpo", False, False), ("orpo", True, False),
                                                ("orpo", False, True), ("simpo", False, False),
                                                ("dpo", False, False), ("ipo", False, False),
-                                               ("hinge", False, False), ("grpo", False, False)])
+                                               ("hinge", False, False), ("grpo", False, False),
+                                               ("orpo", None, False)])
 def test_cpu_baseline_leg(objective, q4, full):
+    # q4 None: the bf16 head with a frozen weight (bench.py --no-dw), dh only.
+    want_dw = q4 is False
+    q4 = bool(q4)
     sys.path.insert(0, ROOT)
     import bench
     cfg = synth.HeadConfig(0, "cpu-leg", M=256, d=128, V=1024, pairs=1, len_lo=100, len_hi=120,
                            softcap=30.0, lam=0.1, q4=q4, prompt_lo=20 if full else 0,
                            prompt_hi=30 if full else 0)
     inp = synth.make_inputs(cfg, seed=1)
-    out = bench.cpu_baseline(inp, 96, objective)
+    out = bench.cpu_baseline(inp, 96, objective, want_dw)
     assert out["kind"] == "oracle" and out["unit"] == "tokens/s"
     assert out["value"] > 0 and out["cores"] >= 1
     assert "first 96 tokens" in out["sample"] and objective in out["sample"]
-    assert ("+ dW" in out["sample"]) == (not q4)
+    assert ("+ dW" in out["sample"]) == want_dw
