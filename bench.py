@@ -317,10 +317,12 @@ def main():
         dom_peak = {"fwd": PEAK_FP8, "coeff": PEAK_FP8, "dhdw": PEAK_BF16,
                     "bwd": 6.0 / (2.0 / PEAK_FP8 + 4.0 / PEAK_BF16)}.get(dom, PEAK_BF16)
     traffic = None
+    # The counters were taken on the ORPO step of this workload (dh only: its own file), exact.
     tfile = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                         f"{cfg.name}_traffic.txt")
+                         f"{cfg.name}{'-dh-only' if args.no_dw else ''}_traffic.txt")
     t = prof_summary.read_traffic(tfile)
-    if t is not None and t[0] == dom and not args.fp8 and args.skip_eps == 0:
+    if (t is not None and t[0] == dom and not args.fp8 and args.skip_eps == 0
+            and args.objective == "orpo"):
         traffic = round(t[1])
     per_kernel = {k: {"launches_per_step": v[0] / n_tr, "avg_ms": v[1] / max(v[0], 1),
                       "ms_per_step": v[1] / n_tr,
