@@ -11,15 +11,17 @@
 // in two stages. Dense operands go global -> LDS directly (buffer_load_dwordx4 ... lds): each wave
 // instruction fills 1 KiB of LDS, lane l writing bytes [16 l, 16 l + 16), and the buffer
 // descriptor's range check returns zeros past the operand's last valid row, so tails need no VALU
-// work and loads need no staging registers. 4-bit weights take a register path that dequantises on
-// the way into LDS. Within a K step the fragments of K group g + 1 are read while group g's MFMAs
-// run (one read between consecutive MFMAs, pinned with sched_group_barrier); for K-major x K-major
+// work and loads need no staging registers; a step's direct loads go out one per MFMA of the group
+// after the barrier. 4-bit weights take a register path that dequantises on the way into LDS,
+// loaded steps ahead into two register sets and dequantised between the MFMAs (gemm_run_q4k,
+// gemm_run_q4n). Within a K step the fragments of K group g + 1 are read while group g's MFMAs run
+// (one read between consecutive MFMAs, pinned with sched_group_barrier); for K-major x K-major
 // stages the step's barrier sits before its last K group (gemm_step), for the others at its end
 // (gemm_step_end).
 //
 // Each operand tile keeps its global orientation in LDS, unpadded and XOR-swizzled per 16-byte
 // chunk (chunk c of row r is stored at chunk c ^ swz(r)):
-//   K-major  ([rows][k], k contiguous):   [256 rows][128 B], swz = r & 7;
+//   K-major  ([rows][k], k contiguous):   [256 rows][128 B], swz = (r >> 1) & 7 (fp8: r & 6);
 //                                          fragments via ds_read_b128.
 //   MN-major ([k][cols], cols contiguous): bf16 [64 rows][512 B], swz = 10 (r & 3);
 //                                          fragments via the transposing ds_read_b64_tr_b16.
@@ -66,9 +68,9 @@ __device__ __forceinline__ int swz_mn32(int r) { return ((r >> 2) & 1) << 3; }
 // Wait until this wave's outstanding vector-memory operations (including LDS-direct loads) are done.
 __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // The same wait as an instruction the compiler's wait insertion sees (s_waitcnt immediate on gfx9:
-// vmcnt bits [3:0] and [15:14] zero, expcnt 7 and lgkmcnt 15, i.e. not waited on): loads issued
-// before it then count as complete, so no later vmcnt wait is added for them, also where the
-// paths into a loop header would otherwise merge to vmcnt(0).
+// vmcnt bits [3:0] and [15:14] zero, expcnt 7 and lgkmcnt 15, i.e. not waited on): register loads
+// issued before it then count as complete, so the compiler adds no later wait for them (the 4-bit
+// loops read such loads' registers a step after the barrier that waited for them).
 __device__ __forceinline__ void vm_wait_seen() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {

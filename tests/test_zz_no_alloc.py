@@ -38,6 +38,28 @@ def test_noalloc_forward_matches_allocating_forward(cap):
         assert torch.equal(logp, ref_logp) and torch.equal(lse, ref_lse)
 
 
+def test_noalloc_forward_4bit_head():
+    # The 4-bit head through the same entry point, two calls in a row (the second smaller).
+    d = torch.device("cuda:0")
+    for M, dd, V in ((1100, 192, 3001), (300, 128, 1000)):
+        print(f"[case] noalloc q4 M={M} d={dd} V={V}", flush=True)
+        rng = np.random.default_rng(M)
+        h = synth.to_bf16(rng.standard_normal((M, dd))).to(d)
+        w32 = (rng.standard_normal((V, dd)) * (3.0 / np.sqrt(dd))).astype(np.float32)
+        wq, sc, bi = synth.encode_q4(w32, 64)
+        w = torch.from_numpy(wq.view(np.int32)).to(d)
+        sc, bi = sc.to(d), bi.to(d)
+        labels = rng.integers(0, V, size=M).astype(np.int32)
+        labels[::5] = -100
+        lab = torch.from_numpy(labels).to(d)
+        ref_logp, ref_lse = H.head_fwd(h, w, lab, 30.0, scales=sc, biases=bi)
+        logp = torch.full((M,), float("nan"), device=d)
+        lse = torch.full((M,), float("nan"), device=d)
+        H.head_fwd_noalloc(h, w, lab, logp, lse, 30.0, scales=sc, biases=bi)
+        torch.cuda.synchronize()
+        assert torch.equal(logp, ref_logp) and torch.equal(lse, ref_lse)
+
+
 def test_noalloc_refuses_a_call_beyond_its_array():
     # M = 2^20 tokens needs 8 MiB of partials: refused before anything is enqueued.
     L = H.lib()
