@@ -799,28 +799,28 @@ __device__ __forceinline__ void gemm_run(const Smem& sm, int n_tiles, int nk, Is
 
 // ------------------------------------------------------------------------------------------
 // The 4-bit head's K-major loop (forward and coefficient tiles, A = the 4-bit weights, B dense).
-// The two-stage schedule of gemm_step with the A operand one step further ahead: at step s's
-// barrier the words of step s + 3 are loaded (register set (s + 1) % 2) and B's direct loads of
-// step s + 2 issued. The words of a step t (loaded at step t - 3's barrier, complete since step
-// t - 2's) are dequantised one word (8 codes a thread) per K group over the last group of step
-// t - 2 (after its barrier, when step t - 2's stage, which is step t's, is no longer read) and the
-// first three of step t - 1, their VALU work and LDS writes pinned between the MFMAs.
+// The two-stage schedule of gemm_step with the A operand one step further ahead: after step s's
+// barrier B's direct loads of step s + 2 are issued, then (in a scheduling region of their own, so
+// that they come after them) the words of step s + 3 into register set (s + 1) % 2. The words of a
+// step t are dequantised during the first three K groups of step t - 1 (words 0-1, 2 and 3 of a
+// thread's four), their VALU work and LDS writes pinned between the MFMAs. The barrier waits for
+// every load but the words last issued (`vmcnt(3)`), so those stay in flight for the next step as
+// well; the dequantisation's own compiler-placed wait takes them.
 //   issue_a(set, tile, ks): load the words of step (tile, ks) into set `set` (integral_constant)
 //   commit_a(set, stageA, w0, w1): dequantise words [w0, w1) of set `set` into stageA
 //   issue_b(tile, ks, stageB): B's direct loads of step (tile, ks)
 // With an odd number nk of K steps a tile runs nk + 1, the last (ks == nk) staging zeros in both
 // operands, so that the steps come in pairs; issue_a and issue_b see ks == nk there.
 // ------------------------------------------------------------------------------------------
-// One K group of a 4-bit step: per MFMA its share of the next group's fragment reads, of kLoads
-// vector-memory loads (the post-barrier group: the next steps' loads) and of the VALU work of one
-// dequantised word, whose LDS write follows the last MFMA. Each group is its own scheduling
-// region (sched_barrier(0) after it), so that the dequantisation cannot gather in one block.
-template <class E, int kLoads, bool AK = true, bool BK = true, bool kNextReads = true>
-__device__ __forceinline__ void sched_group_dequant() {
-  constexpr int kReads = kNextReads ? 4 * reads_per_frag<E, AK>() + 2 * reads_per_frag<E, BK>() : 0;
-  constexpr int kMfma = 8 * mfma_per_mma<E>();
-  constexpr int kSpan = kMfma * 3 / 4;
-  constexpr int kValu = (30 + kMfma - 1) / kMfma;   // ~23 VALU a word + the scale and bias
+// Pins the order of one scheduling region of a 4-bit step: kMfma MFMAs, with kReads LDS reads
+// spread over the first three quarters of them, one of kLoads vector-memory loads after each of
+// the first kLoads MFMAs, kValu VALU instructions after every MFMA and kWrites LDS writes spread
+// evenly (each after its share of the VALU work). The region ends with sched_barrier(0) at the
+// caller, so that the dequantisation cannot gather in one block and loads keep their order across
+// regions.
+template <int kMfma, int kReads, int kLoads, int kValu, int kWrites>
+__device__ __forceinline__ void sched_region() {
+  constexpr int kSpan = kMfma * 3 / 4 > 0 ? kMfma * 3 / 4 : 1;
   static_assert(kLoads <= kMfma, "one load per MFMA");
 #pragma unroll
   for (int i = 0; i < kMfma; ++i) {
@@ -828,10 +828,33 @@ __device__ __forceinline__ void sched_group_dequant() {
     const int n = i < kSpan ? (i + 1) * kReads / kSpan - i * kReads / kSpan : 0;
     if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (n == 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     if (i < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    if (kValu > 0) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    if (kWrites > 0 && (i + 1) % (kMfma / kWrites) == 0)
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+}
+
+// The MFMAs of rows blocks MB0 and MB0 + 1 of one K group (half of mma_group).
+template <class E, int MB0>
+__device__ __forceinline__ void mma_half(f32x16 (&acc)[4][2], const typename E::Frag (&a)[4],
+                                         const typename E::Frag (&b)[2],
+                                         const typename E::Scales& sc) {
+  E::template mma<MB0, 0>(acc[MB0][0], a[MB0], b[0], sc);
+  E::template mma<MB0, 1>(acc[MB0][1], a[MB0], b[1], sc);
+  E::template mma<MB0 + 1, 0>(acc[MB0 + 1][0], a[MB0 + 1], b[0], sc);
+  E::template mma<MB0 + 1, 1>(acc[MB0 + 1][1], a[MB0 + 1], b[1], sc);
+}
+
+// The workgroup barrier of a 4-bit K-major step: this wave's LDS writes done, and every vector
+// load except its last kLoadsA (the weight words just issued, which the next step's dequantisation
+// waits for itself), so that the step's direct loads into the stage read next are done. In inline
+// assembly: __syncthreads() would wait for every load.
+template <int kLoadsA>
+__device__ __forceinline__ void barrier_keep_words() {
+  static_assert(kLoadsA == 3, "the wait count below");
+  asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool kClear, int kLoadsA, class IssueA, class CommitA, class IssueB, class Epi>
@@ -840,7 +863,10 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
                                              f32x16 (&acc)[4][2]) {
   typedef EBf16 E;
   constexpr int kG = E::kGroups;
-  static_assert(kG == 4, "the dequantisation of a step is split over four K groups");
+  static_assert(kG == 4, "the dequantisation of a step is split over the first three K groups");
+  constexpr int kLoadsB = 4;   // DmaKS issues four direct loads per thread
+  constexpr int kReads = 4 * reads_per_frag<E, true>() + 2 * reads_per_frag<E, true>();
+  constexpr int kMfma = 8 * mfma_per_mma<E>();
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int wm = w >> 2, wn = w & 3;
   // An odd nk gets one more K step per tile that stages zeros (see above), for an even total.
@@ -851,7 +877,6 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
   const std::integral_constant<int, 0> set0{};
   const std::integral_constant<int, 1> set1{};
   typedef std::integral_constant<int, 0> W0;
-  typedef std::integral_constant<int, 1> W1;
   typedef std::integral_constant<int, 2> W2;
   typedef std::integral_constant<int, 3> W3;
   typedef std::integral_constant<int, 4> W4;
@@ -865,7 +890,6 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
   commit_a(set0, sm.a0, W0{}, W4{});
   issue_a(set0, pa.tile, pa.ks);   // step 2
   pa.next(nkp);
-  commit_a(set1, sm.a1, W0{}, W1{});   // step 1's first word; step 0 commits the rest
   issue_b(pb.tile, pb.ks, sm.b1);  // step 1
   pb.next(nkp);
   vm_wait_seen();
@@ -875,32 +899,37 @@ __device__ __forceinline__ void gemm_run_q4k(const Smem& sm, int n_tiles, int nk
   auto step = [&](auto parity, int s, char* __restrict__ ca, char* __restrict__ cb,
                   char* __restrict__ na, char* __restrict__ nb) {
     const std::integral_constant<int, 1 - decltype(parity)::value> next_set{};
-    // Groups 0-2: words 1, 2 and 3 of step s + 1 (set s + 1) into its stage.
-    auto group = [&](auto kg_c, auto w0_c) {
+    // Groups 0-2: step s + 1's words (set s + 1, loaded after step s - 2's barrier) into its
+    // stage, words 0-1, 2 and 3.
+    auto group = [&](auto kg_c, auto w0_c, auto w1_c) {
       constexpr int kg = decltype(kg_c)::value;
+      constexpr int kWords = decltype(w1_c)::value - decltype(w0_c)::value;
       load_frags<E, true, true>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
       mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
-      commit_a(next_set, na, w0_c, std::integral_constant<int, decltype(w0_c)::value + 1>{});
-      sched_group_dequant<E, 0>();
+      commit_a(next_set, na, w0_c, w1_c);
+      sched_region<kMfma, kReads, 0, (kWords * 30 + kMfma - 1) / kMfma, kWords>();
       __builtin_amdgcn_sched_barrier(0);
     };
-    group(W0{}, W1{});
-    group(W1{}, W2{});
-    group(W2{}, W3{});
+    group(std::integral_constant<int, 0>{}, W0{}, W2{});
+    group(std::integral_constant<int, 1>{}, W2{}, W3{});
+    group(std::integral_constant<int, 2>{}, W3{}, W4{});
     const bool ends_tile = cur.ks == nkp - 1;
-    vm_wait_seen();
-    __syncthreads();
-    // Group 3, after the barrier (step s's stage is free): step s + 2's B loads and its first
-    // word (set s, complete since the barrier) into step s's stage, and step s + 3's words into
-    // the set committed above, with the next step's first fragment reads.
+    barrier_keep_words<kLoadsA>();
+    // Group 3: B's direct loads of step s + 2 with the first half of the MFMAs and the next
+    // stage's first fragment reads, then (a region of its own, so that they follow the direct
+    // loads and the next barrier can leave them in flight) step s + 3's words into the set
+    // committed above with the second half.
     issue_b(pb.tile, pb.ks, cb);
     pb.next(nkp);
-    commit_a(parity, ca, W0{}, W1{});
+    load_frags<E, true, true>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
+    mma_half<E, 0>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
+    sched_region<kMfma / 2, kReads, kLoadsB, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
     issue_a(next_set, pa.tile, pa.ks);
     pa.next(nkp);
-    load_frags<E, true, true>(na, nb, 0, wm, wn, l, f.a[0], f.b[0]);
-    mma_group<E>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
-    sched_group_dequant<E, 4 + kLoadsA>();
+    mma_half<E, 2>(acc, f.a[(kG - 1) & 1], f.b[(kG - 1) & 1], sc);
+    sched_region<kMfma / 2, 0, kLoadsA, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
     if (ends_tile) {
       epi(cur.tile, acc);
       if (kClear) zero_acc(acc);
@@ -964,7 +993,10 @@ __device__ __forceinline__ void gemm_run_q4n(const Smem& sm, int nk, IssueA&& is
         load_frags<E, true, false>(ca, cb, kg + 1, wm, wn, l, f.a[(kg + 1) & 1], f.b[(kg + 1) & 1]);
       mma_group<E>(acc, f.a[kg & 1], f.b[kg & 1], sc);
       commit_b(next_set, nb, kg_c, std::integral_constant<int, kg + 1>{});
-      sched_group_dequant<E, kg == 0 ? kLoadsA + kLoadsB : 0, true, false, (kg + 1 < kG)>();
+      sched_region<8 * mfma_per_mma<E>(),
+                   (kg + 1 < kG) ? 4 * reads_per_frag<E, true>() + 2 * reads_per_frag<E, false>() : 0,
+                   kg == 0 ? kLoadsA + kLoadsB : 0, (30 + 8 * mfma_per_mma<E>() - 1) / (8 * mfma_per_mma<E>()),
+                   1>();
       __builtin_amdgcn_sched_barrier(0);
     };
     group(std::integral_constant<int, 0>{});

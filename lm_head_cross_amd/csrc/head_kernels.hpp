@@ -197,8 +197,13 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
   const int64_t row_bytes = a.d * E::kSize;
 
   // The token of accumulator column block nb, recomputed where needed rather than held (as two
-  // 64-bit values) across the K loop.
-  auto tok_of = [&](int nb) { return t0 + acc_n(wn, nb, l); };
+  // 64-bit values) across the K loop. The 4-bit loop, with its dequantisation registers, needs
+  // the column made opaque to keep the compiler from hoisting the sum out of the loop.
+  auto tok_of = [&](int nb) {
+    int n = acc_n(wn, nb, l);
+    if constexpr (Q4) asm("" : "+v"(n));
+    return t0 + n;
+  };
   int y[2];
   float m[2], s[2];
 #pragma unroll
@@ -333,7 +338,11 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs a) {
     if constexpr (TMAX) {
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
-      if (l == 0) a.tmax[((int64_t)tb * a.n_vtiles + tile0 + tile) * 8 + w] = rmax;
+      // In the 4-bit loop the wave index is made uniform (readfirstlane), so that no per-lane
+      // 64-bit address is held across the K loop for this once-per-tile store.
+      int wi = w;
+      if constexpr (Q4) wi = __builtin_amdgcn_readfirstlane(w);
+      if (l == 0) a.tmax[((int64_t)tb * a.n_vtiles + tile0 + tile) * 8 + wi] = rmax;
     }
   };
   constexpr bool kF8 = std::is_same<E, EFp8>::value;
