@@ -45,6 +45,9 @@ def parse():
                          "with its distance from the exact head)")
     ap.add_argument("--no-dw", action="store_true",
                     help="frozen head: the backward computes dh only (no dW), as for the 4-bit head")
+    ap.add_argument("--q4-stage", action="store_true",
+                    help="4-bit workloads: each step dequantises W once into bf16 rows and runs the "
+                         "bf16 kernels on them (instead of dequantising every tile in the kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--mfma-peak", nargs="?", const="both", default=None,
@@ -250,10 +253,13 @@ def main():
     if args.fp8 and (cfg.q4 or cfg.dtype != "bf16"):
         print("--fp8 approximates a bf16 head: pick a bf16 workload", file=sys.stderr)
         sys.exit(2)
+    if args.q4_stage and not cfg.q4:
+        print("--q4-stage stages a 4-bit head: pick a q4 workload", file=sys.stderr)
+        sys.exit(2)
     want_dw = not cfg.q4 and not args.no_dw      # the 4-bit head is frozen: dh only
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
                       want_dW=want_dw, scope=cfg.scope, objective=args.objective, obj=obj,
-                      skip_eps=args.skip_eps, fp8=args.fp8)
+                      skip_eps=args.skip_eps, fp8=args.fp8, q4_stage=args.q4_stage)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -322,7 +328,7 @@ def main():
                          f"{cfg.name}{'-dh-only' if args.no_dw else ''}_traffic.txt")
     t = prof_summary.read_traffic(tfile)
     if (t is not None and t[0] == dom and not args.fp8 and args.skip_eps == 0
-            and args.objective == "orpo"):
+            and args.objective == "orpo" and not args.q4_stage):
         traffic = round(t[1])
     per_kernel = {k: {"launches_per_step": v[0] / n_tr, "avg_ms": v[1] / max(v[0], 1),
                       "ms_per_step": v[1] / n_tr,
@@ -397,6 +403,7 @@ def main():
             "objective": args.objective, "skip_eps": args.skip_eps, "fp8": args.fp8,
             "dW": want_dw,
             "w_format": "q4g64" if cfg.q4 else ("f32" if cfg.dtype == "f32" else "bf16"),
+            "q4_stage": args.q4_stage,
             "parallelism": "single GPU",
         },
         "mfma_frac_of_peak": round(mfma_frac, 4),

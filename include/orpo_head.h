@@ -323,6 +323,24 @@ orpo_status orpo_quantize_fp8(const void* x, int64_t rows, int64_t cols, uint8_t
                               hipStream_t stream);
 
 /*
+ * orpo_q4_stage — a 4-bit head (ORPO_Q4G64) dequantised once into bf16 rows, so that a step can run
+ * the bf16 kernels on it instead of dequantising the same weight tile again in every token tile.
+ * The map is the format's affine one ("ORPO training — design", the flash-CCE Metal kernel note
+ * on in-kernel affine dequantisation; "Training — design" §5.1 "The head", where the 4-bit head's
+ * operands are dequantised for the logit products): w_bf16[v, k] = bf16(scale * q + bias), the
+ * product and sum in fp32 and one rounding to nearest even, the same arithmetic the 4-bit tiled
+ * loops apply to each tile they stage. orpo_head_fwd / orpo_head_bwd with w_fmt = ORPO_BF16 on the
+ * staged rows therefore see the operand values that w_fmt = ORPO_Q4G64 gives them.
+ *   W       device: words [V, d/8] (uint32, 4-byte aligned), bf16 scales and biases [V, d/64]
+ *   V, d    V > 0 and at most INT32_MAX; d > 0, a multiple of 64 and at most 2^20
+ *   w_bf16  device output, bf16 [V, d] row-major, 16-byte aligned, caller-owned (2 V d bytes);
+ *           it must not overlap W
+ * Errors: ORPO_EINVAL for bad sizes, a null or misaligned pointer (nothing is launched). Reads
+ * and writes only the arrays named; asynchronous on `stream`.
+ */
+orpo_status orpo_q4_stage(orpo_weight W, int64_t V, int64_t d, void* w_bf16, hipStream_t stream);
+
+/*
  * orpo_head_fwd_fp8 — orpo_head_fwd with the logits taken from FP8 operands.
  *   desc   the bf16 head being approximated: h_fmt = w_fmt = ORPO_BF16 and d a multiple of 128
  *          (else ORPO_EUNSUPPORTED); M, V, softcap, ignore_index, skip_eps as for orpo_head_fwd,
@@ -373,7 +391,8 @@ typedef enum {
   ORPO_K_DHDW = 4,   /* backward launch with dh / dW tiles only (last of a pass)         */
   ORPO_K_BWD = 5,    /* backward launch with both (all the others)                       */
   ORPO_K_QUANT = 6,  /* FP8 row quantisation (orpo_quantize_fp8)                          */
-  ORPO_K_COUNT = 7
+  ORPO_K_STAGE = 7,  /* 4-bit head staged as bf16 rows (orpo_q4_stage)                    */
+  ORPO_K_COUNT = 8
 } orpo_kernel_kind;
 orpo_status orpo_trace_enable(int32_t max_launches);   /* 0 disables and releases the events */
 orpo_status orpo_trace_collect(int32_t kind, int64_t* launches, double* total_ms, double* flops);

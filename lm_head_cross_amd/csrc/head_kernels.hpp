@@ -2,6 +2,7 @@
 //
 //   quant_fp8_kernel: bf16 rows -> FP8 E4M3 codes with one power-of-two (E8M0) scale per row, for
 //                   the low-precision logit operands.
+//   q4_stage_kernel: a 4-bit head -> bf16 rows, the tiled loops' own dequantisation done once.
 //   fwd_kernel    : raw = W . h^T tile by tile (MFMA), softcap, online softmax per token over the
 //                   workgroup's vocabulary split, label-logit capture -> per-split (max, sum) partials.
 //   merge_kernel  : partials of all splits -> lse, logp = z[y] - lse.
@@ -133,6 +134,36 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* x, int64
   const int e = fp8_row_exponent(amax);
   for (int64_t c = (int64_t)l * 8; c < cols; c += 512) *(u32x2*)(qr + c) = e4m3_codes8(*(const u32x4*)(xr + c), e);
   if (l == 0) exps[r] = (uint8_t)(e + 127);
+}
+
+// A 4-bit head dequantised to bf16 rows in HBM: each lane takes one packed word (8 codes) and
+// stores its 16 bytes, so a wave's store covers 1 KB of contiguous output; kQ4StagePer words per
+// lane and iteration are loaded before any is converted. The arithmetic is dequant_word's, the
+// one the tiled loops apply in LDS (fp32 scale * q + bias, rounded to nearest even), so the
+// staged rows equal what those loops would stage, bit for bit. d % 64 == 0: the 8 words of a
+// group lie in one row, and word j's group is j / 8 of the flattened [V, d / 64] scales.
+constexpr int kQ4StagePer = 4;
+__global__ __launch_bounds__(256) void q4_stage_kernel(Q4Weight W, uint16_t* out, int64_t n_words) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * kQ4StagePer;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kQ4StagePer + threadIdx.x; base < n_words;
+       base += stride) {
+    uint32_t q[kQ4StagePer];
+    uint16_t sb[kQ4StagePer], bb[kQ4StagePer];
+#pragma unroll
+    for (int i = 0; i < kQ4StagePer; ++i) {
+      const int64_t j = base + i * 256;
+      const int64_t jj = j < n_words ? j : 0;
+      q[i] = W.wq[jj];
+      sb[i] = W.scales[jj >> 3];
+      bb[i] = W.biases[jj >> 3];
+    }
+#pragma unroll
+    for (int i = 0; i < kQ4StagePer; ++i) {
+      const int64_t j = base + i * 256;
+      if (j < n_words)
+        *(u32x4*)(out + j * 8) = dequant_word(q[i], bf16_bits_to_f32(sb[i]), bf16_bits_to_f32(bb[i]));
+    }
+  }
 }
 
 // E8M0 exponent bytes of rows r0 + lane_row + 32 i (i < N) packed little-endian, the MFMA's

@@ -398,6 +398,27 @@ orpo_status orpo_quantize_fp8(const void* x, int64_t rows, int64_t cols, uint8_t
   return launched();
 }
 
+orpo_status orpo_q4_stage(orpo_weight W, int64_t V, int64_t d, void* w_bf16, hipStream_t stream) {
+  if (V <= 0 || d <= 0 || d % 64 != 0 || V > INT32_MAX || d > (int64_t(1) << 20)) return ORPO_EINVAL;
+  if (!W.w || !W.scales || !W.biases || !w_bf16) return ORPO_EINVAL;
+  if ((uintptr_t)W.w % 4 || (uintptr_t)W.scales % 2 || (uintptr_t)W.biases % 2 ||
+      (uintptr_t)w_bf16 % 16)
+    return ORPO_EINVAL;
+  Q4Weight q;
+  q.wq = (const uint32_t*)W.w;
+  q.scales = (const uint16_t*)W.scales;
+  q.biases = (const uint16_t*)W.biases;
+  q.V = V;
+  q.d = d;
+  const int64_t n_words = V * (d / 8);
+  // Enough workgroups to keep every CU's loads in flight; the loop strides over the rest.
+  const int64_t blocks = std::min<int64_t>(cdiv(n_words, 256 * kQ4StagePer), 256 * 16);
+  TraceScope ts(ORPO_K_STAGE, 0.0, stream);
+  hipLaunchKernelGGL(q4_stage_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, q,
+                     (uint16_t*)w_bf16, n_words);
+  return launched();
+}
+
 static orpo_status loss_impl(int32_t S, int64_t M, int32_t n_pairs, const int32_t* seg_offsets,
                              const float* logp, const int32_t* labels, int64_t V,
                              int32_t ignore_index, double lambda, double* out, float* g, void* ws,

@@ -64,6 +64,7 @@ _SIGS = {
     "orpo_head_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), _P, Weight, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P, _P]),
     "orpo_quantize_fp8": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
+    "orpo_q4_stage": (ctypes.c_int, [Weight, ctypes.c_int64, ctypes.c_int64, _P, _P]),
     "orpo_head_fwd_fp8": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Fp8Operands), _P, _P,
                                          _P, _P, ctypes.c_size_t, _P]),
     "orpo_head_bwd_fp8": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(Fp8Operands), _P,
@@ -78,7 +79,8 @@ _SIGS = {
                                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "orpo_trace_reset": (ctypes.c_int, []),
 }
-KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw", 5: "bwd", 6: "quant"}
+KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw", 5: "bwd", 6: "quant",
+                7: "stage"}
 _lib = None
 
 
@@ -335,6 +337,27 @@ def head_bwd(h, w, labels, lse, g, softcap=0.0, want_dW=True, ignore_index=IGNOR
     return dh, dW
 
 
+def q4_stage(w, scales, biases, out=None):
+    """The 4-bit head (packed words [V, d/8] int32, bf16 scales and biases [V, d/64]) dequantised
+    to bf16 rows [V, d] (orpo_q4_stage): the operand values the 4-bit kernels stage per tile."""
+    _need_dtype("w", w, torch.int32)
+    _need_dtype("scales", scales, torch.bfloat16)
+    _need_dtype("biases", biases, torch.bfloat16)
+    _need_dtype("out", out, torch.bfloat16)
+    _need_gpu(w, scales, biases, out)
+    if w.dim() != 2:
+        raise OrpoError("w must be the packed words [V, d/8]")
+    V, d = w.shape[0], w.shape[1] * 8
+    _need_shape("scales", scales, (V, d // 64))
+    _need_shape("biases", biases, (V, d // 64))
+    if out is None:
+        out = torch.empty(V, d, dtype=torch.bfloat16, device=w.device)
+    _need_shape("out", out, (V, d))
+    _check(lib().orpo_q4_stage(Weight(w.data_ptr(), scales.data_ptr(), biases.data_ptr()), V, d,
+                               _ptr(out), _stream(w.device)), "orpo_q4_stage")
+    return out
+
+
 # ------------------------------------------------------------------------------------------------
 # The FP8 head: row-wise E4M3 logit operands (an opt-in approximation of the bf16 head)
 # ------------------------------------------------------------------------------------------------
@@ -507,7 +530,7 @@ def grpo_loss(logp, old_logp, ref_logp, advantages, labels, seg_offsets, V, clip
 class HeadStep:
     def __init__(self, h, w, labels, seg_offsets, V, softcap, lam, scales=None, biases=None,
                  want_dW=True, ignore_index=IGNORE_INDEX, scope="response", objective="orpo",
-                 obj=None, skip_eps=0.0, dh_bf16=False, fp8=False):
+                 obj=None, skip_eps=0.0, dh_bf16=False, fp8=False, q4_stage=False):
         """One head step: forward -> loss -> backward on preallocated buffers.
 
         objective "orpo" (lam, scope "response" | "full"), or a sibling on the same forward and
@@ -516,7 +539,10 @@ class HeadStep:
         beta, old_logp [M], ref_logp [M], advantages [S] float32, seg_offsets are then [S+1]
         completions}. dh_bf16: dh as bfloat16 (the fp32 sums rounded once). fp8: the FP8 head (an
         approximation): each step quantises h and W to row-wise E4M3 (part of the step) and takes
-        the logits from them; the gradient products keep the bf16 h and W."""
+        the logits from them; the gradient products keep the bf16 h and W. q4_stage (a 4-bit
+        head): each step first dequantises W once into a bf16 copy (orpo_q4_stage, part of the
+        step, 2 V d bytes more memory) and runs the bf16 kernels on it, with the operand values
+        the 4-bit kernels would stage tile by tile."""
         if objective != "orpo" and objective != "grpo" and objective not in PREF_KINDS:
             raise OrpoError(f"unknown objective {objective!r}")
         o = dict(obj or {})
@@ -535,6 +561,8 @@ class HeadStep:
             raise OrpoError(f"V = {V} but the head has {Vw} vocabulary rows")
         if scales is not None and want_dW:
             raise OrpoError("a 4-bit head is frozen: it has no dW (pass want_dW=False)")
+        if q4_stage and (scales is None or fp8):
+            raise OrpoError("q4_stage stages a 4-bit head (scales and biases given, not fp8)")
         S = SCOPES[scope] if objective == "orpo" else (1 if objective == "grpo" else 2)
         P = _need_offsets(seg_offsets, S)
         if objective in ("dpo", "ipo", "hinge"):
@@ -559,8 +587,10 @@ class HeadStep:
         self.S = S
         self.P = P
         dev = h.device
-        self.desc = make_desc(self.M, self.d, V, h.dtype, _w_fmt(w, scales), softcap, ignore_index,
-                              flags=ORPO_DH_BF16 if dh_bf16 else 0, skip_eps=skip_eps)
+        self.q4_stage = bool(q4_stage)
+        self.desc = make_desc(self.M, self.d, V, h.dtype,
+                              ORPO_BF16 if self.q4_stage else _w_fmt(w, scales), softcap,
+                              ignore_index, flags=ORPO_DH_BF16 if dh_bf16 else 0, skip_eps=skip_eps)
         L = lib()
         self.fws = _workspace(L.orpo_head_fwd_workspace_bytes(ctypes.byref(self.desc)), dev)
         self.bws = _workspace(L.orpo_head_bwd_workspace_bytes(ctypes.byref(self.desc)), dev)
@@ -576,6 +606,10 @@ class HeadStep:
         self.dW = torch.empty(V, self.d, dtype=torch.float32, device=dev) if want_dW else None
         self.wt = Weight(w.data_ptr(), None if scales is None else scales.data_ptr(),
                          None if biases is None else biases.data_ptr())
+        if self.q4_stage:
+            self.wq4 = self.wt
+            self.w16 = torch.empty(V, self.d, dtype=torch.bfloat16, device=dev)
+            self.wt = Weight(self.w16.data_ptr(), None, None)
         self.fp8 = bool(fp8)
         if self.fp8:
             self.hq = torch.empty(self.M, self.d, dtype=torch.uint8, device=dev)
@@ -590,6 +624,9 @@ class HeadStep:
         return _stream(self.h.device)
 
     def forward(self):
+        if self.q4_stage:
+            _check(lib().orpo_q4_stage(self.wq4, self.V, self.d, _ptr(self.w16), self._s()),
+                   "orpo_q4_stage")
         if self.fp8:
             L = lib()
             _check(L.orpo_quantize_fp8(_ptr(self.h), self.M, self.d, _ptr(self.hq), _ptr(self.h_exp),
@@ -649,4 +686,6 @@ class HeadStep:
         n = self.fws.numel() + self.bws.numel() + self.lws.numel()
         if self.fp8:
             n += self.hq.numel() + self.h_exp.numel() + self.wq.numel() + self.w_exp.numel()
+        if self.q4_stage:
+            n += self.w16.numel() * 2
         return n

@@ -71,14 +71,18 @@ def oracle_weight(inp: synth.HeadInputs) -> np.ndarray:
     return inp.w.float().numpy().astype(np.float64)
 
 
-def run_gpu(inp: synth.HeadInputs, want_dW=None, g_override=None):
-    """fwd -> loss -> bwd on the GPU; returns numpy results (and the GPU tensors under 't')."""
+def run_gpu(inp: synth.HeadInputs, want_dW=None, g_override=None, q4_stage=False):
+    """fwd -> loss -> bwd on the GPU; returns numpy results. q4_stage: a 4-bit head is first
+    staged as bf16 rows (orpo_q4_stage) and the bf16 kernels run on them."""
     d = dev()
     cfg = inp.cfg
     if want_dW is None:
         want_dW = not cfg.q4
     h = inp.h.to(d)
     w, sc, bi = gpu_weights(inp, d)
+    if q4_stage:
+        assert cfg.q4
+        w, sc, bi = H.q4_stage(w, sc, bi), None, None
     labels = torch.from_numpy(inp.labels).to(d)
     off = torch.from_numpy(inp.seg_offsets).to(d)
     logp, lse, fws = H.head_fwd(h, w, labels, cfg.softcap, scales=sc, biases=bi, return_ws=True)
@@ -98,19 +102,21 @@ def run_gpu(inp: synth.HeadInputs, want_dW=None, g_override=None):
     }
 
 
-def mfma_operand_weight(inp: synth.HeadInputs) -> np.ndarray:
+def mfma_operand_weight(inp: synth.HeadInputs, rows=None) -> np.ndarray:
     """W as the kernels multiply it: dense weights as given; 4-bit weights dequantised as
     fp32(scale) * q + fp32(bias) (the product is exact in fp32, the sum rounds once) and rounded to
     bf16, which is what the kernels stage for the MFMA. Test-side data preparation for the
-    per-token gates; the oracle itself always dequantises exactly."""
+    per-token gates; the oracle itself always dequantises exactly. rows: only those rows (4-bit)."""
     if not inp.cfg.q4:
         return oracle_weight(inp)
-    V, nw = inp.wq.shape
+    sel = slice(None) if rows is None else np.asarray(rows)
+    wq = inp.wq[sel]
+    V, nw = wq.shape
     d = nw * 8
     shifts = (np.arange(8, dtype=np.uint32) * 4)[None, None, :]
-    q = ((inp.wq[:, :, None] >> shifts) & 0xF).reshape(V, d).astype(np.float32)
-    sc = np.repeat(inp.scales.float().numpy(), 64, axis=1)
-    bi = np.repeat(inp.biases.float().numpy(), 64, axis=1)
+    q = ((wq[:, :, None] >> shifts) & 0xF).reshape(V, d).astype(np.float32)
+    sc = np.repeat(inp.scales.float().numpy()[sel], 64, axis=1)
+    bi = np.repeat(inp.biases.float().numpy()[sel], 64, axis=1)
     w32 = (sc * q + bi).astype(np.float32)
     return torch.from_numpy(w32).to(torch.bfloat16).float().numpy().astype(np.float64)
 

@@ -300,3 +300,12 @@ def test_fp8_entry_points_validate_before_any_launch():
     assert L.orpo_quantize_fp8(4096, 4, 64, 4100, 4096, None) == EINVAL      # q not 8-byte aligned
     assert L.orpo_quantize_fp8(None, 4, 64, 4096, 4096, None) == EINVAL
     assert L.orpo_quantize_fp8(None, 0, 64, None, None, None) == 0           # nothing to do
+    # 4-bit staging: sizes, nulls and alignment are refused before any launch.
+    q4 = H.Weight(4096, 8192, 8192)
+    assert L.orpo_q4_stage(q4, 4, 96, 4096, None) == EINVAL                   # d % 64
+    assert L.orpo_q4_stage(q4, 0, 64, 4096, None) == EINVAL                   # V = 0
+    assert L.orpo_q4_stage(q4, 4, 64, None, None) == EINVAL                   # no output
+    assert L.orpo_q4_stage(H.Weight(4096, None, 8192), 4, 64, 4096, None) == EINVAL
+    assert L.orpo_q4_stage(H.Weight(4098, 8192, 8192), 4, 64, 4096, None) == EINVAL  # words not 4-byte aligned
+    assert L.orpo_q4_stage(H.Weight(4096, 8193, 8192), 4, 64, 4096, None) == EINVAL  # scales not 2-byte aligned
+    assert L.orpo_q4_stage(q4, 4, 64, 4104, None) == EINVAL                   # output not 16-byte aligned

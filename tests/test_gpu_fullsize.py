@@ -35,10 +35,14 @@ def _sample_rows(inp, n_per_branch=2, seed=0):
 
 @pytest.mark.parametrize("name", ["minicpm-like-bf16", "e4b-bf16-softcap30",
                                   "q4g64-minicpm-shape-softcap30", "q4g64-e4b-shape-softcap30",
+                                  "q4g64-minicpm-shape-softcap30+stage",
+                                  "q4g64-e4b-shape-softcap30+stage",
                                   "12b-like-bf16-softcap30", "e4b-bf16-softcap30-fullnll"])
 def test_full_size_sampled_parity(name):
+    # "+stage": the 4-bit head staged as bf16 rows each step (HeadStep q4_stage, bench --q4-stage).
+    name, _, variant = name.partition("+")
     cfg = synth.workload(name)
-    say(f"[fullsize] {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}")
+    say(f"[fullsize] {cfg.name}{'+' + variant if variant else ''} M={cfg.M} d={cfg.d} V={cfg.V}")
     inp = synth.make_inputs(cfg, seed=0, label_device="cuda")
     d = dev()
     h = inp.h.to(d)
@@ -50,7 +54,7 @@ def test_full_size_sampled_parity(name):
     labels = torch.from_numpy(inp.labels).to(d)
     off = torch.from_numpy(inp.seg_offsets).to(d)
     step = H.HeadStep(h, w, labels, off, cfg.V, cfg.softcap, cfg.lam, scales=sc, biases=bi,
-                      want_dW=not cfg.q4, scope=cfg.scope)
+                      want_dW=not cfg.q4, scope=cfg.scope, q4_stage=variant == "stage")
     step.forward()
     step.loss()
     torch.cuda.synchronize()
