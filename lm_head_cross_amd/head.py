@@ -344,15 +344,15 @@ def q4_stage(w, scales, biases, out=None):
     _need_dtype("scales", scales, torch.bfloat16)
     _need_dtype("biases", biases, torch.bfloat16)
     _need_dtype("out", out, torch.bfloat16)
-    _need_gpu(w, scales, biases, out)
     if w.dim() != 2:
         raise OrpoError("w must be the packed words [V, d/8]")
     V, d = w.shape[0], w.shape[1] * 8
     _need_shape("scales", scales, (V, d // 64))
     _need_shape("biases", biases, (V, d // 64))
+    _need_shape("out", out, (V, d))
+    _need_gpu(w, scales, biases, out)
     if out is None:
         out = torch.empty(V, d, dtype=torch.bfloat16, device=w.device)
-    _need_shape("out", out, (V, d))
     _check(lib().orpo_q4_stage(Weight(w.data_ptr(), scales.data_ptr(), biases.data_ptr()), V, d,
                                _ptr(out), _stream(w.device)), "orpo_q4_stage")
     return out

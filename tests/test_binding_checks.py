@@ -50,6 +50,19 @@ def test_q4_shapes():
                    scales=sc, biases=bi)
 
 
+def test_q4_stage_shapes():
+    wq, sc, bi = t(V, D // 8, dtype=I32), t(V, D // 64), t(V, D // 64)
+    _raises_device(lambda: H.q4_stage(wq, sc, bi))
+    _raises_device(lambda: H.q4_stage(wq, sc, bi, out=t(V, D)))
+    _raises_shape(lambda: H.q4_stage(wq, t(V, D // 32), bi), "scales")
+    _raises_shape(lambda: H.q4_stage(wq, sc, t(V + 1, D // 64)), "biases")
+    _raises_shape(lambda: H.q4_stage(wq, sc, bi, out=t(V, D + 64)), "out")
+    with pytest.raises(H.OrpoError, match="bfloat16"):
+        H.q4_stage(wq, sc, bi, out=t(V, D, dtype=F32))
+    with pytest.raises(H.OrpoError):
+        H.q4_stage(t(V * D // 8, dtype=I32), sc, bi)                       # words not 2-D
+
+
 def test_head_bwd_shapes():
     h, w, lab = t(M, D), t(V, D), t(M, dtype=I32)
     lse, g = t(M, dtype=F32), t(M, dtype=F32)
@@ -107,6 +120,11 @@ def test_head_step_checks():
                   "ref_sums")
     with pytest.raises(H.OrpoError, match="ref_sums"):
         H.HeadStep(h, w, lab, off, V, 30.0, 0.1, objective="dpo", obj={"beta": 0.1})
+    with pytest.raises(H.OrpoError, match="q4_stage"):                    # a bf16 head has no words
+        H.HeadStep(h, w, lab, off, V, 30.0, 0.1, q4_stage=True)
+    wq, sc, bi = t(V, D // 8, dtype=I32), t(V, D // 64), t(V, D // 64)
+    _raises_device(lambda: H.HeadStep(h, wq, lab, off, V, 30.0, 0.1, scales=sc, biases=bi,
+                                      want_dW=False, q4_stage=True))
     g_obj = {"clip_eps": 0.2, "beta": 0.04, "old_logp": t(M, dtype=F32), "ref_logp": t(M, dtype=F32),
              "advantages": t(4, dtype=F32)}
     _raises_device(lambda: H.HeadStep(h, w, lab, off, V, 30.0, 0.1, objective="grpo", obj=g_obj))
