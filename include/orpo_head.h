@@ -94,7 +94,9 @@ typedef struct {
 /* Workspace sizes in bytes (0 on invalid arguments). The forward workspace grows as 256 + 8 * NBLK
  * * M (per-token partials over NBLK vocabulary splits, like lse it is O(M)); the backward
  * workspace holds two coefficient tiles of fixed size (double-buffered), independent of M beyond
- * one token chunk. The loss workspace (O(n_pairs)) serves both orpo_loss and orpo_loss_full. */
+ * one token chunk, and for a small M (few dh tiles, each with a long vocabulary K, split over
+ * several workgroups) up to 64 MiB of fp32 dh partial sums, which are added in a fixed order. The
+ * loss workspace (O(n_pairs)) serves both orpo_loss and orpo_loss_full. */
 size_t orpo_head_fwd_workspace_bytes(const orpo_head_desc* desc);
 size_t orpo_head_bwd_workspace_bytes(const orpo_head_desc* desc);
 size_t orpo_loss_workspace_bytes(int64_t M, int32_t n_pairs);
@@ -392,7 +394,8 @@ typedef enum {
   ORPO_K_BWD = 5,    /* backward launch with both (all the others)                       */
   ORPO_K_QUANT = 6,  /* FP8 row quantisation (orpo_quantize_fp8)                          */
   ORPO_K_STAGE = 7,  /* 4-bit head staged as bf16 rows (orpo_q4_stage)                    */
-  ORPO_K_COUNT = 8
+  ORPO_K_DHSUM = 8,  /* sum of split dh tiles' partials (small M; orpo_head_bwd)          */
+  ORPO_K_COUNT = 9
 } orpo_kernel_kind;
 orpo_status orpo_trace_enable(int32_t max_launches);   /* 0 disables and releases the events */
 orpo_status orpo_trace_collect(int32_t kind, int64_t* launches, double* total_ms, double* flops);

@@ -668,9 +668,12 @@ struct BwdItem {
   void* coeff;            // [C, BVb] of E::T, token-major
   uint8_t* fdh;           // coefficient filter flags for dh: [C/256][BVb/64][4] (null: filter off)
   uint8_t* fdw;           // ... and for dW: [BVb/256][C/64][2]
-  int32_t n_tiles;        // tiles of this item in the launch (coefficient: n_vt * n_tt; GEMM: dh + dW)
+  int32_t n_tiles;        // workgroups of this item in the launch (coefficient: n_vt * n_tt; GEMM: dh + dW)
   int32_t n_vt, n_tt;     // 256-tiles along vocabulary and tokens
-  int32_t n_dh;           // dh tiles (GEMM item); dW tiles are n_tiles - n_dh
+  int32_t n_dh;           // dh workgroups (GEMM item: dh tiles x dh_split); dW tiles are n_tiles - n_dh
+  int32_t dh_split;       // K ranges per dh tile (1: none); each writes an fp32 partial to dh_part
+  float* dh_part;         // [dh_split][C][d] partial sums over chunk rows (dh_split > 1)
+  int64_t dh_part_pitch;  // elements from one split's partial to the next (C d)
   int32_t dh_first, dw_first;
   int32_t dh_last;        // the chunk's last vocabulary block (bf16 dh is written then)
 };
@@ -951,6 +954,17 @@ __device__ __forceinline__ int build_klist(const uint8_t* flags, int nk, int par
   return total;
 }
 
+// The first position of the ascending run list [0, n) whose step is >= v (n if none).
+__device__ __forceinline__ int klist_lower_bound(const uint16_t* list, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int)list[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Row offset of accumulator element r within its 32 x 32 block (acc_m(wm, mb, r, l) - acc_m(wm, mb, 0, l)).
 __device__ __forceinline__ int acc_dr(int r) { return 8 * (r >> 2) + (r & 3); }
 
@@ -1062,6 +1076,12 @@ __device__ __forceinline__ void store_out_bf16(uint16_t* out16, const float* pre
 }
 
 // Phase 2a: dh[c0 + i][j] (+)= sum_v coeff[i][v] W[v0 + v][j]   (m = token, n = hidden, k = vocabulary)
+// With it.dh_split = S > 1 (few dh tiles, each with a long K), workgroup u of the dh range runs
+// split s = u / n_tiles of tile u % n_tiles: the K steps [nk s / S, nk (s + 1) / S) (under the
+// coefficient filter, those of its run list), and stores its fp32 sum as partial s;
+// dh_reduce_kernel then adds the S partials in split order. The ranges are of step indices, not
+// of run positions, so a filter that drops only all-zero steps sums the same steps per split as
+// the exact backward and gives the same bits.
 template <class E, bool Q4, bool SKIP>
 __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, const BwdItem& it, int bid,
                                         uint16_t* klist, int* wave_tot) {
@@ -1069,7 +1089,10 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   const int64_t row_bytes = a.d * E::kSize;
   const int64_t cpitch = a.BVb * E::kSize;
   const int64_t t_end = min(a.M, it.c0 + it.C_cur);
-  const int t = xcd_remap(bid, it.n_dh);
+  const int S = it.dh_split;
+  const int u = xcd_remap(bid, it.n_dh);
+  const int n_dh_tiles = it.n_dh / S;
+  const int t = u % n_dh_tiles, split = u / n_dh_tiles;
   const int ti = t / a.n_jt, jt = t % a.n_jt;
   const int64_t i0 = (int64_t)ti * kTile, j0 = (int64_t)jt * kTile;
   const int64_t kv = ((it.BV_cur + kTile - 1) / kTile) * kTile;   // coefficient columns written
@@ -1083,10 +1106,16 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
   else lb.init((const char*)a.w + it.v0 * row_bytes, row_bytes, v_end - it.v0);   // block rows
   // Coefficient filter: run only the vocabulary slices some coefficient of this token tile needs.
   constexpr bool filt = SKIP;
-  const int n_run = filt ? build_klist(it.fdh + (int64_t)ti * a.nsl_v * 4, nk, 4, klist, wave_tot) : nk;
-  // The vocabulary step of run position ks (positions past n_run: the last one, in bounds).
+  const int n_all = filt ? build_klist(it.fdh + (int64_t)ti * a.nsl_v * 4, nk, 4, klist, wave_tot) : nk;
+  // This workgroup's run positions [kb, kb + n_run): its K steps' range, located in the ascending
+  // run list under the filter.
+  const int lo = (int)((int64_t)nk * split / S), hi = (int)((int64_t)nk * (split + 1) / S);
+  const int kb = filt ? __builtin_amdgcn_readfirstlane(klist_lower_bound(klist, n_all, lo)) : lo;
+  const int n_run = (filt ? __builtin_amdgcn_readfirstlane(klist_lower_bound(klist, n_all, hi)) : hi) - kb;
+  // The vocabulary step of run position kb + ks (positions past n_run: the last one, in bounds).
   auto step_of = [&](int ks) {
-    return filt ? __builtin_amdgcn_readfirstlane(klist[min(ks, n_run - 1)]) : min(ks, nk - 1);
+    const int pos = kb + min(ks, n_run - 1);
+    return filt ? __builtin_amdgcn_readfirstlane(klist[pos]) : pos;
   };
   f32x16 acc[4][2];
   zero_acc(acc);
@@ -1105,7 +1134,8 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
     gemm_run_q4n<Q4N2::kLoads>(smem, n_run, issue_a, issue_b, commit_b, acc);
   } else {
     auto issue = [&](int, int ks, char* sa, char* sb) {
-      const int64_t k0 = (int64_t)(filt ? __builtin_amdgcn_readfirstlane(klist[ks]) : ks) * E::kBK;
+      const int pos = kb + ks;
+      const int64_t k0 = (int64_t)(filt ? __builtin_amdgcn_readfirstlane(klist[pos]) : pos) * E::kBK;
       la.issue(i0, k0 * E::kSize, sa);
       lb.issue(k0, j0 * E::kSize, sb);
     };
@@ -1117,6 +1147,10 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
     gemm_run<E, true, false, false, !SKIP>(smem, 1, n_run, issue, commit, nop, acc);
   }
   (void)tid;
+  if (S > 1) {   // every split stores its partial (the reduction reads all of them), zeros included
+    store_out<E>(it.dh_part + split * it.dh_part_pitch, a.d, i0, t_end - it.c0, j0, a.d, true, acc);
+    return;
+  }
   if (!a.dh16) {
     if (n_run > 0 || it.dh_first)
       store_out<E>(a.dh, a.d, it.c0 + i0, t_end, j0, a.d, it.dh_first != 0, acc);
@@ -1125,6 +1159,28 @@ __device__ __forceinline__ void dh_tile(const Smem& smem, const BwdArgs& a, cons
                    acc);
   } else if (n_run > 0 || it.dh_first) {
     store_out<E>(a.dh_acc, a.d, i0, t_end - it.c0, j0, a.d, it.dh_first != 0, acc);
+  }
+}
+
+// The split dh tiles' partials of the chunk's rows, added in split order, then stored as an
+// unsplit tile stores its sum: dh overwritten on the chunk's first vocabulary block and added to
+// after it; bf16 dh through the chunk's fp32 accumulator, rounded once on the last block.
+__global__ __launch_bounds__(256) void dh_reduce_kernel(BwdArgs a) {
+  const BwdItem& it = a.gm;
+  const int64_t n = (min(a.M, it.c0 + it.C_cur) - it.c0) * a.d;
+  const int S = it.dh_split;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    float v = it.dh_part[e];
+    for (int s = 1; s < S; ++s) v += it.dh_part[s * it.dh_part_pitch + e];
+    if (!a.dh16) {
+      float* p = a.dh + it.c0 * a.d + e;
+      *p = it.dh_first ? v : *p + v;
+    } else if (it.dh_last) {
+      const float w = it.dh_first ? v : a.dh_acc[e] + v;
+      a.dh16[it.c0 * a.d + e] = (uint16_t)(pack_bf16x2(w, 0.f) & 0xffffu);
+    } else {
+      a.dh_acc[e] = it.dh_first ? v : a.dh_acc[e] + v;
+    }
   }
 }
 

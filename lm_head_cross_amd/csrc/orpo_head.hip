@@ -142,6 +142,8 @@ struct BwdPlan {
   int64_t C, BVb;
   size_t dh_acc_bytes;   // fp32 [C, d] chunk accumulator for bf16 dh over several blocks (else 0)
   size_t fl_bytes;   // skip flags per coefficient buffer (0 without the coefficient filter)
+  int dh_split;      // K ranges per dh tile (1: none)
+  size_t part_off, part_bytes;   // fp32 [dh_split][C][d] dh partials (dh_split > 1)
   size_t ws;
 };
 
@@ -171,7 +173,28 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
   p.dh_acc_bytes = (d->flags & ORPO_DH_BF16) && cdiv(d->V, p.BVb) > 1
                        ? round_up(size_t(p.C) * size_t(d->d) * sizeof(float), 256)
                        : 0;
-  p.ws = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize) + 2 * p.fl_bytes + p.dh_acc_bytes;
+  // Split-K dh. A dh tile's K is the whole vocabulary block, so with few token tiles (small M) a
+  // launch holds a few dh tiles that each run far longer than the launch's average work per CU,
+  // and the launch waits for them. When a dh tile's K steps reach twice that average, its K is
+  // split over dh_split workgroups (at most one round of kTargetWorkgroups dh workgroups, at most
+  // 16 splits, at least 4 K steps each), so the partials take at most 256 tiles x 256 x 256 fp32 =
+  // 64 MiB. The average assumes dW tiles are present (the workspace size does not know whether dW
+  // is asked for).
+  {
+    const int64_t kbk = k == kF32 ? 32 : 64;
+    const int64_t n_jt = cdiv(d->d, kTile), n_tt = cdiv(p.C, kTile), n_vt = cdiv(p.BVb, kTile);
+    const int64_t nk_dh = cdiv(p.BVb, kbk), n_dh = n_tt * n_jt;
+    const int64_t work = n_dh * nk_dh + n_vt * n_jt * cdiv(p.C, kbk) + n_tt * n_vt * cdiv(d->d, kbk);
+    const int64_t per_cu = cdiv(work, kTargetWorkgroups);
+    int64_t S = 1;
+    if (nk_dh >= 2 * per_cu)
+      S = std::min<int64_t>(std::min<int64_t>(cdiv(nk_dh, per_cu), kTargetWorkgroups / n_dh),
+                            std::min<int64_t>(16, nk_dh / 4));
+    p.dh_split = S >= 2 ? (int)S : 1;
+  }
+  p.part_bytes = p.dh_split > 1 ? round_up(size_t(p.dh_split) * size_t(p.C) * size_t(d->d) * 4, 256) : 0;
+  p.part_off = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize) + 2 * p.fl_bytes;
+  p.ws = p.part_off + p.part_bytes + p.dh_acc_bytes;
   return p;
 }
 
@@ -636,7 +659,10 @@ orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
     it.dh_last = blk == n_blocks - 1;
     it.dw_first = c == 0 && !acc_dw;
     if (gemm) {
-      it.n_dh = it.n_tt * a.n_jt;
+      it.dh_split = p.dh_split;
+      it.dh_part = p.dh_split > 1 ? (float*)((char*)ws + p.part_off) : nullptr;
+      it.dh_part_pitch = p.C * desc->d;
+      it.n_dh = it.n_tt * a.n_jt * p.dh_split;
       it.n_tiles = it.n_dh + (dW ? it.n_vt * a.n_jt : 0);
     } else {
       it.n_tiles = it.n_vt * it.n_tt;
@@ -652,6 +678,13 @@ orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
     else if (k == kBf16) st = sc ? launch_bwd<EBf16, false, true>(a, grid, stream) : launch_bwd<EBf16, false, false>(a, grid, stream);
     else st = sc ? launch_bwd<EBf16, true, true>(a, grid, stream) : launch_bwd<EBf16, true, false>(a, grid, stream);
     if (st != ORPO_OK) return st;
+    if (a.gm.n_tiles > 0 && a.gm.dh_split > 1) {   // the split dh tiles' partials, in split order
+      TraceScope ts(ORPO_K_DHSUM, 0.0, stream);
+      const int64_t n = a.gm.C_cur * desc->d;
+      hipLaunchKernelGGL(dh_reduce_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 2048)),
+                         dim3(256), 0, stream, a);
+      if ((st = launched()) != ORPO_OK) return st;
+    }
   }
   return ORPO_OK;
 }

@@ -80,7 +80,7 @@ _SIGS = {
     "orpo_trace_reset": (ctypes.c_int, []),
 }
 KERNEL_KINDS = {0: "fwd", 1: "merge", 2: "loss", 3: "coeff", 4: "dhdw", 5: "bwd", 6: "quant",
-                7: "stage"}
+                7: "stage", 8: "dhsum"}
 _lib = None
 
 

@@ -30,6 +30,24 @@ def _desc(M=512, d=256, V=4096, h=H.ORPO_BF16, w=H.ORPO_BF16, cap=0.0, flags=0):
     return H.Desc(M, d, V, h, w, cap, -100, flags, 0.0)
 
 
+def _cd(a, b):
+    return -(-a // b)
+
+
+def _dh_part_bytes(C, d, BVb, f32=False):
+    """The backward's split-K dh partials, as its sizing rule states it: with K steps of 32 (fp32)
+    or 64 elements, a dh tile (K = the vocabulary block BVb) is split when its K steps reach twice
+    the average K steps per CU (256) of a launch holding one item's dh, dW and coefficient tiles,
+    into S = min(ceil(steps / average), 256 // dh tiles, 16, steps // 4) ranges (none when S < 2);
+    the partials take S * C * d fp32, rounded up to 256 bytes."""
+    kbk = 32 if f32 else 64
+    n_jt, n_tt, n_vt = _cd(d, 256), _cd(C, 256), _cd(BVb, 256)
+    nk, n_dh = _cd(BVb, kbk), n_tt * n_jt
+    per_cu = _cd(n_dh * nk + n_vt * n_jt * _cd(C, kbk) + n_tt * n_vt * _cd(d, kbk), 256)
+    S = min(_cd(nk, per_cu), 256 // n_dh, 16, nk // 4) if nk >= 2 * per_cu else 1
+    return _cd(S * C * d * 4, 256) * 256 if S >= 2 else 0
+
+
 def test_workspace_sizes():
     L = H.lib()
     d = _desc(M=8192, d=2560, V=262144)
@@ -51,7 +69,14 @@ def test_workspace_sizes():
         assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(dv)) == 256 + 2 * M * bv * 2, (M, V)
     # fp32 coefficients: the budget binds first.
     df = _desc(M=8192, d=256, V=262144, h=H.ORPO_F32, w=H.ORPO_F32)
-    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(df)) == 256 + 2 * 8192 * 8192 * 4
+    parts = _dh_part_bytes(8192, 256, 8192, f32=True)
+    assert parts == 3 * 8192 * 256 * 4        # 32 dh tiles of 256 K steps: split in 3
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(df)) == 256 + 2 * 8192 * 8192 * 4 + parts
+    # The e4b head at a small M: 40 dh tiles of 512 steps against ~240 per CU, split in 3.
+    ds = _desc(M=1024, d=2560, V=262144)
+    assert _dh_part_bytes(1024, 2560, 32768) == 3 * 1024 * 2560 * 4
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(ds)) == (256 + 2 * 1024 * 32768 * 2 +
+                                                                3 * 1024 * 2560 * 4)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -108,10 +133,12 @@ def test_bwd_tiling_knob_validates_and_resizes():
     d = _desc(M=4096, d=256, V=4096)
     try:
         assert L.orpo_set_bwd_tiling(512, 512 * 1024 * 2) == 0
-        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 2 * 512 * 1024 * 2
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == (256 + 2 * 512 * 1024 * 2 +
+                                                                   _dh_part_bytes(512, 256, 1024))
     finally:
         assert L.orpo_set_bwd_tiling(0, 0) == 0
-    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == 256 + 2 * 4096 * 4096 * 2
+    assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(d)) == (256 + 2 * 4096 * 4096 * 2 +
+                                                               _dh_part_bytes(4096, 256, 4096))
 
 
 def test_filter_k_step_limit_reported_by_workspace_size_and_entry_point():
@@ -124,7 +151,10 @@ def test_filter_k_step_limit_reported_by_workspace_size_and_entry_point():
     try:
         assert L.orpo_set_bwd_tiling(256, 256 * 524288 * 2) == 0           # 8192 slices of 64: the limit
         fl = 524288 // 64 * 4 + 524288 // 256 * 4 * 2                       # dh and dW block flags
-        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == 256 + 2 * 256 * 524288 * 2 + 2 * fl
+        parts = _dh_part_bytes(256, 256, 524288)
+        assert parts == 16 * 256 * 256 * 4                                 # one dh tile, 8192 steps
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == (256 + 2 * 256 * 524288 * 2 +
+                                                                     2 * fl + parts)
         assert L.orpo_set_bwd_tiling(256, 256 * (524288 + 256) * 2) == 0   # one slice more
         assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(big)) == 0
         w = H.Weight(16, None, None)
