@@ -31,6 +31,9 @@ def parse():
     ap.add_argument("--config", default="e4b-bf16-softcap30",
                     help="workload name (lm_head_cross_amd.synth.WORKLOADS) or its integer key")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload at this many tokens M (its pairs scaled with M); "
+                         "0 = the workload's own M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
     ap.add_argument("--trace-steps", type=int, default=5,
@@ -55,6 +58,19 @@ def parse():
                     help="instead of the head: the bf16 MFMA rate this GPU sustains (microbenchmark), "
                          "with zero and/or random operands")
     return ap.parse_args()
+
+
+def workload_for(config: str, tokens: int = 0):
+    """The named workload, or (tokens > 0) the same head, distributions and lengths at M = tokens,
+    its pairs scaled with M (at least one; branch lengths shrink to fit when they do not)."""
+    from lm_head_cross_amd import synth
+    cfg = synth.workload(config)
+    if tokens:
+        if tokens < 0:
+            raise ValueError("--tokens must be positive")
+        pairs = max(1, round(cfg.pairs * tokens / cfg.M))
+        cfg = cfg.replace(M=tokens, pairs=pairs, name=f"{cfg.name}-M{tokens}")
+    return cfg
 
 
 def _objective_inputs(objective: str, cfg, off: np.ndarray, n_valid_per_span: np.ndarray, M: int,
@@ -219,7 +235,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    cfg = synth.workload(args.config)
+    cfg = workload_for(args.config, args.tokens)
     print(f"[bench] generating {cfg.name} M={cfg.M} d={cfg.d} V={cfg.V}", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, seed=args.seed, label_device="cuda")
     h = inp.h.to(dev)

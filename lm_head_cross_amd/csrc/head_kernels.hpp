@@ -5,7 +5,8 @@
 //   q4_stage_kernel: a 4-bit head -> bf16 rows, the tiled loops' own dequantisation done once.
 //   fwd_kernel    : raw = W . h^T tile by tile (MFMA), softcap, online softmax per token over the
 //                   workgroup's vocabulary split, label-logit capture -> per-split (max, sum) partials.
-//   merge_kernel  : partials of all splits -> lse, logp = z[y] - lse.
+//   merge_kernel  : partials of all splits -> lse, logp = z[y] - lse (merge_wide_kernel: the
+//                   same with one wave per token, for the many splits of a small M).
 //   loss_kernel   : segmented per-branch means (f64), scalar ORPO epilogue (f64), cotangent g.
 //   bwd_kernel    : one launch of the backward pipeline: coefficient tiles (recompute a logit tile,
 //                   coeff = g (onehot - softmax) sech^2) of one (token chunk, vocabulary block) item
@@ -442,6 +443,24 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 // ------------------------------------------------------------------------------------------
 // Merge the per-split partials: G = max_k m_k, S = sum_k s_k 2^(m_k - G), lse = (G + log2 S) ln 2.
 // ------------------------------------------------------------------------------------------
+// lse and logp of token t from the merged maximum G (log2 units) and sum S against it.
+__device__ __forceinline__ void merge_finish(int64_t t, float G, float S, const int32_t* labels,
+                                             int64_t V, int32_t ignore_index, float* logp,
+                                             float* lse, uint32_t* status) {
+  const float L = (G + log2_(S)) * kLn2;
+  lse[t] = L;
+  const int y = labels[t];
+  if (y == ignore_index) {
+    logp[t] = 0.f;
+  } else if (y < 0 || (int64_t)y >= V) {
+    logp[t] = 0.f;
+    atomicOr(status, kStatusBadLabel);
+  } else {
+    logp[t] = logp[t] - L;
+  }
+}
+
+// One thread per token, the splits in order: for few splits (large M).
 __global__ __launch_bounds__(256) void merge_kernel(const float2* part, int nblk, int64_t M,
                                                     const int32_t* labels, int64_t V,
                                                     int32_t ignore_index, float* logp, float* lse,
@@ -455,17 +474,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const float2* part, int nblk
     const float2 p = part[(int64_t)k * M + t];
     if (p.y > 0.f) S += p.y * exp2_(p.x - G);
   }
-  const float L = (G + log2_(S)) * kLn2;
-  lse[t] = L;
-  const int y = labels[t];
-  if (y == ignore_index) {
-    logp[t] = 0.f;
-  } else if (y < 0 || (int64_t)y >= V) {
-    logp[t] = 0.f;
-    atomicOr(status, kStatusBadLabel);
-  } else {
-    logp[t] = logp[t] - L;
+  merge_finish(t, G, S, labels, V, ignore_index, logp, lse, status);
+}
+
+// One wave per token, lane l taking splits l, l + 64, ...: for many splits (small M, where the
+// forward spreads each token tile over up to 256 vocabulary splits and one thread per token would
+// leave most of the chip idle behind long serial loops). The wave's maximum and sum are xor-shuffle
+// butterflies, a fixed order.
+__global__ __launch_bounds__(256) void merge_wide_kernel(const float2* part, int nblk, int64_t M,
+                                                         const int32_t* labels, int64_t V,
+                                                         int32_t ignore_index, float* logp,
+                                                         float* lse, uint32_t* status) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // uniform per wave
+  const int l = threadIdx.x & 63;
+  if (t >= M) return;
+  float G = kNegInf;
+  for (int k = l; k < nblk; k += 64) G = fmaxf(G, part[(int64_t)k * M + t].x);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) G = fmaxf(G, __shfl_xor(G, o));
+  float S = 0.f;
+  for (int k = l; k < nblk; k += 64) {
+    const float2 p = part[(int64_t)k * M + t];
+    if (p.y > 0.f) S += p.y * exp2_(p.x - G);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o);
+  if (l == 0) merge_finish(t, G, S, labels, V, ignore_index, logp, lse, status);
 }
 
 // ------------------------------------------------------------------------------------------

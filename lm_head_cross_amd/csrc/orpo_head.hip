@@ -19,6 +19,7 @@ using namespace orpo;
 thread_local int32_t g_last_hip = 0;
 
 constexpr size_t kHeader = 256;                     // status word + padding at the start of a workspace
+constexpr int kMergeWideSplits = 32;                // from this many forward splits, a wave per token merges
 constexpr int kTargetWorkgroups = 256;              // forward grid target (one round on 256 CUs)
 constexpr int64_t kChunkDefault = 8192;             // backward token chunk C (multiple of 256)
 // Default coefficient block: the largest that fits 256 MiB per coefficient buffer, but no wider
@@ -330,9 +331,14 @@ orpo_status fwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
   else st = launch_fwd<EBf16, true>(a, grid, stream);
   if (st != ORPO_OK) return st;
   TraceScope ts(ORPO_K_MERGE, 0.0, stream);
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)cdiv(desc->M, 256)), dim3(256), 0, stream,
-                     (const float2*)a.part, p.nblk, desc->M, labels, desc->V, desc->ignore_index,
-                     logp, lse, a.status);
+  if (p.nblk >= kMergeWideSplits)   // small M: many splits per token, one wave per token
+    hipLaunchKernelGGL(merge_wide_kernel, dim3((unsigned)cdiv(desc->M, 4)), dim3(256), 0, stream,
+                       (const float2*)a.part, p.nblk, desc->M, labels, desc->V, desc->ignore_index,
+                       logp, lse, a.status);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)cdiv(desc->M, 256)), dim3(256), 0, stream,
+                       (const float2*)a.part, p.nblk, desc->M, labels, desc->V, desc->ignore_index,
+                       logp, lse, a.status);
   return launched();
 }
 

@@ -31,6 +31,21 @@ def test_no_gpu_is_an_error_not_a_fallback():
     assert r.returncode == 1 and "needs a GPU" in r.stderr and r.stdout == ""
 
 
+def test_tokens_option_scales_the_workload():
+    sys.path.insert(0, ROOT)
+    import bench
+    cfg = bench.workload_for("e4b-bf16-softcap30", 512)
+    assert (cfg.M, cfg.pairs, cfg.d, cfg.V) == (512, 1, 2560, 262144)
+    assert cfg.name == "e4b-bf16-softcap30-M512"
+    assert bench.workload_for("e4b-bf16-softcap30", 2048).pairs == 4
+    assert bench.workload_for("3") == synth.workload(3)
+    # The two branches of the one pair are drawn from [192, 320] and shrink to fit in 512 tokens.
+    lens = synth.draw_lengths(synth._streams(cfg.key, 0)[0], 2, cfg.len_lo, cfg.len_hi, cfg.M)
+    assert lens.sum() <= 512 and (lens >= 1).all()
+    with pytest.raises(ValueError):
+        bench.workload_for("e4b-bf16-softcap30", -1)
+
+
 @pytest.mark.parametrize("objective,q4,full", [("orpo", False, False), ("orpo", True, False),
                                                ("orpo", False, True), ("simpo", False, False),
                                                ("dpo", False, False), ("ipo", False, False),
