@@ -143,8 +143,9 @@ struct BwdPlan {
   int64_t C, BVb;
   size_t dh_acc_bytes;   // fp32 [C, d] chunk accumulator for bf16 dh over several blocks (else 0)
   size_t fl_bytes;   // skip flags per coefficient buffer (0 without the coefficient filter)
-  int dh_split;      // K ranges per dh tile (1: none)
-  size_t part_off, part_bytes;   // fp32 [dh_split][C][d] dh partials (dh_split > 1)
+  int dh_split;      // K ranges per dh tile in a launch with coefficient tiles (1: none)
+  int dh_split_last; // ... in the last launch, which holds only dh / dW tiles
+  size_t part_off, part_bytes;   // fp32 [max split][C][d] dh partials (a split > 1)
   size_t ws;
 };
 
@@ -176,24 +177,29 @@ BwdPlan plan_bwd(const orpo_head_desc* d, Kind k) {
                        : 0;
   // Split-K dh. A dh tile's K is the whole vocabulary block, so with few token tiles (small M) a
   // launch holds a few dh tiles that each run far longer than the launch's average work per CU,
-  // and the launch waits for them. When a dh tile's K steps reach twice that average, its K is
-  // split over dh_split workgroups (at most one round of kTargetWorkgroups dh workgroups, at most
-  // 16 splits, at least 4 K steps each), so the partials take at most 256 tiles x 256 x 256 fp32 =
-  // 64 MiB. The average assumes dW tiles are present (the workspace size does not know whether dW
-  // is asked for).
+  // and the launch waits for them. When a dh tile's K steps reach 1.5 times that average, its K
+  // is split over S = ceil(steps / average) workgroups (at most one round of kTargetWorkgroups dh
+  // workgroups, at most 16 splits, at least 4 K steps each), so the partials take at most 256
+  // tiles x 256 x 256 fp32 = 64 MiB. The average is taken with an item's dh, dW and coefficient
+  // tiles for the mixed launches and without the coefficient tiles for the last launch; it assumes
+  // dW tiles are present (the workspace size does not know whether dW is asked for).
   {
     const int64_t kbk = k == kF32 ? 32 : 64;
     const int64_t n_jt = cdiv(d->d, kTile), n_tt = cdiv(p.C, kTile), n_vt = cdiv(p.BVb, kTile);
     const int64_t nk_dh = cdiv(p.BVb, kbk), n_dh = n_tt * n_jt;
-    const int64_t work = n_dh * nk_dh + n_vt * n_jt * cdiv(p.C, kbk) + n_tt * n_vt * cdiv(d->d, kbk);
-    const int64_t per_cu = cdiv(work, kTargetWorkgroups);
-    int64_t S = 1;
-    if (nk_dh >= 2 * per_cu)
-      S = std::min<int64_t>(std::min<int64_t>(cdiv(nk_dh, per_cu), kTargetWorkgroups / n_dh),
-                            std::min<int64_t>(16, nk_dh / 4));
-    p.dh_split = S >= 2 ? (int)S : 1;
+    const int64_t gemm = n_dh * nk_dh + n_vt * n_jt * cdiv(p.C, kbk);
+    auto split_for = [&](int64_t work) {
+      const int64_t per_cu = cdiv(work, kTargetWorkgroups);
+      if (2 * nk_dh < 3 * per_cu) return 1;
+      const int64_t S = std::min<int64_t>(std::min<int64_t>(cdiv(nk_dh, per_cu), kTargetWorkgroups / n_dh),
+                                          std::min<int64_t>(16, nk_dh / 4));
+      return S >= 2 ? (int)S : 1;
+    };
+    p.dh_split = split_for(gemm + n_tt * n_vt * cdiv(d->d, kbk));
+    p.dh_split_last = split_for(gemm);
   }
-  p.part_bytes = p.dh_split > 1 ? round_up(size_t(p.dh_split) * size_t(p.C) * size_t(d->d) * 4, 256) : 0;
+  const int s_max = std::max(p.dh_split, p.dh_split_last);
+  p.part_bytes = s_max > 1 ? round_up(size_t(s_max) * size_t(p.C) * size_t(d->d) * 4, 256) : 0;
   p.part_off = kHeader + 2 * size_t(p.C) * size_t(p.BVb) * size_t(esize) + 2 * p.fl_bytes;
   p.ws = p.part_off + p.part_bytes + p.dh_acc_bytes;
   return p;
@@ -648,7 +654,7 @@ orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
   const int64_t n_blocks = cdiv(desc->V, p.BVb);
   const int64_t n_items = cdiv(desc->M, p.C) * n_blocks;
   // Item i = (chunk i / n_blocks, block i % n_blocks); launch i = coefficients of item i + dh/dW of item i-1.
-  auto make_item = [&](int64_t i, bool gemm) {
+  auto make_item = [&](int64_t i, bool gemm, int split) {
     BwdItem it{};
     if (i < 0 || i >= n_items) return it;   // n_tiles = 0: absent
     const int64_t c = i / n_blocks, blk = i % n_blocks;
@@ -665,10 +671,10 @@ orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
     it.dh_last = blk == n_blocks - 1;
     it.dw_first = c == 0 && !acc_dw;
     if (gemm) {
-      it.dh_split = p.dh_split;
-      it.dh_part = p.dh_split > 1 ? (float*)((char*)ws + p.part_off) : nullptr;
+      it.dh_split = split;
+      it.dh_part = split > 1 ? (float*)((char*)ws + p.part_off) : nullptr;
       it.dh_part_pitch = p.C * desc->d;
-      it.n_dh = it.n_tt * a.n_jt * p.dh_split;
+      it.n_dh = it.n_tt * a.n_jt * split;
       it.n_tiles = it.n_dh + (dW ? it.n_vt * a.n_jt : 0);
     } else {
       it.n_tiles = it.n_vt * it.n_tt;
@@ -676,8 +682,8 @@ orpo_status bwd_impl(const orpo_head_desc* desc, Kind k, const void* h, const or
     return it;
   };
   for (int64_t i = 0; i <= n_items; ++i) {
-    a.cf = make_item(i, false);
-    a.gm = make_item(i - 1, true);
+    a.cf = make_item(i, false, 1);
+    a.gm = make_item(i - 1, true, i < n_items ? p.dh_split : p.dh_split_last);
     const int grid = a.cf.n_tiles + a.gm.n_tiles;
     if (q8) st = sc ? launch_bwd<EBf16, false, true, true>(a, grid, stream) : launch_bwd<EBf16, false, false, true>(a, grid, stream);
     else if (k == kF32) st = sc ? launch_bwd<EF32, false, true>(a, grid, stream) : launch_bwd<EF32, false, false>(a, grid, stream);

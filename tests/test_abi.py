@@ -36,15 +36,23 @@ def _cd(a, b):
 
 def _dh_part_bytes(C, d, BVb, f32=False):
     """The backward's split-K dh partials, as its sizing rule states it: with K steps of 32 (fp32)
-    or 64 elements, a dh tile (K = the vocabulary block BVb) is split when its K steps reach twice
-    the average K steps per CU (256) of a launch holding one item's dh, dW and coefficient tiles,
-    into S = min(ceil(steps / average), 256 // dh tiles, 16, steps // 4) ranges (none when S < 2);
-    the partials take S * C * d fp32, rounded up to 256 bytes."""
+    or 64 elements, a dh tile (K = the vocabulary block BVb) is split when its K steps reach 1.5
+    times the average K steps per CU (256) of a launch, into S = min(ceil(steps / average),
+    256 // dh tiles, 16, steps // 4) ranges (none when S < 2). The average is taken over one item's
+    dh, dW and coefficient tiles (mixed launches) and over its dh and dW tiles (the last launch);
+    the partials take the larger S * C * d fp32, rounded up to 256 bytes."""
     kbk = 32 if f32 else 64
     n_jt, n_tt, n_vt = _cd(d, 256), _cd(C, 256), _cd(BVb, 256)
     nk, n_dh = _cd(BVb, kbk), n_tt * n_jt
-    per_cu = _cd(n_dh * nk + n_vt * n_jt * _cd(C, kbk) + n_tt * n_vt * _cd(d, kbk), 256)
-    S = min(_cd(nk, per_cu), 256 // n_dh, 16, nk // 4) if nk >= 2 * per_cu else 1
+    gemm = n_dh * nk + n_vt * n_jt * _cd(C, kbk)
+
+    def split(work):
+        per_cu = _cd(work, 256)
+        if 2 * nk < 3 * per_cu:
+            return 1
+        S = min(_cd(nk, per_cu), 256 // n_dh, 16, nk // 4)
+        return S if S >= 2 else 1
+    S = max(split(gemm + n_tt * n_vt * _cd(d, kbk)), split(gemm))
     return _cd(S * C * d * 4, 256) * 256 if S >= 2 else 0
 
 
@@ -66,17 +74,21 @@ def test_workspace_sizes():
     for M, V, bv in ((8192, 73448, 16384), (4096, 73448, 16384), (2048, 150000, 18944),
                      (8192, 1 << 20, 16384), (2048, 1 << 20, 65536), (8192, 4096, 4096)):
         dv = _desc(M=M, d=1536, V=V)
-        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(dv)) == 256 + 2 * M * bv * 2, (M, V)
+        assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(dv)) == (256 + 2 * M * bv * 2 +
+                                                                    _dh_part_bytes(M, 1536, bv)), (M, V)
     # fp32 coefficients: the budget binds first.
     df = _desc(M=8192, d=256, V=262144, h=H.ORPO_F32, w=H.ORPO_F32)
     parts = _dh_part_bytes(8192, 256, 8192, f32=True)
-    assert parts == 3 * 8192 * 256 * 4        # 32 dh tiles of 256 K steps: split in 3
+    assert parts == 4 * 8192 * 256 * 4        # 32 dh tiles of 256 K steps: the last launch's 4 splits
     assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(df)) == 256 + 2 * 8192 * 8192 * 4 + parts
-    # The e4b head at a small M: 40 dh tiles of 512 steps against ~240 per CU, split in 3.
+    # The e4b head at a small M: 40 dh tiles of 512 steps against ~240 per CU in the mixed
+    # launches (3 splits) and ~160 in the last (4 splits).
     ds = _desc(M=1024, d=2560, V=262144)
-    assert _dh_part_bytes(1024, 2560, 32768) == 3 * 1024 * 2560 * 4
+    assert _dh_part_bytes(1024, 2560, 32768) == 4 * 1024 * 2560 * 4
     assert L.orpo_head_bwd_workspace_bytes(ctypes.byref(ds)) == (256 + 2 * 1024 * 32768 * 2 +
-                                                                3 * 1024 * 2560 * 4)
+                                                                4 * 1024 * 2560 * 4)
+    # At M = 8192 nothing splits.
+    assert _dh_part_bytes(8192, 2560, 16384) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
