@@ -124,6 +124,22 @@ def test_one_token_and_one_row_tails(M, d, V, dtype, cap, lam):
     assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name)
 
 
+# A handful of tokens over a wide vocabulary: one token tile spread over 79 vocabulary splits (the
+# merge's one-wave-per-token path, most of its waves past M), and the backward's single dh tile
+# split 16 ways over two vocabulary blocks, the second 3617 rows wide (splits of 3 or 4 K steps).
+FEW_TOKENS = [
+    (5, 128, 20001, "bf16", 30.0, 0.1),
+    (2, 64, 20001, "f32", 0.0, 0.1),
+]
+
+
+@pytest.mark.parametrize("M,d,V,dtype,cap,lam", FEW_TOKENS)
+def test_few_tokens_wide_vocabulary(M, d, V, dtype, cap, lam):
+    inp = _custom(M, d, V, dtype, cap, lam, seed=7 * M + V, pairs=1)
+    say(f"[case] {inp.cfg.name}")
+    assert_parity(run_gpu(inp), run_oracle(inp), inp.cfg.name)
+
+
 def test_ignored_rows_with_huge_logits_no_softcap():
     # Without a softcap, padding and ignored tokens whose raw logits exceed the float range of
     # e^raw must still get zero coefficients: dh rows exactly zero, dW finite and at parity.
