@@ -163,25 +163,47 @@ def row_gate(name, gpu, ref, zero_rows=None):
 
 
 def assert_parity(gpu, ora, label=""):
-    errs = {
-        "logp": rel(gpu["logp"], ora["logp"]),
-        "lse": rel(gpu["lse"], ora["lse"]),
-        "lw": rel(gpu["lw"], ora["lw"]),
-        "lr": rel(gpu["lr"], ora["lr"]),
-        "loss": srel(gpu["loss"], ora["loss"]),
-        "nll": srel(gpu["nll"], ora["nll"]),
-        "or": srel(gpu["or"], ora["or"]),
-        "margin": abs(gpu["margin"] - ora["margin"]) / max(1.0, abs(ora["margin"])),
-        "g": rel(gpu["g"], ora["g"]),
-        "dh": rel(gpu["dh"], ora["dh"]),
-    }
-    if ora.get("dW") is not None and gpu.get("dW") is not None:
-        errs["dW"] = rel(gpu["dW"], ora["dW"])
-    if gpu.get("pm") is not None:
-        errs["pm"] = rel(gpu["pm"], ora["pm"])
-    say(f"[parity {label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    # Per token and per row, against the oracle on the operands the kernels multiply.
+    """Gates the GPU results against the oracle. For the 4-bit head the kernels multiply the
+    bf16-rounded dequantised weights (ora["op"], the oracle on those operands): every gate holds
+    against it at the stated tolerance, and against the exactly dequantised oracle with, added, the
+    distance between the two oracles (the operand rounding's own effect, which on a branch of one or
+    two tokens can exceed 1e-3 by itself). For dense weights the two are the same oracle."""
     op = ora.get("op", ora)
+
+    def measures(x):
+        m = {
+            "logp": rel(gpu["logp"], x["logp"]),
+            "lse": rel(gpu["lse"], x["lse"]),
+            "lw": rel(gpu["lw"], x["lw"]),
+            "lr": rel(gpu["lr"], x["lr"]),
+            "loss": srel(gpu["loss"], x["loss"]),
+            "nll": srel(gpu["nll"], x["nll"]),
+            "or": srel(gpu["or"], x["or"]),
+            "margin": abs(gpu["margin"] - x["margin"]) / max(1.0, abs(x["margin"])),
+            "g": rel(gpu["g"], x["g"]),
+            "dh": rel(gpu["dh"], x["dh"]),
+        }
+        if x.get("dW") is not None and gpu.get("dW") is not None:
+            m["dW"] = rel(gpu["dW"], x["dW"])
+        if gpu.get("pm") is not None:
+            m["pm"] = rel(gpu["pm"], x["pm"])
+        return m
+
+    errs = measures(ora)
+    errs_op = measures(op) if op is not ora else errs
+    say(f"[parity {label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    if op is not ora:
+        say(f"[parity-op {label}] " + " ".join(f"{k}={v:.2e}" for k, v in errs_op.items()))
+    # The distance between the two oracles, measured as each gate measures the GPU's.
+    slack = {"logp": rel(op["logp"], ora["logp"]), "lse": rel(op["lse"], ora["lse"]),
+             "lw": rel(op["lw"], ora["lw"]), "lr": rel(op["lr"], ora["lr"]),
+             "loss": srel(op["loss"], ora["loss"]), "nll": srel(op["nll"], ora["nll"]),
+             "g": rel(op["g"], ora["g"]), "dh": rel(op["dh"], ora["dh"])}
+    if "dW" in errs:
+        slack["dW"] = rel(op["dW"], ora["dW"])
+    if "pm" in errs:
+        slack["pm"] = rel(op["pm"], ora["pm"])
+    # Per token and per row, against the oracle on the operands the kernels multiply.
     valid = np.asarray(op["g"]) != 0
     diag = {
         "max|dlogp|": token_gate("logp", gpu["logp"], op["logp"]),
@@ -194,21 +216,30 @@ def assert_parity(gpu, ora, label=""):
     say(f"[per-token {label}] " + " ".join(f"{k}={v:.2e}" for k, v in diag.items()))
     for k in ("logp", "lse", "lw", "lr", "loss", "nll", "g", "pm"):
         if k in errs:
-            assert errs[k] <= TOL_SCALAR, (k, errs[k])
+            assert errs_op[k] <= TOL_SCALAR, (k, errs_op[k])
+            assert errs[k] <= TOL_SCALAR + slack[k], (k, errs[k], slack[k])
     # The odds-ratio term and the margin are gated by what the 1e-3 branch-mean gate implies for
     # them: |d log_odds| <= F(lw)|d lw| + F(lr)|d lr| with F(l) = 1/(1 - e^l) and |d softplus(-z)/dz|
     # = 1 - sigmoid(z), so a branch-mean error of TOL * |ell| allows these absolute errors.
-    lw, lr = np.asarray(ora["lw"]), np.asarray(ora["lr"])
+    lw, lr = np.asarray(op["lw"]), np.asarray(op["lr"])
     F = lambda x: 1.0 / -np.expm1(np.minimum(x, -1e-12))
     dz = TOL_SCALAR * (F(lw) * np.abs(lw) + F(lr) * np.abs(lr))
-    one_minus_sig = 1.0 / (1.0 + np.exp(np.asarray(ora["log_odds"])))
-    assert abs(gpu["or"] - ora["or"]) <= np.mean(one_minus_sig * dz) + 1e-12, "or"
-    assert abs(gpu["margin"] - ora["margin"]) <= np.mean(dz) + 1e-12, "margin"
+    one_minus_sig = 1.0 / (1.0 + np.exp(np.asarray(op["log_odds"])))
+    b_or, b_mg = np.mean(one_minus_sig * dz) + 1e-12, np.mean(dz) + 1e-12
+    assert abs(gpu["or"] - op["or"]) <= b_or, "or"
+    assert abs(gpu["margin"] - op["margin"]) <= b_mg, "margin"
+    assert abs(gpu["or"] - ora["or"]) <= b_or + abs(op["or"] - ora["or"]), "or"
+    assert abs(gpu["margin"] - ora["margin"]) <= b_mg + abs(op["margin"] - ora["margin"]), "margin"
     for k in ("dh", "dW"):
         if k in errs:
-            assert errs[k] <= TOL_GRAD, (k, errs[k])
+            assert errs_op[k] <= TOL_GRAD, (k, errs_op[k])
+            assert errs[k] <= TOL_GRAD + slack[k], (k, errs[k], slack[k])
     # Per-branch means individually, not only norm-wise.
-    for a, b in zip(np.concatenate([gpu["lw"], gpu["lr"]]), np.concatenate([ora["lw"], ora["lr"]])):
-        assert srel(a, b) <= TOL_SCALAR
-    assert gpu["accuracy"] == ora["accuracy"] or abs(gpu["lw"] - gpu["lr"]).min() < 1e-4
+    g_l = np.concatenate([gpu["lw"], gpu["lr"]])
+    o_l = np.concatenate([op["lw"], op["lr"]])
+    e_l = np.concatenate([ora["lw"], ora["lr"]])
+    for a, b, c in zip(g_l, o_l, e_l):
+        assert srel(a, b) <= TOL_SCALAR, ("branch mean", a, b)
+        assert abs(a - c) <= TOL_SCALAR * abs(c) + abs(b - c), ("branch mean", a, c)
+    assert gpu["accuracy"] == op["accuracy"] or abs(gpu["lw"] - gpu["lr"]).min() < 1e-4
     return errs
