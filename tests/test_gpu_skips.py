@@ -202,3 +202,43 @@ def test_cold_tile_skip_is_exact_for_the_filter_and_skips_tiles():
     n_cold = int(untouched.sum().item())
     say(f"[filter cold tiles] {n_cold} of {untouched.numel()} coefficient tiles skipped")
     assert n_cold > 0
+
+
+def _filter_cases(n, seed, budget=4e9):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([rng.integers(16, 64), rng.integers(64, 700), rng.integers(700, 1300)]))
+        d = int(rng.choice([64, 128, 192, 256, 320, 448, 512]))
+        V = int(rng.choice([rng.integers(2, 600), rng.integers(600, 8000), rng.integers(8000, 30000)]))
+        cap = float(rng.choice([0.0, 30.0]))
+        if M * V * d > budget:
+            continue
+        out.append((M, d, V, cap, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("M,d,V,cap,seed", _filter_cases(8, 4049))
+def test_filter_random_shapes(M, d, V, cap, seed):
+    # Seeded random shapes (one to several token tiles, short and long vocabulary blocks, so the dh
+    # tiles' K is split 1 to 16 ways): a cotangent loud on random 64-token blocks and 1e-6
+    # elsewhere, eps = 1e-3, against the oracle's filtered backward; and eps = 1e-30 (only the
+    # all-zero slices past V dropped) bitwise equal to the exact backward.
+    say(f"[case] filter sweep M={M} d={d} V={V} cap={cap} seed={seed}")
+    h, w, labels = _custom(M, d, V, cap, seed=seed)
+    hh, W = h.float().numpy().astype(np.float64), w.float().numpy().astype(np.float64)
+    _, lse = orc.forward(hh, W, labels, cap)
+    rng = np.random.default_rng(seed + 1)
+    g = np.full(M, 1e-6)
+    for b in range(0, M, 64):
+        if rng.random() < 0.4:
+            g[b:b + 64] = rng.choice([-1.0, 0.5])
+    g[labels == -100] = 0
+    dh, dW = _gpu_bwd(h, w, labels, lse, g, cap, 1e-3)
+    fh, fw, kh, kw = orc.backward_filtered(hh, W, labels, lse, g, cap, 1e-3)
+    e_dh, e_dW = rel(dh, fh), rel(dW, fw)
+    say(f"[filter sweep] kept dh {kh:.3f} dW {kw:.3f}; vs filtered dh={e_dh:.2e} dW={e_dW:.2e}")
+    assert e_dh <= TOL_GRAD and e_dW <= TOL_GRAD
+    a = _gpu_bwd(h, w, labels, lse, g, cap, 0.0)
+    b = _gpu_bwd(h, w, labels, lse, g, cap, 1e-30)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
