@@ -120,6 +120,29 @@ def test_fp8_step_parity_small(M, d, V, pairs, lo, hi, cap):
     assert_parity(gpu, ora, cfg.name)
 
 
+def _fp8_random_cases(n, seed, budget=4e9):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.choice([rng.integers(16, 128), rng.integers(128, 700), rng.integers(700, 1300)]))
+        d = int(rng.choice([128, 256, 384, 512]))
+        V = int(rng.choice([rng.integers(2, 600), rng.integers(600, 8000), rng.integers(8000, 30000)]))
+        pairs = int(rng.integers(1, 4))
+        cap = float(rng.choice([0.0, 30.0]))
+        if M * V * d > budget or M < 4 * pairs:
+            continue
+        lo = max(1, M // (4 * pairs))
+        out.append((M, d, V, pairs, lo, max(lo, M // (2 * pairs) - 1), cap))
+    return out
+
+
+@pytest.mark.parametrize("M,d,V,pairs,lo,hi,cap", _fp8_random_cases(6, 5081))
+def test_fp8_step_parity_random_shapes(M, d, V, pairs, lo, hi, cap):
+    # Seeded random shapes: a handful of tokens to over a thousand, vocabularies from one tile to
+    # ~30k (the backward's dh tiles split 1 to 16 ways, the forward merged either way).
+    test_fp8_step_parity_small(M, d, V, pairs, lo, hi, cap)
+
+
 def test_fp8_step_dh_bf16_and_tiled_backward():
     cfg = synth.HeadConfig(0, "fp8-tiled", M=1024, d=256, V=4096, pairs=2, len_lo=200, len_hi=256,
                            softcap=30.0, lam=0.1)
